@@ -1,0 +1,170 @@
+"""CPU oracle for the GPT-OSS MXFP4 mixture-of-experts layer.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the benchmark's CPU-baseline leg, never by the product package. It is a
+thin ctypes wrapper around ``oracle.c`` (plain C, IEEE double, built with gcc
+without fast-math or FMA contraction). It shares no code with the HIP library.
+
+Every function takes the host numpy arrays produced by ``workloads.make_inputs``
+(bf16 as uint16 bit patterns, packed MXFP4 as uint8) and returns float64
+results. See ``oracle.c`` for the page passages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_P = np.ctypeslib.ndpointer
+_u8 = _P(dtype=np.uint8, flags="C_CONTIGUOUS")
+_u16 = _P(dtype=np.uint16, flags="C_CONTIGUOUS")
+_i32 = _P(dtype=np.int32, flags="C_CONTIGUOUS")
+_i64 = _P(dtype=np.int64, flags="C_CONTIGUOUS")
+_f64 = _P(dtype=np.float64, flags="C_CONTIGUOUS")
+_f64_or_null = ctypes.c_void_p
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` next to it (gcc, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-fno-fast-math", "-ffp-contract=off", "-fvisibility=hidden",
+               _SRC, "-o", _LIB + ".tmp", "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    lib.oracle_e2m1.restype = ctypes.c_double
+    lib.oracle_e2m1.argtypes = [ctypes.c_int]
+    lib.oracle_e8m0.restype = ctypes.c_double
+    lib.oracle_e8m0.argtypes = [ctypes.c_int]
+    lib.oracle_swiglu.restype = ctypes.c_double
+    lib.oracle_swiglu.argtypes = [ctypes.c_double] * 4
+    lib.oracle_dequant.restype = None
+    lib.oracle_dequant.argtypes = [_u8, _u8, ctypes.c_int64, ctypes.c_int64, _f64]
+    lib.oracle_router.restype = None
+    lib.oracle_router.argtypes = [_u16, _u16, _u16, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                  _f64, _f64_or_null]
+    lib.oracle_topk_softmax.restype = None
+    lib.oracle_topk_softmax.argtypes = [_f64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _i32, _f64]
+    lib.oracle_expert.restype = None
+    lib.oracle_expert.argtypes = [_u16, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  _u8, _u8, _u16, _u8, _u8, _u16,
+                                  ctypes.c_double, ctypes.c_double, _f64_or_null, _f64]
+    lib.oracle_forward_tokens.restype = None
+    lib.oracle_forward_tokens.argtypes = [
+        _i64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        _u16, _u16, _u16, _u8, _u8, _u16, _u8, _u8, _u16,
+        ctypes.c_double, ctypes.c_double,
+        _f64, _f64_or_null, _i32, _f64, _f64_or_null, _f64_or_null, _f64]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def e2m1(code: int) -> float:
+    return _load().oracle_e2m1(int(code))
+
+
+def e8m0(byte: int) -> float:
+    return _load().oracle_e8m0(int(byte))
+
+
+def swiglu(gate: float, up: float, alpha: float = 1.702, limit: float = 7.0) -> float:
+    return _load().oracle_swiglu(float(gate), float(up), float(alpha), float(limit))
+
+
+def dequant(blocks: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Packed ``[..., rows, cols/2]`` blocks + ``[..., rows, cols/32]`` scales -> float64 ``[..., rows, cols]``."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    cols = blocks.shape[-1] * 2
+    rows = int(np.prod(blocks.shape[:-1]))
+    if scales.shape[:-1] != blocks.shape[:-1] or scales.shape[-1] * 32 != cols:
+        raise ValueError("blocks/scales shape mismatch")
+    out = np.empty(blocks.shape[:-1] + (cols,), dtype=np.float64)
+    _load().oracle_dequant(blocks.reshape(-1), scales.reshape(-1), rows, cols, out.reshape(-1))
+    return out
+
+
+def router(x, router_w, router_b, with_abs_sum: bool = False):
+    T, H = x.shape
+    E = router_w.shape[0]
+    logits = np.empty((T, E), dtype=np.float64)
+    abs_sum = np.empty((T, E), dtype=np.float64) if with_abs_sum else None
+    _load().oracle_router(np.ascontiguousarray(x), np.ascontiguousarray(router_w),
+                          np.ascontiguousarray(router_b), T, H, E, logits, _ptr(abs_sum))
+    return (logits, abs_sum) if with_abs_sum else logits
+
+
+def topk_softmax(logits: np.ndarray, k: int):
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
+    T, E = logits.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    _load().oracle_topk_softmax(logits, T, E, k, idx, w)
+    return idx, w
+
+
+def expert(x_row, e: int, inp: Dict[str, np.ndarray], alpha=1.702, limit=7.0):
+    """One expert on one bf16 token row; returns (h [I], o [H]) in float64."""
+    H = inp["router_w"].shape[1]
+    I = inp["dn_blocks"].shape[2] * 2
+    h = np.empty(I, dtype=np.float64)
+    o = np.empty(H, dtype=np.float64)
+    _load().oracle_expert(np.ascontiguousarray(x_row), int(e), H, I, inp["gu_blocks"],
+                          inp["gu_scales"], inp["gu_bias"], inp["dn_blocks"], inp["dn_scales"],
+                          inp["dn_bias"], float(alpha), float(limit), _ptr(h), o)
+    return h, o
+
+
+def forward(inp: Dict[str, np.ndarray], k: int, tokens: Optional[Sequence[int]] = None,
+            alpha: float = 1.702, limit: float = 7.0, intermediates: bool = False):
+    """The whole layer for ``tokens`` (default: all rows of ``inp['x']``).
+
+    Returns a dict with ``y [n, H]``, ``idx [n, k]``, ``w [n, k]``, ``logits [n, E]``,
+    ``abs_sum [n, E]`` and, when ``intermediates``, ``h [n, k, I]`` and ``o [n, k, H]``.
+    """
+    x = inp["x"]
+    T, H = x.shape
+    E = inp["router_w"].shape[0]
+    I = inp["dn_blocks"].shape[2] * 2
+    tok = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    n = tok.shape[0]
+    out = {
+        "tokens": tok,
+        "logits": np.empty((n, E), dtype=np.float64),
+        "abs_sum": np.empty((n, E), dtype=np.float64),
+        "idx": np.empty((n, k), dtype=np.int32),
+        "w": np.empty((n, k), dtype=np.float64),
+        "y": np.empty((n, H), dtype=np.float64),
+    }
+    h = np.empty((n, k, I), dtype=np.float64) if intermediates else None
+    o = np.empty((n, k, H), dtype=np.float64) if intermediates else None
+    _load().oracle_forward_tokens(
+        np.ascontiguousarray(tok), n, H, I, E, k, np.ascontiguousarray(x),
+        inp["router_w"], inp["router_b"], inp["gu_blocks"], inp["gu_scales"], inp["gu_bias"],
+        inp["dn_blocks"], inp["dn_scales"], inp["dn_bias"], float(alpha), float(limit),
+        out["logits"], _ptr(out["abs_sum"]), out["idx"], out["w"], _ptr(h), _ptr(o), out["y"])
+    if intermediates:
+        out["h"], out["o"] = h, o
+    return out
