@@ -1,0 +1,187 @@
+/*
+ * moe_mxfp4.h — C ABI of the MI355X (gfx950) GPT-OSS MXFP4 mixture-of-experts layer.
+ *
+ * The layer (ZeroModels GPT-OSS page, list item "Mixture-of-experts feed-forward"):
+ *   1. router logits  l[t, e] = sum_h x[t, h] * Wr[e, h] + br[e]
+ *   2. top-k experts per token (larger logit first, equal logits -> lower index),
+ *      routing weights w = softmax over the k selected logits
+ *   3. for each selected expert e: gu = x[t] . Wgu[e]^T + bgu[e]   (MXFP4 Wgu, dequantized
+ *      on the fly: same page, "MXFP4 experts")
+ *   4. gate = gu[0::2], up = gu[1::2] (MaxText PR "Checkpoint conversion utility: gpt-oss
+ *      orbax scan to hf ...", section "1 Support many-to-one transform"; Megatron-Bridge
+ *      gpt_oss_bridge page, GPTOSSMLPGateUpProjMapping: alternating row interleaving),
+ *      h = (clamp(up, -limit, limit) + 1) * g * sigmoid(alpha * g), g = min(gate, limit)
+ *   5. o = h . Wdn[e]^T + bdn[e]   (MXFP4 Wdn)
+ *   6. y[t] = sum_j w[t, j] * o_j
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous, owned by the
+ *    caller. The library allocates nothing, frees nothing and keeps no state between
+ *    calls. Inputs are read-only; outputs are fully overwritten.
+ *  - bf16 tensors are passed as uint16_t bit patterns (moe_bf16_t).
+ *  - `stream` is a hipStream_t (NULL = the null stream). All work is enqueued on it;
+ *    no call synchronises. Calls on different streams with distinct output/workspace
+ *    buffers may run concurrently.
+ *  - T == 0 (no tokens) returns MOE_OK once the shape is valid, without reading any
+ *    pointer argument and without launching anything.
+ *  - Validation is host-only and happens before any launch. On error the call returns
+ *    a nonzero moe_status_t, launches nothing and writes nothing; moe_mxfp4_last_error()
+ *    returns a message (thread-local, valid until the next call on the thread). Launch
+ *    failures return MOE_EHIP. Device faults surface at the caller's next synchronisation.
+ *  - Determinism: identical inputs give bit-identical outputs (fixed summation orders,
+ *    no floating-point atomics).
+ *
+ * Packed MXFP4 layout (ZeroModels GPT-OSS page, "MXFP4 experts": uint8 nibble blocks plus
+ * e8m0 scales; orientation from the Megatron-Bridge gpt_oss_bridge page,
+ * maybe_modify_loaded_hf_weight: dequantized gate_up is [E, 2I, H], down is [E, H, I]):
+ *  - blocks [E, R, C/2] uint8: byte j of a row holds column 2j (low nibble) and column
+ *    2j+1 (high nibble) as FP4 E2M1 codes. (Identical bytes to a [E, R, C/32, 16] view.)
+ *  - scales [E, R, C/32] uint8: E8M0, the 32-column block c/32 of a row is multiplied by
+ *    2^(s - 127). Supported scale bytes: 2..252 (every dequantized value is then an exact
+ *    normal bf16); other bytes give unspecified values.
+ *  - gate_up rows are interleaved: row 2i is gate_i, row 2i+1 is up_i (bias likewise).
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MXFP4_ABI_VERSION 1
+
+typedef uint16_t moe_bf16_t;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,      /* NULL pointer where one is required, T < 0, non-finite alpha/limit */
+    MOE_ESHAPE = 2,      /* H or I not a positive multiple of 32, k < 1, k > E, k > 8, E > 256,
+                            E < 1, sizes too large for 32-bit row indexing */
+    MOE_EALIGN = 3,      /* a tensor pointer not 16-byte aligned (scale pointers: any alignment) */
+    MOE_EWORKSPACE = 4,  /* workspace NULL or smaller than moe_mxfp4_workspace_bytes() */
+    MOE_EHIP = 5         /* a HIP launch failed */
+} moe_status_t;
+
+/* Layer shape. T = tokens, H = hidden (embed_dim), I = expert intermediate (mlp_dim),
+ * E = experts, k = experts per token. alpha / limit: the SwiGLU constants (GPT-OSS:
+ * 1.702 and 7.0, ZeroModels GPT-OSS page, "Mixture-of-experts feed-forward"). */
+typedef struct {
+    int64_t T;
+    int32_t H, I, E, k;
+    float swiglu_alpha;
+    float swiglu_limit;
+} moe_mxfp4_shape_t;
+
+/* ABI version of the loaded library (MOE_MXFP4_ABI_VERSION at build time). */
+int moe_mxfp4_abi_version(void);
+
+/* Message describing the last error on this thread ("" if none). Never NULL. */
+const char *moe_mxfp4_last_error(void);
+
+/* Host-only validation of a shape; launches nothing. */
+moe_status_t moe_mxfp4_check_shape(const moe_mxfp4_shape_t *shape);
+
+/* Bytes of device workspace moe_mxfp4_forward needs for `shape` (written to *bytes).
+ * Host-only; launches nothing. */
+moe_status_t moe_mxfp4_workspace_bytes(const moe_mxfp4_shape_t *shape, size_t *bytes);
+
+/*
+ * The whole layer, steps 1-6 above.
+ *  x          [T, H]        bf16
+ *  router_w   [E, H]        bf16      router_b [E] bf16
+ *  gu_blocks  [E, 2I, H/2]  uint8     gu_scales [E, 2I, H/32] uint8   gu_bias [E, 2I] bf16
+ *  dn_blocks  [E, H, I/2]   uint8     dn_scales [E, H, I/32]  uint8   dn_bias [E, H]  bf16
+ *  y          [T, H]        bf16 (out)
+ *  topk_idx   [T, k] int32  (out, or NULL)   selected experts in selection order
+ *  topk_w     [T, k] fp32   (out, or NULL)   their softmax weights
+ *  workspace  device scratch of at least moe_mxfp4_workspace_bytes() bytes, 256-byte
+ *             aligned; its contents on entry are ignored.
+ */
+moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape,
+                               const moe_bf16_t *x,
+                               const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                               const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                               const moe_bf16_t *gu_bias,
+                               const uint8_t *dn_blocks, const uint8_t *dn_scales,
+                               const moe_bf16_t *dn_bias,
+                               moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Steps 1-2 only (router, top-k, softmax). Logits are accumulated in double precision
+ * from the exact bf16 products, so the selection agrees with exact arithmetic except for
+ * logits closer than ~1e-12 relative. Outputs: topk_idx [T, k] int32, topk_w [T, k] fp32
+ * (both required), logits [T, E] fp32 (optional, NULL to skip; the double logits
+ * rounded to fp32). Only shape->T, H, E, k are used.
+ */
+moe_status_t moe_mxfp4_route(const moe_mxfp4_shape_t *shape,
+                             const moe_bf16_t *x,
+                             const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                             int32_t *topk_idx, float *topk_w, float *logits,
+                             void *stream);
+
+/*
+ * Expert-sorted permutation of the routed (token, slot) pairs, the grouping the grouped
+ * GEMMs consume. From topk_idx / topk_w [T, k]:
+ *  expert_offsets [E + 1] int32: rows of expert e are [offsets[e], offsets[e+1]).
+ *  sorted_token   [T*k]   int32: token of each sorted row; rows of one expert are in
+ *                                increasing (token, slot) order (a stable sort).
+ *  sorted_weight  [T*k]   fp32 : routing weight of each sorted row.
+ *  slot_row       [T*k]   int32: sorted row of pair (t, j), at index t*k + j.
+ * Only shape->T, E, k are used. topk_idx entries must lie in [0, E).
+ */
+moe_status_t moe_mxfp4_permute(const moe_mxfp4_shape_t *shape,
+                               const int32_t *topk_idx, const float *topk_w,
+                               int32_t *expert_offsets, int32_t *sorted_token,
+                               float *sorted_weight, int32_t *slot_row, void *stream);
+
+/*
+ * Steps 3-4 over the sorted rows (grouped gate_up GEMM with fused MXFP4 dequantization,
+ * bias and clamped SwiGLU):  h[r, :] = swiglu(x[sorted_token[r]] . Wgu[e]^T + bgu[e])
+ * for every row r of expert e. h [T*k, I] bf16 (out). expert_offsets / sorted_token as
+ * produced by moe_mxfp4_permute.
+ */
+moe_status_t moe_mxfp4_expert_up(const moe_mxfp4_shape_t *shape,
+                                 const moe_bf16_t *x,
+                                 const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                                 const moe_bf16_t *gu_bias,
+                                 const int32_t *expert_offsets, const int32_t *sorted_token,
+                                 moe_bf16_t *h, void *stream);
+
+/*
+ * Step 5 over the sorted rows (grouped down GEMM with fused dequantization and bias),
+ * scaled by the row's routing weight: o[r, :] = sorted_weight[r] * (h[r] . Wdn[e]^T + bdn[e]).
+ * o [T*k, H] fp32 (out).
+ */
+moe_status_t moe_mxfp4_expert_down(const moe_mxfp4_shape_t *shape,
+                                   const moe_bf16_t *h,
+                                   const uint8_t *dn_blocks, const uint8_t *dn_scales,
+                                   const moe_bf16_t *dn_bias,
+                                   const int32_t *expert_offsets, const float *sorted_weight,
+                                   float *o, void *stream);
+
+/*
+ * Step 6 (un-permute and weighted sum; the weights are already applied in o):
+ * y[t, :] = sum_{j = 0..k-1} o[slot_row[t*k + j], :], summed in slot order, rounded to bf16.
+ */
+moe_status_t moe_mxfp4_combine(const moe_mxfp4_shape_t *shape,
+                               const float *o, const int32_t *slot_row,
+                               moe_bf16_t *y, void *stream);
+
+/*
+ * Standalone MXFP4 -> bf16 dequantization of a packed [rows, cols] matrix
+ * (ZeroModels GPT-OSS page, "MXFP4 experts"): out[r, c] = e2m1(nibble) * 2^(scale - 127),
+ * exact for scale bytes 2..252. blocks [rows, cols/2], scales [rows, cols/32],
+ * out [rows, cols] bf16. cols must be a positive multiple of 32; rows >= 0.
+ */
+moe_status_t moe_mxfp4_dequant(const uint8_t *blocks, const uint8_t *scales,
+                               int64_t rows, int32_t cols, moe_bf16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

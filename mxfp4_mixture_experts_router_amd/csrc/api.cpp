@@ -1,0 +1,277 @@
+// C ABI of the MXFP4 mixture-of-experts layer: host-side validation, workspace layout
+// and the launch sequence. No allocation, no synchronisation, no state between calls.
+#include "../../include/moe_mxfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+
+#define MOE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+moe_status_t ok() {
+    g_last_error.clear();
+    return MOE_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status_t check_shape(const moe_mxfp4_shape_t *s, bool need_experts) {
+    if (!s) return fail(MOE_EINVAL, "shape is NULL");
+    if (s->T < 0) return fail(MOE_EINVAL, "T = %lld is negative", static_cast<long long>(s->T));
+    if (s->H <= 0 || s->H % 32) return fail(MOE_ESHAPE, "H = %d is not a positive multiple of 32", s->H);
+    if (need_experts && (s->I <= 0 || s->I % 32))
+        return fail(MOE_ESHAPE, "I = %d is not a positive multiple of 32", s->I);
+    if (s->E < 1 || s->E > 256) return fail(MOE_ESHAPE, "E = %d outside 1..256", s->E);
+    if (s->k < 1 || s->k > 8 || s->k > s->E)
+        return fail(MOE_ESHAPE, "k = %d outside 1..min(E, 8) (E = %d)", s->k, s->E);
+    if (s->T > (static_cast<int64_t>(1) << 24))
+        return fail(MOE_ESHAPE, "T = %lld exceeds the supported 2^24 tokens per call",
+                    static_cast<long long>(s->T));
+    if (need_experts && (!std::isfinite(s->swiglu_alpha) || !std::isfinite(s->swiglu_limit)))
+        return fail(MOE_EINVAL, "swiglu_alpha / swiglu_limit must be finite");
+    return MOE_OK;
+}
+
+moe::Dims dims_of(const moe_mxfp4_shape_t *s) {
+    return moe::Dims{s->T, s->H, s->I, s->E, s->k, s->swiglu_alpha, s->swiglu_limit};
+}
+
+// Workspace regions (each 256-byte aligned), in order.
+struct Layout {
+    size_t idx, w, offsets, sorted_token, sorted_w, slot_row, h, o, total;
+};
+
+size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+Layout layout_of(const moe_mxfp4_shape_t *s) {
+    const size_t N = static_cast<size_t>(s->T) * s->k;
+    Layout L{};
+    size_t p = 0;
+    L.idx = p;          p += round_up(N * 4);
+    L.w = p;            p += round_up(N * 4);
+    if (s->T <= moe::kDecodeMaxT) {
+        L.h = p;        p += round_up(N * static_cast<size_t>(s->I) * 2);
+        L.offsets = L.sorted_token = L.sorted_w = L.slot_row = L.o = 0;
+    } else {
+        L.offsets = p;      p += round_up((static_cast<size_t>(s->E) + 1) * 4);
+        L.sorted_token = p; p += round_up(N * 4);
+        L.sorted_w = p;     p += round_up(N * 4);
+        L.slot_row = p;     p += round_up(N * 4);
+        L.h = p;            p += round_up(N * static_cast<size_t>(s->I) * 2);
+        L.o = p;            p += round_up(N * static_cast<size_t>(s->H) * 4);
+    }
+    L.total = p;
+    return L;
+}
+
+moe_status_t hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+#define REQUIRE(ptr, name)                                                            \
+    do {                                                                              \
+        if (!(ptr)) return fail(MOE_EINVAL, "%s is NULL", name);                      \
+    } while (0)
+#define REQUIRE16(ptr, name)                                                          \
+    do {                                                                              \
+        if (!(ptr)) return fail(MOE_EINVAL, "%s is NULL", name);                      \
+        if (!aligned16(ptr)) return fail(MOE_EALIGN, "%s is not 16-byte aligned", name); \
+    } while (0)
+#define LAUNCH(call, what)                                                            \
+    do {                                                                              \
+        moe_status_t st_ = hip_status((call), what);                                  \
+        if (st_ != MOE_OK) return st_;                                                \
+    } while (0)
+
+}  // namespace
+
+MOE_EXPORT int moe_mxfp4_abi_version(void) { return MOE_MXFP4_ABI_VERSION; }
+
+MOE_EXPORT const char *moe_mxfp4_last_error(void) { return g_last_error.c_str(); }
+
+MOE_EXPORT moe_status_t moe_mxfp4_check_shape(const moe_mxfp4_shape_t *shape) {
+    moe_status_t st = check_shape(shape, true);
+    return st != MOE_OK ? st : ok();
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_workspace_bytes(const moe_mxfp4_shape_t *shape, size_t *bytes) {
+    moe_status_t st = check_shape(shape, true);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    REQUIRE(bytes, "bytes");
+    *bytes = layout_of(shape).total;
+    return ok();
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
+                                          const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                                          const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                                          const moe_bf16_t *gu_bias, const uint8_t *dn_blocks,
+                                          const uint8_t *dn_scales, const moe_bf16_t *dn_bias,
+                                          moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
+                                          void *workspace, size_t workspace_bytes, void *stream) {
+    moe_status_t st = check_shape(shape, true);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    REQUIRE16(x, "x");
+    REQUIRE16(router_w, "router_w");
+    REQUIRE(router_b, "router_b");
+    REQUIRE16(gu_blocks, "gu_blocks");
+    REQUIRE(gu_scales, "gu_scales");
+    REQUIRE(gu_bias, "gu_bias");
+    REQUIRE16(dn_blocks, "dn_blocks");
+    REQUIRE(dn_scales, "dn_scales");
+    REQUIRE(dn_bias, "dn_bias");
+    REQUIRE16(y, "y");
+    const Layout L = layout_of(shape);
+    if (!workspace) return fail(MOE_EWORKSPACE, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(MOE_EALIGN, "workspace is not 256-byte aligned");
+    if (workspace_bytes < L.total)
+        return fail(MOE_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+
+    const moe::Dims d = dims_of(shape);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    int32_t *idx = topk_idx ? topk_idx : reinterpret_cast<int32_t *>(ws + L.idx);
+    float *w = topk_w ? topk_w : reinterpret_cast<float *>(ws + L.w);
+    uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
+
+    LAUNCH(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, s), "route");
+    if (shape->T <= moe::kDecodeMaxT) {
+        LAUNCH(moe::launch_up_decode(d, x, gu_blocks, gu_scales, gu_bias, idx, w, h, s), "up (decode)");
+        LAUNCH(moe::launch_down_decode(d, h, dn_blocks, dn_scales, dn_bias, idx, w, y, s), "down (decode)");
+        return ok();
+    }
+    int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+    int32_t *sorted_token = reinterpret_cast<int32_t *>(ws + L.sorted_token);
+    float *sorted_w = reinterpret_cast<float *>(ws + L.sorted_w);
+    int32_t *slot_row = reinterpret_cast<int32_t *>(ws + L.slot_row);
+    float *o = reinterpret_cast<float *>(ws + L.o);
+    LAUNCH(moe::launch_permute(d, idx, w, offsets, sorted_token, sorted_w, slot_row, s), "permute");
+    LAUNCH(moe::launch_up_grouped(d, x, gu_blocks, gu_scales, gu_bias, offsets, sorted_token, h, s), "up");
+    LAUNCH(moe::launch_down_grouped(d, h, dn_blocks, dn_scales, dn_bias, offsets, sorted_w, o, s), "down");
+    LAUNCH(moe::launch_combine(d, o, slot_row, y, s), "combine");
+    return ok();
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_route(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
+                                        const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                                        int32_t *topk_idx, float *topk_w, float *logits,
+                                        void *stream) {
+    moe_status_t st = check_shape(shape, false);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    REQUIRE16(x, "x");
+    REQUIRE16(router_w, "router_w");
+    REQUIRE(router_b, "router_b");
+    REQUIRE(topk_idx, "topk_idx");
+    REQUIRE(topk_w, "topk_w");
+    LAUNCH(moe::launch_route(dims_of(shape), x, router_w, router_b, topk_idx, topk_w, logits,
+                             static_cast<hipStream_t>(stream)), "route");
+    return ok();
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_permute(const moe_mxfp4_shape_t *shape, const int32_t *topk_idx,
+                                          const float *topk_w, int32_t *expert_offsets,
+                                          int32_t *sorted_token, float *sorted_weight,
+                                          int32_t *slot_row, void *stream) {
+    moe_status_t st = check_shape(shape, false);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    REQUIRE(topk_idx, "topk_idx");
+    REQUIRE(topk_w, "topk_w");
+    REQUIRE(expert_offsets, "expert_offsets");
+    REQUIRE(sorted_token, "sorted_token");
+    REQUIRE(sorted_weight, "sorted_weight");
+    REQUIRE(slot_row, "slot_row");
+    LAUNCH(moe::launch_permute(dims_of(shape), topk_idx, topk_w, expert_offsets, sorted_token,
+                               sorted_weight, slot_row, static_cast<hipStream_t>(stream)), "permute");
+    return ok();
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_expert_up(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
+                                            const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                                            const moe_bf16_t *gu_bias, const int32_t *expert_offsets,
+                                            const int32_t *sorted_token, moe_bf16_t *h, void *stream) {
+    moe_status_t st = check_shape(shape, true);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    REQUIRE16(x, "x");
+    REQUIRE16(gu_blocks, "gu_blocks");
+    REQUIRE(gu_scales, "gu_scales");
+    REQUIRE(gu_bias, "gu_bias");
+    REQUIRE(expert_offsets, "expert_offsets");
+    REQUIRE(sorted_token, "sorted_token");
+    REQUIRE16(h, "h");
+    LAUNCH(moe::launch_up_grouped(dims_of(shape), x, gu_blocks, gu_scales, gu_bias, expert_offsets,
+                                  sorted_token, h, static_cast<hipStream_t>(stream)), "up");
+    return ok();
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_expert_down(const moe_mxfp4_shape_t *shape, const moe_bf16_t *h,
+                                              const uint8_t *dn_blocks, const uint8_t *dn_scales,
+                                              const moe_bf16_t *dn_bias, const int32_t *expert_offsets,
+                                              const float *sorted_weight, float *o, void *stream) {
+    moe_status_t st = check_shape(shape, true);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    REQUIRE16(h, "h");
+    REQUIRE16(dn_blocks, "dn_blocks");
+    REQUIRE(dn_scales, "dn_scales");
+    REQUIRE(dn_bias, "dn_bias");
+    REQUIRE(expert_offsets, "expert_offsets");
+    REQUIRE(sorted_weight, "sorted_weight");
+    REQUIRE16(o, "o");
+    LAUNCH(moe::launch_down_grouped(dims_of(shape), h, dn_blocks, dn_scales, dn_bias, expert_offsets,
+                                    sorted_weight, o, static_cast<hipStream_t>(stream)), "down");
+    return ok();
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_combine(const moe_mxfp4_shape_t *shape, const float *o,
+                                          const int32_t *slot_row, moe_bf16_t *y, void *stream) {
+    moe_status_t st = check_shape(shape, false);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    REQUIRE16(o, "o");
+    REQUIRE(slot_row, "slot_row");
+    REQUIRE16(y, "y");
+    LAUNCH(moe::launch_combine(dims_of(shape), o, slot_row, y, static_cast<hipStream_t>(stream)),
+           "combine");
+    return ok();
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_dequant(const uint8_t *blocks, const uint8_t *scales, int64_t rows,
+                                          int32_t cols, moe_bf16_t *out, void *stream) {
+    REQUIRE16(blocks, "blocks");
+    REQUIRE(scales, "scales");
+    REQUIRE16(out, "out");
+    if (rows < 0) return fail(MOE_EINVAL, "rows = %lld is negative", static_cast<long long>(rows));
+    if (cols <= 0 || cols % 32) return fail(MOE_ESHAPE, "cols = %d is not a positive multiple of 32", cols);
+    if (rows * (cols / 32) >= (static_cast<int64_t>(1) << 40))
+        return fail(MOE_ESHAPE, "rows * cols too large");
+    if (rows == 0) return ok();
+    LAUNCH(moe::launch_dequant(blocks, scales, rows, cols, out, static_cast<hipStream_t>(stream)),
+           "dequant");
+    return ok();
+}

@@ -1,0 +1,72 @@
+// Device helpers shared by the gfx950 kernels of the MXFP4 mixture-of-experts layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// E8M0 scale byte -> the fp32 power of two 2^(s - 127) (valid for s in 1..254, which
+// covers the supported 2..252).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) { return __uint_as_float(s << 23); }
+
+// One packed 32-bit word = 8 FP4 E2M1 codes (byte j: low nibble = element 2j, high
+// nibble = element 2j+1) -> 8 bf16 values scaled by `scale`. gfx950 converts a byte to
+// two scaled bf16 values in one instruction (v_cvt_scalef32_pk_bf16_fp4).
+__device__ __forceinline__ bf16x8 mxfp4_word_to_bf16x8(uint32_t word, float scale) {
+    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
+    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
+    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2);
+    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16) on one wavefront.
+// Lane l supplies A row (l % 16) and B column (l % 16), 8 consecutive entries of the
+// contraction each, for contraction group (l / 16); D lane l holds column (l % 16), rows
+// 4 * (l / 16) + 0..3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// sigmoid-gated clamped SwiGLU of the GPT-OSS experts: (clamp(up) + 1) * g * sigmoid(alpha*g)
+// with g = min(gate, limit) and up clamped to [-limit, limit].
+__device__ __forceinline__ float swiglu(float gate, float up, float alpha, float limit) {
+    float g = fminf(gate, limit);
+    float u = fminf(fmaxf(up, -limit), limit);
+    float sig = 1.0f / (1.0f + __expf(-alpha * g));
+    return (u + 1.0f) * g * sig;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    return (1ull << __lane_id()) - 1ull;
+}
+
+}  // namespace moe

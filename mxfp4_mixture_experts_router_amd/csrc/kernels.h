@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe_mxfp4.so).
+// Each returns hipSuccess or the launch error; none synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Token count up to which the forward pass takes the decode path (route -> fused
+// up-projection -> fused down-projection + combine, no sorted permutation in memory).
+constexpr int64_t kDecodeMaxT = 64;
+
+struct Dims {
+    int64_t T;
+    int H, I, E, k;
+    float alpha, limit;
+};
+
+hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *router_w,
+                        const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
+                        float *logits, hipStream_t s);
+
+hipError_t launch_permute(const Dims &d, const int32_t *topk_idx, const float *topk_w,
+                          int32_t *offsets, int32_t *sorted_token, float *sorted_w,
+                          int32_t *slot_row, hipStream_t s);
+
+hipError_t launch_up_grouped(const Dims &d, const uint16_t *x, const uint8_t *gu_blocks,
+                             const uint8_t *gu_scales, const uint16_t *gu_bias,
+                             const int32_t *offsets, const int32_t *sorted_token,
+                             uint16_t *h, hipStream_t s);
+
+hipError_t launch_down_grouped(const Dims &d, const uint16_t *h, const uint8_t *dn_blocks,
+                               const uint8_t *dn_scales, const uint16_t *dn_bias,
+                               const int32_t *offsets, const float *sorted_w, float *o,
+                               hipStream_t s);
+
+hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row,
+                          uint16_t *y, hipStream_t s);
+
+// Decode path (T <= kDecodeMaxT).
+// up: hw[t*k + j, :] = bf16(w[t, j] * swiglu(x[t] . Wgu[e_tj]^T + bgu[e_tj]))
+hipError_t launch_up_decode(const Dims &d, const uint16_t *x, const uint8_t *gu_blocks,
+                            const uint8_t *gu_scales, const uint16_t *gu_bias,
+                            const int32_t *topk_idx, const float *topk_w, uint16_t *hw,
+                            hipStream_t s);
+// down + combine: y[t, :] = bf16(sum_j hw[t*k + j] . Wdn[e_tj]^T + sum_j w[t, j] * bdn[e_tj])
+hipError_t launch_down_decode(const Dims &d, const uint16_t *hw, const uint8_t *dn_blocks,
+                              const uint8_t *dn_scales, const uint16_t *dn_bias,
+                              const int32_t *topk_idx, const float *topk_w, uint16_t *y,
+                              hipStream_t s);
+
+hipError_t launch_dequant(const uint8_t *blocks, const uint8_t *scales, int64_t rows, int cols,
+                          uint16_t *out, hipStream_t s);
+
+}  // namespace moe

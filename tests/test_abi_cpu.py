@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch.
+
+Every call here fails validation (or is a pure host query), so the HIP runtime is
+never asked to launch anything; pointer arguments are fake addresses that are never
+dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_mixture_experts_router_amd as moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe_mxfp4.h")
+EINVAL, ESHAPE, EALIGN, EWORKSPACE = 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.library_path()):
+        from mxfp4_mixture_experts_router_amd import build
+        build.build()
+    return moe.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_mxfp4_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(moe._SIGS), "binding signatures and header disagree"
+
+
+def test_abi_version(lib):
+    assert moe.abi_version() == 1
+    assert "#define MOE_MXFP4_ABI_VERSION 1" in open(HEADER).read()
+
+
+def shape(T=1, H=2880, I=2880, E=32, k=4, alpha=1.702, limit=7.0):
+    return moe._shape(T, H, I, E, k, alpha, limit)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), EINVAL), (dict(H=2881), ESHAPE), (dict(H=0), ESHAPE), (dict(I=48), ESHAPE),
+    (dict(E=0), ESHAPE), (dict(E=257), ESHAPE), (dict(k=0), ESHAPE), (dict(k=9, E=16), ESHAPE),
+    (dict(k=5, E=4), ESHAPE), (dict(T=(1 << 24) + 1), ESHAPE),
+    (dict(alpha=float("nan")), EINVAL), (dict(limit=float("inf")), EINVAL),
+])
+def test_check_shape_rejects(lib, kw, code):
+    s = shape(**kw)
+    assert lib.moe_mxfp4_check_shape(ctypes.byref(s)) == code
+    assert lib.moe_mxfp4_last_error().decode()
+    n = ctypes.c_size_t(12345)
+    assert lib.moe_mxfp4_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == code
+    assert n.value == 12345  # nothing written on error
+
+
+def test_check_shape_null(lib):
+    assert lib.moe_mxfp4_check_shape(None) == EINVAL
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(1, 2880, 2880, 32, 4), (64, 2880, 2880, 32, 4),
+                                       (4096, 2880, 2880, 32, 4), (2048, 2880, 2880, 128, 4),
+                                       (8, 64, 64, 4, 2), (0, 64, 64, 4, 2)])
+def test_workspace_sizes(lib, T, H, I, E, k):
+    s = shape(T, H, I, E, k)
+    assert lib.moe_mxfp4_check_shape(ctypes.byref(s)) == 0
+    assert lib.moe_mxfp4_last_error() == b""
+    n = moe.workspace_bytes(T, H, I, E, k)
+    N = T * k
+    if T <= moe.DECODE_MAX_T:
+        assert n >= N * I * 2 + 2 * N * 4
+    else:
+        assert n >= N * (I * 2 + H * 4) + 3 * N * 4
+    assert n % 256 == 0
+
+
+A = 0x10000  # fake, 16-byte aligned device addresses; never dereferenced
+
+
+def fwd(lib, s, **over):
+    args = dict(x=A, rw=A, rb=A, gb=A, gs=A, gbias=A, db=A, ds=A, dbias=A, y=A, idx=None, w=None,
+                ws=0x100000, wsb=1 << 40, stream=None)
+    args.update(over)
+    return lib.moe_mxfp4_forward(ctypes.byref(s), *[args[k] for k in
+                                 ("x", "rw", "rb", "gb", "gs", "gbias", "db", "ds", "dbias", "y",
+                                  "idx", "w", "ws")], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("field", ["x", "rw", "rb", "gb", "gs", "gbias", "db", "ds", "dbias", "y"])
+def test_forward_null_pointer(lib, field):
+    s = shape()
+    assert fwd(lib, s, **{field: None}) == EINVAL
+    assert "NULL" in lib.moe_mxfp4_last_error().decode()
+
+
+@pytest.mark.parametrize("field", ["x", "rw", "gb", "db", "y"])
+def test_forward_misaligned(lib, field):
+    s = shape()
+    assert fwd(lib, s, **{field: A + 2}) == EALIGN
+
+
+def test_forward_workspace_checks(lib):
+    s = shape()
+    need = moe.workspace_bytes(1, 2880, 2880, 32, 4)
+    assert fwd(lib, s, ws=None) == EWORKSPACE
+    assert fwd(lib, s, wsb=need - 1) == EWORKSPACE
+    assert fwd(lib, s, ws=0x100010) == EALIGN
+
+
+def test_forward_bad_shape_before_pointers(lib):
+    s = shape(k=0)
+    assert fwd(lib, s, x=None) == ESHAPE
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    # T = 0 validates, then returns without touching the device
+    s = shape(T=0)
+    assert fwd(lib, s) == 0
+    assert lib.moe_mxfp4_route(ctypes.byref(s), A, A, A, A, A, None, None) == 0
+
+
+def test_stage_entry_points_validate(lib):
+    s = shape()
+    assert lib.moe_mxfp4_route(ctypes.byref(s), A, A, A, None, A, None, None) == EINVAL
+    assert lib.moe_mxfp4_route(ctypes.byref(s), A + 8, A, A, A, A, None, None) == EALIGN
+    assert lib.moe_mxfp4_permute(ctypes.byref(s), A, A, A, A, A, None, None) == EINVAL
+    assert lib.moe_mxfp4_expert_up(ctypes.byref(s), A, A, A, A, A, A, A + 4, None) == EALIGN
+    assert lib.moe_mxfp4_expert_down(ctypes.byref(s), A, A, A, A, A, None, A, None) == EINVAL
+    assert lib.moe_mxfp4_combine(ctypes.byref(s), A, A, None, None) == EINVAL
+    bad = shape(E=300)
+    assert lib.moe_mxfp4_permute(ctypes.byref(bad), A, A, A, A, A, A, None) == ESHAPE
+
+
+def test_dequant_validates(lib):
+    assert lib.moe_mxfp4_dequant(A, A, 4, 48, A, None) == ESHAPE
+    assert lib.moe_mxfp4_dequant(A, A, -1, 64, A, None) == EINVAL
+    assert lib.moe_mxfp4_dequant(None, A, 4, 64, A, None) == EINVAL
+    assert lib.moe_mxfp4_dequant(A + 1, A, 4, 64, A, None) == EALIGN
+    assert lib.moe_mxfp4_dequant(A, A, 0, 64, A, None) == 0       # empty: no launch
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(moe.MoeLibraryMissing):
+        moe.load_library()

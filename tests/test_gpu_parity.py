@@ -1,0 +1,272 @@
+"""GPU parity: every step of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: dequantized weights, top-k indices and the permutation bit-exact; routing
+weights within 1e-6 relative; h, o and y within per-token relative L2 1e-2 and
+per-element 5e-2 * rms (see gpu_util). Inputs are the seeded workloads (tiny, the
+GPT-OSS-20B decode / batched decode / 4k prefill shapes and the 120B-shaped prefill)
+plus fixtures: non-square H != I, duplicated router rows (ties), zero up rows
+(gate/up interleave), maximal E and k, and ragged token counts on both sides of the
+decode/prefill switch. Full-size configs run in the same launch configuration as the
+benchmark and are compared on a sample of tokens (every token is independent).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_mixture_experts_router_amd as moe
+import oracle
+from workloads import CONFIGS, make_inputs, f32_from_bf16_bits, bf16_bits_from_f32
+
+from gpu_util import (assert_close_rows, bf16_bits, bf16_to_f64, check_selection, host_permutation,
+                      to_dev, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import os
+    if not os.path.exists(moe.library_path()):
+        from mxfp4_mixture_experts_router_amd import build
+        build.build()
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    moe.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _sample(T, n, seed=0):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(T, n - 2, replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s))
+
+
+def _forward(inp_d, k, cfg, **kw):
+    return moe.moe_forward(inp_d["x"], inp_d["router_w"], inp_d["router_b"], inp_d["gu_blocks"],
+                           inp_d["gu_scales"], inp_d["gu_bias"], inp_d["dn_blocks"],
+                           inp_d["dn_scales"], inp_d["dn_bias"], k, cfg.alpha, cfg.limit, **kw)
+
+
+# ----------------------------------------------------------------------------- dequant
+
+def _oracle_bf16_bits(blocks, scales):
+    ref = oracle.dequant(blocks, scales).astype(np.float32)
+    bits = bf16_bits_from_f32(ref)
+    assert np.array_equal(f32_from_bf16_bits(bits), ref)     # exact in bf16
+    return bits
+
+
+def test_dequant_every_byte_and_scale():
+    scales_range = np.arange(2, 253, dtype=np.uint8)            # supported scale bytes
+    rows = scales_range.size
+    blocks = np.tile(np.arange(256, dtype=np.uint8), (rows, 1))   # every byte, every row
+    scales = np.repeat(scales_range[:, None], 512 // 32, axis=1)
+    want = _oracle_bf16_bits(blocks, scales)
+    got = bf16_bits(moe.dequant(to_dev(blocks), to_dev(scales)))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_20b"])
+def test_dequant_expert_banks(name):
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, parts=("gu_blocks", "gu_scales", "dn_blocks", "dn_scales"))
+    e = cfg.E - 1
+    for b, s in (("gu_blocks", "gu_scales"), ("dn_blocks", "dn_scales")):
+        want = _oracle_bf16_bits(inp[b][e], inp[s][e])
+        got = bf16_bits(moe.dequant(to_dev(inp[b][e]), to_dev(inp[s][e])))
+        np.testing.assert_array_equal(got, want)
+    # a whole bank in one call (rows = E * R)
+    want = _oracle_bf16_bits(inp["dn_blocks"][:2], inp["dn_scales"][:2])
+    got = bf16_bits(moe.dequant(to_dev(inp["dn_blocks"][:2]), to_dev(inp["dn_scales"][:2])))
+    np.testing.assert_array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------- route
+
+def _check_route(cfg, inp):
+    ref_logits, abs_sum = oracle.router(inp["x"], inp["router_w"], inp["router_b"], with_abs_sum=True)
+    ref_idx, ref_w = oracle.topk_softmax(ref_logits, cfg.k)
+    ref = {"logits": ref_logits, "abs_sum": abs_sum, "idx": ref_idx, "w": ref_w}
+    d = upload(inp)
+    idx, w, logits = moe.route(d["x"], d["router_w"], d["router_b"], cfg.k, return_logits=True)
+    idx, w, logits = idx.cpu().numpy(), w.cpu().numpy(), logits.cpu().numpy()
+    ok = check_selection(idx, ref, cfg.H, cfg.k)
+    np.testing.assert_allclose(w[ok], ref_w[ok], rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-6)
+    err = np.abs(logits.astype(np.float64) - ref_logits)
+    assert np.all(err <= 2.0 ** -23 * np.abs(ref_logits) + 1e-10 * abs_sum)
+    return idx, ok
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_20b", "batched_decode_20b", "prefill_20b",
+                                  "prefill_120b"])
+def test_route_matches_oracle(name):
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, parts=("x", "router_w", "router_b"))
+    _, ok = _check_route(cfg, inp)
+    assert ok.mean() > 0.99
+
+
+@pytest.mark.parametrize("T", [1, 16, 17, 300])
+def test_route_ties_go_to_lower_index(T):
+    cfg = CONFIGS["tiny"].with_(E=8, k=3, H=96)
+    inp = make_inputs(cfg, seed=5, T=T, parts=("x", "router_w", "router_b"))
+    for dup in (5, 6, 7):
+        inp["router_w"][dup] = inp["router_w"][2]
+        inp["router_b"][dup] = inp["router_b"][2]
+    idx, _ = _check_route(cfg, inp)
+    d = upload(inp)
+    _, _, logits = moe.route(d["x"], d["router_w"], d["router_b"], cfg.k, return_logits=True)
+    lg = logits.cpu().numpy()
+    assert np.array_equal(lg[:, 2], lg[:, 5]) and np.array_equal(lg[:, 2], lg[:, 7])
+    for t in range(T):
+        sel = list(idx[t])
+        for hi in (5, 6, 7):
+            if hi in sel:
+                assert 2 in sel and sel.index(2) < sel.index(hi)
+
+
+def test_route_max_experts_and_k():
+    cfg = CONFIGS["tiny"].with_(E=256, k=8, H=64)
+    inp = make_inputs(cfg, seed=3, T=40, parts=("x", "router_w", "router_b"))
+    _check_route(cfg, inp)
+
+
+# ----------------------------------------------------------------------------- permute
+
+def _random_routing(T, E, k, seed, skew=0.0):
+    rng = np.random.default_rng(seed)
+    p = np.exp(skew * rng.standard_normal(E))
+    p /= p.sum()
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    return idx, w
+
+
+@pytest.mark.parametrize("T,E,k,skew", [(1, 32, 4, 0.0), (64, 32, 4, 2.0), (4096, 32, 4, 0.0),
+                                        (2048, 128, 4, 1.0), (333, 256, 8, 3.0), (1025, 4, 4, 0.0),
+                                        (500, 16, 1, 5.0)])
+def test_permute_is_a_stable_sort(T, E, k, skew):
+    idx, w = _random_routing(T, E, k, seed=T + E, skew=skew)
+    offsets, sorted_token, order, slot_row = host_permutation(idx, E)
+    g_off, g_tok, g_w, g_slot = moe.permute(to_dev(idx), to_dev(w), E)
+    np.testing.assert_array_equal(g_off.cpu().numpy(), offsets)
+    np.testing.assert_array_equal(g_tok.cpu().numpy(), sorted_token)
+    np.testing.assert_array_equal(g_w.cpu().numpy(), w.reshape(-1)[order])
+    np.testing.assert_array_equal(g_slot.cpu().numpy(), slot_row)
+
+
+# ----------------------------------------------------------------------------- grouped experts
+
+def _grouped_case(cfg, T, seed, n_sample):
+    inp = make_inputs(cfg, seed=seed, T=T)
+    tokens = _sample(T, n_sample, seed)
+    ref = oracle.forward(inp, cfg.k, tokens=tokens, alpha=cfg.alpha, limit=cfg.limit,
+                         intermediates=True)
+    # the routing of all tokens (the permutation needs every row): oracle router + top-k
+    logits = oracle.router(inp["x"], inp["router_w"], inp["router_b"])
+    idx, w = oracle.topk_softmax(logits, cfg.k)
+    assert np.array_equal(idx[tokens], ref["idx"])
+    return inp, tokens, ref, idx, w
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k", [
+    ("tiny", 8, 64, 64, 4, 2), ("tiny", 200, 96, 64, 5, 2), ("tiny", 333, 64, 128, 3, 2),
+    ("prefill_20b", 4096, 2880, 2880, 32, 4), ("prefill_120b", 2048, 2880, 2880, 128, 4)])
+def test_expert_up_and_down_grouped(name, T, H, I, E, k):
+    cfg = CONFIGS[name].with_(H=H, I=I, E=E, k=k)
+    inp, tokens, ref, idx, w = _grouped_case(cfg, T, seed=7, n_sample=24)
+    offsets, sorted_token, order, slot_row = host_permutation(idx, E)
+    d = upload(inp)
+    h = moe.expert_up(d["x"], d["gu_blocks"], d["gu_scales"], d["gu_bias"], to_dev(offsets),
+                      to_dev(sorted_token), k, cfg.alpha, cfg.limit)
+    rows = slot_row.reshape(T, k)[tokens]                      # [n, k] sorted rows of the sample
+    h_np = bf16_to_f64(h)
+    assert_close_rows(h_np[rows.reshape(-1)], ref["h"].reshape(-1, I), "h")
+    # down: feed the oracle's h (rounded to bf16) so this step is checked on its own
+    h_in = np.zeros((T * k, I), dtype=np.uint16)
+    h_in[rows.reshape(-1)] = bf16_bits_from_f32(ref["h"].reshape(-1, I).astype(np.float32))
+    sorted_w = w.reshape(-1)[order].astype(np.float32)
+    o = moe.expert_down(to_dev(h_in), d["dn_blocks"], d["dn_scales"], d["dn_bias"], to_dev(offsets),
+                        to_dev(sorted_w), k)
+    o_np = o.cpu().numpy().astype(np.float64)[rows.reshape(-1)]
+    want = (ref["o"] * ref["w"][:, :, None]).reshape(-1, H)
+    assert_close_rows(o_np, want, "o")
+    # combine of the GPU's o: the sampled tokens' y against the oracle
+    y = bf16_to_f64(moe.combine(o, to_dev(slot_row), k))
+    assert_close_rows(y[tokens], ref["y"], "y from combine")
+
+
+# ----------------------------------------------------------------------------- whole layer
+
+FORWARD_CASES = [
+    # (config, T override, H, I, E, k, tokens compared)
+    ("tiny", None, None, None, None, None, 64),
+    ("tiny", 1, 96, 64, 5, 2, 64),          # non-square, decode path
+    ("tiny", 64, 64, 128, 4, 3, 64),        # non-square, largest decode batch
+    ("tiny", 65, 96, 64, 5, 2, 65),         # non-square, smallest prefill batch
+    ("tiny", 300, 64, 128, 3, 2, 300),      # few experts: several ragged m-tiles each
+    ("tiny", 17, 64, 64, 256, 8, 17),       # maximal E and k, decode path
+    ("tiny", 140, 64, 64, 256, 8, 140),     # maximal E and k, prefill path
+    ("decode_20b", None, None, None, None, None, 1),
+    ("batched_decode_20b", None, None, None, None, None, 64),
+    ("prefill_20b", None, None, None, None, None, 24),
+    ("prefill_120b", None, None, None, None, None, 24),
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k,n_cmp", FORWARD_CASES)
+def test_forward_matches_oracle(name, T, H, I, E, k, n_cmp):
+    cfg = CONFIGS[name]
+    over = {key: v for key, v in dict(H=H, I=I, E=E, k=k).items() if v is not None}
+    cfg = cfg.with_(**over)
+    T = cfg.T if T is None else T
+    inp = make_inputs(cfg, seed=1, T=T)
+    tokens = _sample(T, n_cmp, seed=T)
+    ref = oracle.forward(inp, cfg.k, tokens=tokens, alpha=cfg.alpha, limit=cfg.limit)
+    d = upload(inp)
+    y, idx, w = _forward(d, cfg.k, cfg, return_topk=True)
+    y_np = bf16_to_f64(y)[tokens]
+    idx_np = idx.cpu().numpy()[tokens]
+    ok = check_selection(idx_np, ref, cfg.H, cfg.k)
+    np.testing.assert_allclose(w.cpu().numpy()[tokens][ok], ref["w"][ok], rtol=1e-6, atol=1e-7)
+    assert_close_rows(y_np[ok], ref["y"][ok], f"y ({name}, T={T})")
+    # determinism: a second call is bit-identical
+    y2 = _forward(d, cfg.k, cfg)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [3, 100])
+def test_forward_interleave_fixture(T):
+    """Up rows all zero and up bias -1: every h is 0, so y = sum_j w_j * b_dn[e_j]."""
+    cfg = CONFIGS["tiny"].with_(H=64, I=96, E=4, k=2)
+    inp = make_inputs(cfg, seed=9, T=T)
+    inp["gu_blocks"].reshape(4, 2 * 96, 32)[:, 1::2, :] = 0
+    inp["gu_bias"][:, 1::2] = bf16_bits_from_f32(np.array([-1.0], dtype=np.float32))[0]
+    ref = oracle.forward(inp, cfg.k)
+    y = bf16_to_f64(_forward(upload(inp), cfg.k, cfg))
+    assert_close_rows(y, ref["y"], "interleave fixture")
+
+
+@pytest.mark.parametrize("T", [1, 64, 65, 1000])
+def test_forward_tie_fixture(T):
+    cfg = CONFIGS["tiny"].with_(E=8, k=3, H=64, I=64)
+    inp = make_inputs(cfg, seed=21, T=T)
+    for dup in (3, 6):
+        inp["router_w"][dup] = inp["router_w"][1]
+        inp["router_b"][dup] = inp["router_b"][1]
+    tokens = _sample(T, 64, seed=1)
+    ref = oracle.forward(inp, cfg.k, tokens=tokens)
+    y, idx, _ = _forward(upload(inp), cfg.k, cfg, return_topk=True)
+    np.testing.assert_array_equal(idx.cpu().numpy()[tokens], ref["idx"])
+    assert_close_rows(bf16_to_f64(y)[tokens], ref["y"], "tie fixture")
+
+
+def test_forward_zero_tokens():
+    cfg = CONFIGS["tiny"]
+    inp = upload(make_inputs(cfg, T=0))
+    y = _forward(inp, cfg.k, cfg)
+    assert y.shape == (0, cfg.H)

@@ -26,7 +26,7 @@ from typing import Dict, Tuple
 
 import numpy as np
 
-__all__ = ["MoeConfig", "CONFIGS", "TENSOR_IDS", "make_inputs", "bf16_bits_from_f32",
+__all__ = ["MoeConfig", "CONFIGS", "TENSOR_IDS", "ALL_PARTS", "make_inputs", "bf16_bits_from_f32",
            "f32_from_bf16_bits", "shape_of"]
 
 TENSOR_IDS = {
@@ -108,32 +108,44 @@ def _scales(cfg, tensor, seed, shape) -> np.ndarray:
     return (127 + e).astype(np.uint8)
 
 
-def make_inputs(cfg: MoeConfig, seed: int = 0, T: int | None = None) -> Dict[str, np.ndarray]:
-    """Draw every input tensor of ``cfg`` (host numpy arrays).
+ALL_PARTS = ("x", "router_w", "router_b", "gu_blocks", "gu_scales", "gu_bias", "dn_blocks",
+             "dn_scales", "dn_bias")
+
+
+def make_inputs(cfg: MoeConfig, seed: int = 0, T: int | None = None,
+                parts=ALL_PARTS) -> Dict[str, np.ndarray]:
+    """Draw the input tensors of ``cfg`` (host numpy arrays).
 
     ``T`` overrides the token count (the weights do not depend on it; ``x`` is
-    drawn for that many tokens).
+    drawn for that many tokens). ``parts`` selects which tensors to draw; each
+    tensor has its own random stream, so a subset has the same values as in the
+    full set.
     """
     T = cfg.T if T is None else T
     H, I, E = cfg.H, cfg.I, cfg.E
     if H % 32 or I % 32:
         raise ValueError("H and I must be multiples of the 32-element scale block")
-    x = _normal_bf16(cfg, "x", seed, (T, H), 1.0)
-    router_w = _normal_bf16(cfg, "router_w", seed, (E, H), cfg.router_w_std)
-    b = _rng(cfg, "router_b", seed).standard_normal(size=(E,), dtype=np.float32)
-    b = b * np.float32(cfg.router_b_std)
-    if cfg.expert_offset_std:
-        off = _rng(cfg, "expert_offset", seed).standard_normal(size=(E,), dtype=np.float32)
-        b = b + off * np.float32(cfg.expert_offset_std)
-    router_b = bf16_bits_from_f32(b)
-    return {
-        "x": x,
-        "router_w": router_w,
-        "router_b": router_b,
-        "gu_blocks": _bytes(cfg, "gu_blocks", seed, (E, 2 * I, H // 2)),
-        "gu_scales": _scales(cfg, "gu_scales", seed, (E, 2 * I, H // 32)),
-        "gu_bias": _normal_bf16(cfg, "gu_bias", seed, (E, 2 * I), cfg.bias_std),
-        "dn_blocks": _bytes(cfg, "dn_blocks", seed, (E, H, I // 2)),
-        "dn_scales": _scales(cfg, "dn_scales", seed, (E, H, I // 32)),
-        "dn_bias": _normal_bf16(cfg, "dn_bias", seed, (E, H), cfg.bias_std),
+
+    def router_bias():
+        b = _rng(cfg, "router_b", seed).standard_normal(size=(E,), dtype=np.float32)
+        b = b * np.float32(cfg.router_b_std)
+        if cfg.expert_offset_std:
+            off = _rng(cfg, "expert_offset", seed).standard_normal(size=(E,), dtype=np.float32)
+            b = b + off * np.float32(cfg.expert_offset_std)
+        return bf16_bits_from_f32(b)
+
+    makers = {
+        "x": lambda: _normal_bf16(cfg, "x", seed, (T, H), 1.0),
+        "router_w": lambda: _normal_bf16(cfg, "router_w", seed, (E, H), cfg.router_w_std),
+        "router_b": router_bias,
+        "gu_blocks": lambda: _bytes(cfg, "gu_blocks", seed, (E, 2 * I, H // 2)),
+        "gu_scales": lambda: _scales(cfg, "gu_scales", seed, (E, 2 * I, H // 32)),
+        "gu_bias": lambda: _normal_bf16(cfg, "gu_bias", seed, (E, 2 * I), cfg.bias_std),
+        "dn_blocks": lambda: _bytes(cfg, "dn_blocks", seed, (E, H, I // 2)),
+        "dn_scales": lambda: _scales(cfg, "dn_scales", seed, (E, H, I // 32)),
+        "dn_bias": lambda: _normal_bf16(cfg, "dn_bias", seed, (E, H), cfg.bias_std),
     }
+    unknown = set(parts) - set(makers)
+    if unknown:
+        raise ValueError(f"unknown input tensors {sorted(unknown)}")
+    return {name: makers[name]() for name in ALL_PARTS if name in parts}
