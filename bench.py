@@ -1,0 +1,423 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 mixture-of-experts layer on one MI355X.
+
+One step = one call of the whole layer (router, top-k + softmax, permutation,
+gate_up GEMM + SwiGLU, down GEMM, combine) on one batch of synthetic tokens whose
+inputs are already resident in HBM. The headline workload is the GPT-OSS-20B
+shaped single-token decode (T=1, H=I=2880, E=32, top-4); the 4096-token prefill of
+the same layer is measured as a secondary workload in the same run.
+
+Timing: W untimed warmup steps, then K steps bracketed by torch.cuda.synchronize()
+and HIP events on the stream the kernels run on. The weights are replicated R
+times (and x drawn R times) and the steps rotate over the replicas so that the
+256 MB last-level cache cannot serve a step's weights from the previous step.
+By default the K steps are replayed from a HIP graph captured over one rotation
+(--mode eager launches every call from Python instead).
+
+Also reported, in the same JSON line:
+* roofline: the dominant kernel's average duration, measured with HIP events
+  recorded between the kernels of moe_mxfp4_forward_timed calls, turned into
+  achieved GB/s (HBM-bound decode) or TFLOP/s (MFMA-bound prefill) from its
+  algorithmic bytes or flops per launch, against MI355X's published peak;
+  `traffic` comes from the committed rocprofv3 counter summary for that kernel
+  when its source has not changed since;
+* cpu_baseline: the CPU oracle timed on this host on a bounded sample of tokens.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode graph|eager]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s, 20B shape, decode & 4k prefill; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+LLC_BYTES = 256 << 20            # MI355X Infinity Cache
+KERNEL_SOURCES = {               # kernel -> files whose text defines it
+    "route": ["route.hip", "device_common.h"],
+    "permute": ["permute.hip", "device_common.h"],
+    "up_decode": ["gemm_decode.hip", "device_common.h"],
+    "down_decode": ["gemm_decode.hip", "device_common.h"],
+    "up_grouped": ["gemm_grouped.hip", "device_common.h"],
+    "down_grouped": ["gemm_grouped.hip", "device_common.h"],
+    "combine": ["gemm_grouped.hip", "device_common.h"],
+}
+DECODE_STAGES = ["route", "up_decode", "down_decode"]
+PREFILL_STAGES = ["route", "permute", "up_grouped", "down_grouped", "combine"]
+
+
+def kernel_source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "mxfp4_mixture_experts_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode_20b")
+    ap.add_argument("--secondary", default="prefill_20b", help="'' to skip")
+    ap.add_argument("--secondary-steps", type=int, default=100)
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to defeat the LLC")
+    ap.add_argument("--timed-steps", type=int, default=200, help="steps of the per-kernel timing run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the CPU sample (0 = auto)")
+    return ap.parse_args()
+
+
+class Hip:
+    """The HIP runtime already loaded in this process (the one torch and the library use)."""
+
+    def __init__(self):
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                m = re.search(r"(/\S*libamdhip64\.so\S*)", line)
+                if m:
+                    path = m.group(1)
+                    break
+        self.lib = ctypes.CDLL(path or "libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+class Workload:
+    """R replicas of one layer's weights and R batches of tokens, resident on the GPU."""
+
+    WEIGHTS = ("router_w", "router_b", "gu_blocks", "gu_scales", "gu_bias", "dn_blocks",
+               "dn_scales", "dn_bias")
+
+    @classmethod
+    def create(cls, name: str, replicas: int):
+        import numpy as np
+        import torch
+        import mxfp4_mixture_experts_router_amd as moe
+        from workloads import CONFIGS, make_inputs
+
+        self = cls()
+        cfg = CONFIGS[name]
+        self.name, self.cfg = name, cfg
+        dev = torch.device("cuda:0")
+
+        def up(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        host_w = make_inputs(cfg, seed=0, parts=self.WEIGHTS)
+        self.host_weights = host_w
+        layer_bytes = sum(v.nbytes for v in host_w.values())
+        if replicas <= 0:
+            touched = self.touched_weight_bytes_estimate(cfg, layer_bytes)
+            replicas = max(2, min(16, -(-2 * LLC_BYTES // max(touched, 1)) + 1))
+        self.R = replicas
+        base = {k: up(v) for k, v in host_w.items()}
+        self.weights = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(replicas - 1)]
+        self.host_x = [make_inputs(cfg, seed=r, parts=("x",))["x"] for r in range(replicas)]
+        self.x = [up(x) for x in self.host_x]
+        T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+        self.shape = moe._shape(T, H, I, E, k, cfg.alpha, cfg.limit)
+        self.y = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(replicas)]
+        self.idx = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(replicas)]
+        self.w = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(replicas)]
+        nbytes = moe.workspace_bytes(T, H, I, E, k)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.lib = moe.load_library()
+        self.layer_bytes = layer_bytes
+        return self
+
+    @staticmethod
+    def touched_weight_bytes_estimate(cfg, layer_bytes):
+        per_expert = layer_bytes / cfg.E
+        return int(min(cfg.E, cfg.T * cfg.k) * per_expert)
+
+    def args(self, r: int, stream_ptr: int):
+        w = self.weights[r]
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        return (ctypes.byref(self.shape), P(self.x[r]), P(w["router_w"]), P(w["router_b"]),
+                P(w["gu_blocks"]), P(w["gu_scales"]), P(w["gu_bias"]), P(w["dn_blocks"]),
+                P(w["dn_scales"]), P(w["dn_bias"]), P(self.y[r]), P(self.idx[r]), P(self.w[r]),
+                P(self.ws), self.ws.numel(), ctypes.c_void_p(stream_ptr))
+
+    def step(self, r: int, stream_ptr: int):
+        st = self.lib.moe_mxfp4_forward(*self.args(r, stream_ptr))
+        if st != 0:
+            raise RuntimeError(self.lib.moe_mxfp4_last_error().decode())
+
+
+def run_timed(wl: Workload, steps: int, warmup: int, mode: str):
+    """Whole-layer throughput. Returns (ms_per_step, wall_ms_per_step, mode_used)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(max(warmup, wl.R)):
+        wl.step(i % wl.R, stream.cuda_stream)
+    torch.cuda.synchronize()
+    reps = max(1, -(-steps // wl.R))
+    steps = reps * wl.R
+    graph = None
+    if mode == "graph":
+        ref = [y.clone() for y in wl.y]
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for r in range(wl.R):
+                wl.step(r, side.cuda_stream)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for r in range(wl.R):
+                wl.step(r, cap.cuda_stream)
+        for y in wl.y:
+            y.zero_()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            for y, want in zip(wl.y, ref):
+                if not torch.equal(y.view(torch.int16), want.view(torch.int16)):
+                    raise RuntimeError("graph replay differs from eager launches")
+            for y in wl.y:
+                y.zero_()
+        for _ in range(2):
+            graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    if graph is not None:
+        for _ in range(reps):
+            graph.replay()
+    else:
+        sp = stream.cuda_stream
+        for i in range(steps):
+            wl.step(i % wl.R, sp)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    gpu_ms = start.elapsed_time(end)
+    return gpu_ms / steps, wall / steps, steps, mode
+
+
+def run_per_kernel(wl: Workload, steps: int, hip: Hip):
+    """Average duration of each kernel of the layer, from events recorded between them."""
+    import torch
+    import mxfp4_mixture_experts_router_amd as moe
+    lib = wl.lib
+    stream = torch.cuda.current_stream()
+    n_ev = moe.MAX_LAUNCHES + 1
+    events = [[hip.event() for _ in range(n_ev)] for _ in range(steps)]
+    arrays = [(ctypes.c_void_p * n_ev)(*evs) for evs in events]
+    n_launch = ctypes.c_int(0)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        st = lib.moe_mxfp4_forward_timed(*wl.args(i % wl.R, stream.cuda_stream), arrays[i], n_ev,
+                                         ctypes.byref(n_launch))
+        if st != 0:
+            raise RuntimeError(lib.moe_mxfp4_last_error().decode())
+    torch.cuda.synchronize()
+    n = n_launch.value
+    sums = [0.0] * n
+    for evs in events:
+        for j in range(n):
+            sums[j] += hip.elapsed_ms(evs[j], evs[j + 1])
+    for evs in events:
+        for ev in evs:
+            hip.destroy(ev)
+    return [s / steps * 1e3 for s in sums]   # microseconds
+
+
+def distinct_experts(wl: Workload):
+    import numpy as np
+    return float(np.mean([len(np.unique(i.cpu().numpy())) for i in wl.idx]))
+
+
+def kernel_work(wl: Workload, kernel: str, D: float):
+    """Algorithmic bytes and flops of one launch of `kernel` (what the method must move or
+    compute; D = distinct routed experts)."""
+    c = wl.cfg
+    T, H, I, E, k = c.T, c.H, c.I, c.E, c.k
+    N = T * k
+    gu_expert = 2 * I * (H // 2) + 2 * I * (H // 32) + 2 * I * 2      # packed + scales + bias
+    dn_expert = H * (I // 2) + H * (I // 32) + H * 2
+    if kernel == "route":
+        return T * H * 2 + E * H * 2 + E * 2 + N * 8, 2 * T * E * H
+    if kernel == "permute":
+        return N * 8 + (E + 1) * 4 + N * 12, 0
+    if kernel == "up_decode":
+        return D * gu_expert + T * H * 2 + N * 8 + N * I * 2, 2 * N * 2 * I * H
+    if kernel == "down_decode":
+        return D * dn_expert + N * I * 2 + N * 8 + T * H * 2, 2 * N * H * I
+    if kernel == "up_grouped":
+        return D * gu_expert + T * H * 2 + N * 4 + N * I * 2, 2 * N * 2 * I * H
+    if kernel == "down_grouped":
+        return D * dn_expert + N * I * 2 + N * 4 + N * H * 4, 2 * N * H * I
+    if kernel == "combine":
+        return N * H * 4 + N * 4 + T * H * 2, 0
+    raise KeyError(kernel)
+
+
+def load_traffic(workload: str, kernel: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("{"):
+            rec = json.loads(line)
+            if rec.get("source_sha") == kernel_source_sha(kernel):
+                return rec.get("traffic_bytes")
+    return None
+
+
+def roofline_for(wl: Workload, stages, kernel_us, D):
+    entries = []
+    for name, us in zip(stages, kernel_us):
+        nbytes, flops = kernel_work(wl, name, D)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        tfs = flops / (us * 1e-6) / 1e12
+        entries.append({"kernel": name, "avg_us": round(us, 3), "alg_bytes": int(nbytes),
+                        "alg_flops": int(flops), "GB/s": round(gbs, 1), "TFLOP/s": round(tfs, 2)})
+    dom = max(range(len(entries)), key=lambda i: entries[i]["avg_us"])
+    e = entries[dom]
+    # bound: arithmetic intensity against the bf16 ridge point
+    intensity = e["alg_flops"] / max(e["alg_bytes"], 1)
+    if intensity > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": e["TFLOP/s"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(e["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": e["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(e["GB/s"] / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = e["kernel"]
+    roof["alg_bytes_per_launch"] = e["alg_bytes"]
+    roof["alg_flops_per_launch"] = e["alg_flops"]
+    roof["avg_us"] = e["avg_us"]
+    roof["traffic"] = load_traffic(wl.name, e["kernel"])
+    return roof, entries
+
+
+def measure(name, steps, warmup, mode, replicas, timed_steps, hip):
+    wl = Workload.create(name, replicas)
+    ms, wall_ms, steps_run, mode = run_timed(wl, steps, warmup, mode)
+    D = distinct_experts(wl)
+    stages = DECODE_STAGES if wl.cfg.T <= 64 else PREFILL_STAGES
+    kus = run_per_kernel(wl, timed_steps, hip)
+    roof, kernels = roofline_for(wl, stages, kus, D)
+    layer_bytes = sum(kernel_work(wl, s, D)[0] for s in stages)
+    layer_flops = sum(kernel_work(wl, s, D)[1] for s in stages)
+    return wl, {
+        "ms_per_step": ms, "wall_ms_per_step": wall_ms, "steps": steps_run, "mode": mode,
+        "value": wl.cfg.T / (ms * 1e-3), "distinct_experts": D, "roofline": roof,
+        "kernels": kernels,
+        "layer": {"alg_bytes": int(layer_bytes), "alg_flops": int(layer_flops),
+                  "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+    }
+
+
+def cpu_baseline(wl: Workload, sample: int):
+    import numpy as np
+    import oracle
+    from workloads import make_inputs
+    cores = oracle.max_threads()
+    n = sample if sample > 0 else max(16, 4 * cores)
+    inp = dict(wl.host_weights)
+    inp["x"] = make_inputs(wl.cfg, seed=10_000, T=n, parts=("x",))["x"]
+    t0 = time.perf_counter()
+    oracle.forward(inp, wl.cfg.k, alpha=wl.cfg.alpha, limit=wl.cfg.limit)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} tokens of the {wl.name} layer (same weights), plain fp64 C oracle, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is a design note, not part of this build).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mxfp4_mixture_experts_router_amd as moe
+    if not os.path.exists(moe.library_path()):
+        from mxfp4_mixture_experts_router_amd import build
+        build.build()
+    moe.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    hip = Hip()
+    wl, main_res = measure(args.workload, args.steps, args.warmup, args.mode, args.replicas,
+                           args.timed_steps, hip)
+    cfg = wl.cfg
+    out = {
+        "metric": METRIC,
+        "value": round(main_res["value"], 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": main_res["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k,
+                   "experts": "mxfp4 e2m1 + e8m0 per 32", "replicas": wl.R, "mode": main_res["mode"],
+                   "distinct_experts_per_step": main_res["distinct_experts"]},
+        "roofline": main_res["roofline"],
+        "layer_roofline": main_res["layer"],
+        "wall_ms_per_step": round(main_res["wall_ms_per_step"], 6),
+        "kernels": main_res["kernels"],
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    del wl
+    torch.cuda.empty_cache()
+    if args.secondary:
+        wl2, res2 = measure(args.secondary, args.secondary_steps, min(args.warmup, 10), args.mode,
+                            0, min(args.timed_steps, 50), hip)
+        out["secondary"] = {
+            "workload": wl2.cfg.name, "T": wl2.cfg.T, "E": wl2.cfg.E,
+            "value": round(res2["value"], 1), "unit": "tokens/s",
+            "ms_per_step": round(res2["ms_per_step"], 6), "steps": res2["steps"],
+            "replicas": wl2.R, "roofline": res2["roofline"], "layer_roofline": res2["layer"],
+            "kernels": res2["kernels"]}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -110,6 +110,30 @@ moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape,
                                moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* Most kernels one moe_mxfp4_forward call launches. */
+#define MOE_MXFP4_MAX_LAUNCHES 5
+
+/*
+ * moe_mxfp4_forward with timing instrumentation for profilers and benchmarks: the same
+ * validation, kernels and results, plus hipEventRecord calls on `stream` between the
+ * launches. `events` holds at least MOE_MXFP4_MAX_LAUNCHES + 1 hipEvent_t handles created
+ * by the caller (timing enabled); events[0] is recorded before the first kernel and
+ * events[i] right after the i-th. *n_launches receives the number of kernels launched:
+ * 3 for T <= 64 (route, up-projection, down-projection with the combine folded in) and
+ * 5 otherwise (route, permute, up-projection, down-projection, combine). MOE_EINVAL if
+ * events, an events[i] or n_launches is NULL, or n_events is too small.
+ */
+moe_status_t moe_mxfp4_forward_timed(const moe_mxfp4_shape_t *shape,
+                                     const moe_bf16_t *x,
+                                     const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                                     const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                                     const moe_bf16_t *gu_bias,
+                                     const uint8_t *dn_blocks, const uint8_t *dn_scales,
+                                     const moe_bf16_t *dn_bias,
+                                     moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
+                                     void *workspace, size_t workspace_bytes, void *stream,
+                                     void *const *events, int n_events, int *n_launches);
+
 /*
  * Steps 1-2 only (router, top-k, softmax). Logits are accumulated in double precision
  * from the exact bf16 products, so the selection agrees with exact arithmetic except for

@@ -32,6 +32,7 @@ _LIB_PATH = os.path.join(_PKG, "libmoe_mxfp4.so")
 _lib = None
 
 DECODE_MAX_T = 64
+MAX_LAUNCHES = 5
 
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ESHAPE", 3: "MOE_EALIGN", 4: "MOE_EWORKSPACE",
           5: "MOE_EHIP"}
@@ -60,6 +61,8 @@ _SIGS = {
     "moe_mxfp4_check_shape": (ctypes.c_int, [ctypes.POINTER(Shape)]),
     "moe_mxfp4_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)]),
     "moe_mxfp4_forward": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 13 + [ctypes.c_size_t, _vp]),
+    "moe_mxfp4_forward_timed": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 13
+                                + [ctypes.c_size_t, _vp, _vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
     "moe_mxfp4_route": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 7),
     "moe_mxfp4_permute": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 7),
     "moe_mxfp4_expert_up": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 8),

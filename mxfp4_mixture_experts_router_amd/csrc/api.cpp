@@ -123,15 +123,29 @@ MOE_EXPORT moe_status_t moe_mxfp4_workspace_bytes(const moe_mxfp4_shape_t *shape
     return ok();
 }
 
-MOE_EXPORT moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
-                                          const moe_bf16_t *router_w, const moe_bf16_t *router_b,
-                                          const uint8_t *gu_blocks, const uint8_t *gu_scales,
-                                          const moe_bf16_t *gu_bias, const uint8_t *dn_blocks,
-                                          const uint8_t *dn_scales, const moe_bf16_t *dn_bias,
-                                          moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
-                                          void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+// Validation + launch sequence shared by moe_mxfp4_forward and moe_mxfp4_forward_timed.
+// With `events`, events[0] is recorded before the first launch and events[i] after the
+// i-th launch, on the same stream.
+moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
+                         const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                         const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                         const moe_bf16_t *gu_bias, const uint8_t *dn_blocks,
+                         const uint8_t *dn_scales, const moe_bf16_t *dn_bias, moe_bf16_t *y,
+                         int32_t *topk_idx, float *topk_w, void *workspace, size_t workspace_bytes,
+                         void *stream, void *const *events, int n_events, int *n_launches) {
     moe_status_t st = check_shape(shape, true);
     if (st != MOE_OK) return st;
+    if (events) {
+        if (n_events < MOE_MXFP4_MAX_LAUNCHES + 1)
+            return fail(MOE_EINVAL, "n_events = %d, at least %d needed", n_events,
+                        MOE_MXFP4_MAX_LAUNCHES + 1);
+        for (int i = 0; i <= MOE_MXFP4_MAX_LAUNCHES; ++i)
+            if (!events[i]) return fail(MOE_EINVAL, "events[%d] is NULL", i);
+        REQUIRE(n_launches, "n_launches");
+        *n_launches = 0;
+    }
     if (shape->T == 0) return ok();
     REQUIRE16(x, "x");
     REQUIRE16(router_w, "router_w");
@@ -156,11 +170,27 @@ MOE_EXPORT moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape, const 
     int32_t *idx = topk_idx ? topk_idx : reinterpret_cast<int32_t *>(ws + L.idx);
     float *w = topk_w ? topk_w : reinterpret_cast<float *>(ws + L.w);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
+    int launched = 0;
+    auto mark = [&]() -> moe_status_t {
+        if (!events) return MOE_OK;
+        hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[launched]), s);
+        if (e != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
+        *n_launches = launched;
+        return MOE_OK;
+    };
+#define STEP(call, what)                                 \
+    do {                                                 \
+        LAUNCH(call, what);                              \
+        ++launched;                                      \
+        moe_status_t m_ = mark();                        \
+        if (m_ != MOE_OK) return m_;                     \
+    } while (0)
 
-    LAUNCH(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, s), "route");
+    if (moe_status_t m0 = mark(); m0 != MOE_OK) return m0;
+    STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, s), "route");
     if (shape->T <= moe::kDecodeMaxT) {
-        LAUNCH(moe::launch_up_decode(d, x, gu_blocks, gu_scales, gu_bias, idx, w, h, s), "up (decode)");
-        LAUNCH(moe::launch_down_decode(d, h, dn_blocks, dn_scales, dn_bias, idx, w, y, s), "down (decode)");
+        STEP(moe::launch_up_decode(d, x, gu_blocks, gu_scales, gu_bias, idx, w, h, s), "up (decode)");
+        STEP(moe::launch_down_decode(d, h, dn_blocks, dn_scales, dn_bias, idx, w, y, s), "down (decode)");
         return ok();
     }
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
@@ -168,11 +198,38 @@ MOE_EXPORT moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape, const 
     float *sorted_w = reinterpret_cast<float *>(ws + L.sorted_w);
     int32_t *slot_row = reinterpret_cast<int32_t *>(ws + L.slot_row);
     float *o = reinterpret_cast<float *>(ws + L.o);
-    LAUNCH(moe::launch_permute(d, idx, w, offsets, sorted_token, sorted_w, slot_row, s), "permute");
-    LAUNCH(moe::launch_up_grouped(d, x, gu_blocks, gu_scales, gu_bias, offsets, sorted_token, h, s), "up");
-    LAUNCH(moe::launch_down_grouped(d, h, dn_blocks, dn_scales, dn_bias, offsets, sorted_w, o, s), "down");
-    LAUNCH(moe::launch_combine(d, o, slot_row, y, s), "combine");
+    STEP(moe::launch_permute(d, idx, w, offsets, sorted_token, sorted_w, slot_row, s), "permute");
+    STEP(moe::launch_up_grouped(d, x, gu_blocks, gu_scales, gu_bias, offsets, sorted_token, h, s), "up");
+    STEP(moe::launch_down_grouped(d, h, dn_blocks, dn_scales, dn_bias, offsets, sorted_w, o, s), "down");
+    STEP(moe::launch_combine(d, o, slot_row, y, s), "combine");
+#undef STEP
     return ok();
+}
+
+}  // namespace
+
+MOE_EXPORT moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
+                                          const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                                          const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                                          const moe_bf16_t *gu_bias, const uint8_t *dn_blocks,
+                                          const uint8_t *dn_scales, const moe_bf16_t *dn_bias,
+                                          moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
+                                          void *workspace, size_t workspace_bytes, void *stream) {
+    return run_forward(shape, x, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks,
+                       dn_scales, dn_bias, y, topk_idx, topk_w, workspace, workspace_bytes, stream,
+                       nullptr, 0, nullptr);
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_forward_timed(
+    const moe_mxfp4_shape_t *shape, const moe_bf16_t *x, const moe_bf16_t *router_w,
+    const moe_bf16_t *router_b, const uint8_t *gu_blocks, const uint8_t *gu_scales,
+    const moe_bf16_t *gu_bias, const uint8_t *dn_blocks, const uint8_t *dn_scales,
+    const moe_bf16_t *dn_bias, moe_bf16_t *y, int32_t *topk_idx, float *topk_w, void *workspace,
+    size_t workspace_bytes, void *stream, void *const *events, int n_events, int *n_launches) {
+    if (!events) return fail(MOE_EINVAL, "events is NULL");
+    return run_forward(shape, x, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks,
+                       dn_scales, dn_bias, y, topk_idx, topk_w, workspace, workspace_bytes, stream,
+                       events, n_events, n_launches);
 }
 
 MOE_EXPORT moe_status_t moe_mxfp4_route(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,

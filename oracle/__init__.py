@@ -47,9 +47,11 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         build(force=True)
     lib = ctypes.CDLL(_LIB)
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
     lib.oracle_e2m1.restype = ctypes.c_double
     lib.oracle_e2m1.argtypes = [ctypes.c_int]
     lib.oracle_e8m0.restype = ctypes.c_double
@@ -79,6 +81,11 @@ def _load():
 
 def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    """Threads the oracle's token-parallel loops use."""
+    return _load().oracle_max_threads()
 
 
 def e2m1(code: int) -> float:

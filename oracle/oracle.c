@@ -38,11 +38,18 @@
  * expert's output includes its own down bias.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_API __attribute__((visibility("default")))
+
+/* Threads the token-parallel loops use (OpenMP's current maximum). */
+ORACLE_API int oracle_max_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* bf16 bit pattern -> double (exact). */
 static double bf16_value(uint16_t bits)
