@@ -51,8 +51,9 @@ KERNEL_SOURCES = {               # kernel -> files whose text defines it
     "up_grouped": ["gemm_grouped.hip", "device_common.h"],
     "down_grouped": ["gemm_grouped.hip", "device_common.h"],
     "combine": ["gemm_grouped.hip", "device_common.h"],
+    "combine_decode": ["gemm_decode.hip", "device_common.h"],
 }
-DECODE_STAGES = ["route", "up_decode", "down_decode"]
+DECODE_STAGES = ["route", "up_decode", "down_decode", "combine_decode"]
 PREFILL_STAGES = ["route", "permute", "up_grouped", "down_grouped", "combine"]
 
 
@@ -278,13 +279,16 @@ def kernel_work(wl: Workload, kernel: str, D: float):
     if kernel == "up_decode":
         return D * gu_expert + T * H * 2 + N * 8 + N * I * 2, 2 * N * 2 * I * H
     if kernel == "down_decode":
-        return D * dn_expert + N * I * 2 + N * 8 + T * H * 2, 2 * N * H * I
+        out = T * H * 2 if T <= 16 else N * H * 4          # y directly, or per-slot partials
+        return D * dn_expert + N * I * 2 + N * 8 + out, 2 * N * H * I
     if kernel == "up_grouped":
         return D * gu_expert + T * H * 2 + N * 4 + N * I * 2, 2 * N * 2 * I * H
     if kernel == "down_grouped":
         return D * dn_expert + N * I * 2 + N * 4 + N * H * 4, 2 * N * H * I
     if kernel == "combine":
         return N * H * 4 + N * 4 + T * H * 2, 0
+    if kernel == "combine_decode":
+        return N * H * 4 + T * H * 2, 0
     raise KeyError(kernel)
 
 

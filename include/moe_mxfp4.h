@@ -118,9 +118,11 @@ moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape,
  * validation, kernels and results, plus hipEventRecord calls on `stream` between the
  * launches. `events` holds at least MOE_MXFP4_MAX_LAUNCHES + 1 hipEvent_t handles created
  * by the caller (timing enabled); events[0] is recorded before the first kernel and
- * events[i] right after the i-th. *n_launches receives the number of kernels launched:
- * 3 for T <= 64 (route, up-projection, down-projection with the combine folded in) and
- * 5 otherwise (route, permute, up-projection, down-projection, combine). MOE_EINVAL if
+ * events[i] right after the i-th. *n_launches receives the number of kernels launched.
+ * With H <= 4096 and I <= 4096: 3 for T <= 16 (route, up-projection, down-projection with
+ * the combine folded in), 4 for 16 < T <= 64 (route, up-projection, down-projection,
+ * combine); 5 for T > 64 or a larger H or I (route, permute, up-projection,
+ * down-projection, combine). MOE_EINVAL if
  * events, an events[i] or n_launches is NULL, or n_events is too small.
  */
 moe_status_t moe_mxfp4_forward_timed(const moe_mxfp4_shape_t *shape,

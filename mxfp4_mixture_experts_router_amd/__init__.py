@@ -24,7 +24,7 @@ import torch
 __all__ = [
     "MoeError", "MoeLibraryMissing", "library_path", "load_library", "abi_version",
     "workspace_bytes", "moe_forward", "route", "permute", "expert_up", "expert_down",
-    "combine", "dequant", "DECODE_MAX_T",
+    "combine", "dequant", "DECODE_MAX_T", "DECODE_MAX_K", "uses_decode_path",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +32,13 @@ _LIB_PATH = os.path.join(_PKG, "libmoe_mxfp4.so")
 _lib = None
 
 DECODE_MAX_T = 64
+DECODE_MAX_K = 4096
+
+
+def uses_decode_path(T, H, I):
+    """Whether moe_forward takes the few-token path (3 or 4 launches, no permutation)."""
+    return T <= DECODE_MAX_T and H <= DECODE_MAX_K and I <= DECODE_MAX_K
+
 MAX_LAUNCHES = 5
 
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ESHAPE", 3: "MOE_EALIGN", 4: "MOE_EWORKSPACE",

@@ -57,7 +57,7 @@ moe::Dims dims_of(const moe_mxfp4_shape_t *s) {
 
 // Workspace regions (each 256-byte aligned), in order.
 struct Layout {
-    size_t idx, w, offsets, sorted_token, sorted_w, slot_row, h, o, total;
+    size_t idx, w, logits, offsets, sorted_token, sorted_w, slot_row, h, o, part, total;
 };
 
 size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -68,8 +68,12 @@ Layout layout_of(const moe_mxfp4_shape_t *s) {
     size_t p = 0;
     L.idx = p;          p += round_up(N * 4);
     L.w = p;            p += round_up(N * 4);
-    if (s->T <= moe::kDecodeMaxT) {
+    L.logits = 0;
+    if (moe::use_decode_path(s->T, s->H, s->I)) {
         L.h = p;        p += round_up(N * static_cast<size_t>(s->I) * 2);
+        L.part = p;
+        if (s->T > moe::kDownTokensMaxT) p += round_up(N * static_cast<size_t>(s->H) * 4);
+        L.logits = p;   p += round_up(static_cast<size_t>(s->T) * s->E * 8);
         L.offsets = L.sorted_token = L.sorted_w = L.slot_row = L.o = 0;
     } else {
         L.offsets = p;      p += round_up((static_cast<size_t>(s->E) + 1) * 4);
@@ -78,6 +82,7 @@ Layout layout_of(const moe_mxfp4_shape_t *s) {
         L.slot_row = p;     p += round_up(N * 4);
         L.h = p;            p += round_up(N * static_cast<size_t>(s->I) * 2);
         L.o = p;            p += round_up(N * static_cast<size_t>(s->H) * 4);
+        L.part = 0;
     }
     L.total = p;
     return L;
@@ -187,12 +192,22 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
     } while (0)
 
     if (moe_status_t m0 = mark(); m0 != MOE_OK) return m0;
-    STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, s), "route");
-    if (shape->T <= moe::kDecodeMaxT) {
-        STEP(moe::launch_up_decode(d, x, gu_blocks, gu_scales, gu_bias, idx, w, h, s), "up (decode)");
-        STEP(moe::launch_down_decode(d, h, dn_blocks, dn_scales, dn_bias, idx, w, y, s), "down (decode)");
+    if (moe::use_decode_path(shape->T, shape->H, shape->I)) {
+        float *part = reinterpret_cast<float *>(ws + L.part);
+        // few tokens: logits in a multi-block kernel, top-k + softmax inside the up-projection
+        const bool split_route = shape->T <= moe::kDownTokensMaxT && shape->H <= 6144;
+        double *logits = split_route ? reinterpret_cast<double *>(ws + L.logits) : nullptr;
+        if (split_route)
+            STEP(moe::launch_logits(d, x, router_w, router_b, logits, s), "router logits");
+        else
+            STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, s), "route");
+        STEP(moe::launch_up_decode(d, x, gu_blocks, gu_scales, gu_bias, logits, idx, w, h, s), "up (decode)");
+        STEP(moe::launch_down_decode(d, h, dn_blocks, dn_scales, dn_bias, idx, w, part, y, s),
+             "down (decode)");
+        if (shape->T > moe::kDownTokensMaxT) STEP(moe::launch_combine_decode(d, part, y, s), "combine (decode)");
         return ok();
     }
+    STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, s), "route");
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
     int32_t *sorted_token = reinterpret_cast<int32_t *>(ws + L.sorted_token);
     float *sorted_w = reinterpret_cast<float *>(ws + L.sorted_w);

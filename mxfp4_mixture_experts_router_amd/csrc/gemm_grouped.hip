@@ -20,7 +20,6 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxE = 256;
 constexpr int kBK = 128;                 // contraction chunk (4 scale blocks)
 constexpr int kAStride = kBK + 8;        // bf16 elements per LDS activation row (padded)
 constexpr int kBStride = kBK / 2 + 16;   // bytes per LDS packed weight row (padded)

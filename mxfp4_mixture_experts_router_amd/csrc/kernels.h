@@ -10,12 +10,24 @@ namespace moe {
 // Token count up to which the forward pass takes the decode path (route -> fused
 // up-projection -> fused down-projection + combine, no sorted permutation in memory).
 constexpr int64_t kDecodeMaxT = 64;
+// Largest H and I the decode kernels take (their scale rows are staged in LDS, 128 bytes per
+// row); larger shapes take the grouped path at any token count.
+constexpr int kDecodeMaxK = 4096;
+
+inline bool use_decode_path(int64_t T, int H, int I) {
+    return T <= kDecodeMaxT && H <= kDecodeMaxK && I <= kDecodeMaxK;
+}
 
 struct Dims {
     int64_t T;
     int H, I, E, k;
     float alpha, limit;
 };
+
+// Router logits only (double [T, E]); for few tokens, where the top-k runs in the
+// up-projection. Needs H <= 6144.
+hipError_t launch_logits(const Dims &d, const uint16_t *x, const uint16_t *router_w,
+                         const uint16_t *router_b, double *logits, hipStream_t s);
 
 hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *router_w,
                         const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
@@ -39,16 +51,24 @@ hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row
                           uint16_t *y, hipStream_t s);
 
 // Decode path (T <= kDecodeMaxT).
-// up: hw[t*k + j, :] = bf16(w[t, j] * swiglu(x[t] . Wgu[e_tj]^T + bgu[e_tj]))
+// Tokens up to which the down-projection keeps all routed experts of a feature tile in one
+// workgroup and writes y directly (beyond: per-slot partial sums + a combine kernel).
+constexpr int64_t kDownTokensMaxT = 16;
+
+// up: hw[t*k + j, :] = bf16(w[t, j] * swiglu(x[t] . Wgu[e_tj]^T + bgu[e_tj])). With `logits`
+// (double [T, E], T <= kDownTokensMaxT) every block computes the top-k + softmax itself and
+// block 0 writes it to topk_idx / topk_w; with logits == nullptr they are inputs.
 hipError_t launch_up_decode(const Dims &d, const uint16_t *x, const uint8_t *gu_blocks,
-                            const uint8_t *gu_scales, const uint16_t *gu_bias,
-                            const int32_t *topk_idx, const float *topk_w, uint16_t *hw,
-                            hipStream_t s);
-// down + combine: y[t, :] = bf16(sum_j hw[t*k + j] . Wdn[e_tj]^T + sum_j w[t, j] * bdn[e_tj])
+                            const uint8_t *gu_scales, const uint16_t *gu_bias, const double *logits,
+                            int32_t *topk_idx, float *topk_w, uint16_t *hw, hipStream_t s);
+// down: T <= kDownTokensMaxT: y[t, :] = bf16(sum_j hw[t*k + j] . Wdn[e_tj]^T + w[t, j] * bdn[e_tj]);
+// otherwise part[t*k + j, :] = hw[t*k + j] . Wdn[e_tj]^T + w[t, j] * bdn[e_tj] (fp32, [T*k, H])
+// and launch_combine_decode forms y.
 hipError_t launch_down_decode(const Dims &d, const uint16_t *hw, const uint8_t *dn_blocks,
-                              const uint8_t *dn_scales, const uint16_t *dn_bias,
-                              const int32_t *topk_idx, const float *topk_w, uint16_t *y,
-                              hipStream_t s);
+                              const uint8_t *dn_scales, const uint16_t *dn_bias, int32_t *topk_idx,
+                              float *topk_w, float *part, uint16_t *y, hipStream_t s);
+// y[t, :] = bf16(sum_{j < k} part[t*k + j, :]), slot order.
+hipError_t launch_combine_decode(const Dims &d, const float *part, uint16_t *y, hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t *blocks, const uint8_t *scales, int64_t rows, int cols,
                           uint16_t *out, hipStream_t s);

@@ -14,7 +14,6 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kMaxE = 256;
 
 // Exclusive scan of cnt[0..E) by one wavefront (E <= 256: four entries per lane).
 __device__ void wave_exclusive_scan(const int *cnt, int *out, int E, int lane) {

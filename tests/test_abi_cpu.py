@@ -77,7 +77,7 @@ def test_workspace_sizes(lib, T, H, I, E, k):
     assert lib.moe_mxfp4_last_error() == b""
     n = moe.workspace_bytes(T, H, I, E, k)
     N = T * k
-    if T <= moe.DECODE_MAX_T:
+    if moe.uses_decode_path(T, H, I):
         assert n >= N * I * 2 + 2 * N * 4
     else:
         assert n >= N * (I * 2 + H * 4) + 3 * N * 4
