@@ -10,6 +10,7 @@
 #include <string>
 
 #include "kernels.h"
+#include "mx_mfma.h"
 
 #define MOE_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -57,7 +58,7 @@ moe::Dims dims_of(const moe_mxfp4_shape_t *s) {
 
 // Workspace regions (each 256-byte aligned), in order.
 struct Layout {
-    size_t idx, w, logits, offsets, sorted_token, sorted_w, slot_row, h, o, part, total;
+    size_t idx, w, logits, offsets, sorted_token, sorted_w, slot_row, h, o, part, x8, h8, total;
 };
 
 size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -70,11 +71,14 @@ Layout layout_of(const moe_mxfp4_shape_t *s) {
     L.w = p;            p += round_up(N * 4);
     L.logits = 0;
     if (moe::use_decode_path(s->T, s->H, s->I)) {
-        L.h = p;        p += round_up(N * static_cast<size_t>(s->I) * 2);
+        // activations as E4M3 hi/lo (mx8) matrices: x as T rows of H, h as 2 T k half-block
+        // rows of I
+        L.x8 = p;       p += round_up(moe::mx8_bytes(s->T, s->H));
+        L.h8 = p;       p += round_up(moe::mx8_bytes(2 * static_cast<int64_t>(N), s->I));
         L.part = p;
         if (s->T > moe::kDownTokensMaxT) p += round_up(N * static_cast<size_t>(s->H) * 4);
         L.logits = p;   p += round_up(static_cast<size_t>(s->T) * s->E * 8);
-        L.offsets = L.sorted_token = L.sorted_w = L.slot_row = L.o = 0;
+        L.h = L.offsets = L.sorted_token = L.sorted_w = L.slot_row = L.o = 0;
     } else {
         L.offsets = p;      p += round_up((static_cast<size_t>(s->E) + 1) * 4);
         L.sorted_token = p; p += round_up(N * 4);
@@ -82,7 +86,7 @@ Layout layout_of(const moe_mxfp4_shape_t *s) {
         L.slot_row = p;     p += round_up(N * 4);
         L.h = p;            p += round_up(N * static_cast<size_t>(s->I) * 2);
         L.o = p;            p += round_up(N * static_cast<size_t>(s->H) * 4);
-        L.part = 0;
+        L.part = L.x8 = L.h8 = 0;
     }
     L.total = p;
     return L;
@@ -194,20 +198,21 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
     if (moe_status_t m0 = mark(); m0 != MOE_OK) return m0;
     if (moe::use_decode_path(shape->T, shape->H, shape->I)) {
         float *part = reinterpret_cast<float *>(ws + L.part);
+        uint8_t *x8 = ws + L.x8, *h8 = ws + L.h8;
         // few tokens: logits in a multi-block kernel, top-k + softmax inside the up-projection
         const bool split_route = shape->T <= moe::kDownTokensMaxT && shape->H <= 6144;
         double *logits = split_route ? reinterpret_cast<double *>(ws + L.logits) : nullptr;
         if (split_route)
-            STEP(moe::launch_logits(d, x, router_w, router_b, logits, s), "router logits");
+            STEP(moe::launch_logits(d, x, router_w, router_b, logits, x8, s), "router logits");
         else
-            STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, s), "route");
-        STEP(moe::launch_up_decode(d, x, gu_blocks, gu_scales, gu_bias, logits, idx, w, h, s), "up (decode)");
-        STEP(moe::launch_down_decode(d, h, dn_blocks, dn_scales, dn_bias, idx, w, part, y, s),
+            STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, x8, s), "route");
+        STEP(moe::launch_up_decode(d, x8, gu_blocks, gu_scales, gu_bias, logits, idx, w, h8, s), "up (decode)");
+        STEP(moe::launch_down_decode(d, h8, dn_blocks, dn_scales, dn_bias, idx, w, part, y, s),
              "down (decode)");
         if (shape->T > moe::kDownTokensMaxT) STEP(moe::launch_combine_decode(d, part, y, s), "combine (decode)");
         return ok();
     }
-    STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, s), "route");
+    STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, nullptr, s), "route");
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
     int32_t *sorted_token = reinterpret_cast<int32_t *>(ws + L.sorted_token);
     float *sorted_w = reinterpret_cast<float *>(ws + L.sorted_w);
@@ -259,7 +264,7 @@ MOE_EXPORT moe_status_t moe_mxfp4_route(const moe_mxfp4_shape_t *shape, const mo
     REQUIRE(router_b, "router_b");
     REQUIRE(topk_idx, "topk_idx");
     REQUIRE(topk_w, "topk_w");
-    LAUNCH(moe::launch_route(dims_of(shape), x, router_w, router_b, topk_idx, topk_w, logits,
+    LAUNCH(moe::launch_route(dims_of(shape), x, router_w, router_b, topk_idx, topk_w, logits, nullptr,
                              static_cast<hipStream_t>(stream)), "route");
     return ok();
 }

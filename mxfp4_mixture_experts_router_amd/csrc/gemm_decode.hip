@@ -1,57 +1,90 @@
-// Decode path (T <= 64): weight-streaming expert GEMMs with the MXFP4 dequantization
-// fused into the register staging.
+// Decode path (T <= 64): weight-streaming expert GEMMs on gfx950's block-scaled MFMA.
 //
 // ZeroModels GPT-OSS page, "MXFP4 experts": on decode only the routed experts' packed
-// weights are touched (the bank stays packed; dequantization happens on the fly). Each
-// packed byte is read from HBM exactly once per call, decoded to bf16 in registers by
-// v_cvt_scalef32_pk_bf16_fp4 (E2M1 code times the block's E8M0 power of two) and fed to
-// bf16 MFMA with fp32 accumulation.
+// weights are touched and the bank stays packed. Here the packed MXFP4 blocks are not
+// dequantized at all: each 16-byte block, as stored, is the B operand of
+// v_mfma_scale_f32_16x16x128_f8f6f4 with its E8M0 byte as the B scale (see mx_mfma.h). The
+// activations enter as exact E4M3 hi/lo pairs (two A rows per activation row), written once
+// per call by their producer: the router kernel for x, the up-projection's epilogue for the
+// SwiGLU output h. Each packed weight byte is read from HBM exactly once per call.
 //
 // Streaming a few MB per call at HBM speed needs every workgroup's share of the packed
 // weights in flight at once: each wavefront issues all (or a large batch) of its 16-byte
 // weight loads before its first MFMA, and the activation rows (a few KB) are staged in LDS
-// while those loads are outstanding.
-//
-// Contraction mapping. A 16x16x32 MFMA step consumes, per lane, 8 consecutive contraction
-// entries; lane group g = lane / 16 is free to take any 8 entries as long as the A and B
-// operands agree. Here one 16-byte load of a weight row = one 32-wide scale block; the four
-// lane groups take four consecutive blocks (a 128-wide chunk), and step s of the chunk uses
-// entries 8s..8s+7 of each group's block. Activations are read to match.
+// while those loads are outstanding. Each load instruction covers 8 rows x 128 contiguous
+// bytes (whole cache lines); one lane exchange then gives every lane two blocks of one row
+// (load_tile_chunk / tile_chunk_to_mfma).
 #include "device_common.h"
 #include "kernels.h"
+#include "mx_mfma.h"
 #include "topk.h"
 
 namespace moe {
 namespace {
 
 constexpr int kMaxRows = 64;          // = kDecodeMaxT: an expert is chosen at most once per token
-constexpr int kDownScaleLds = 16384;   // LDS bytes for the routed experts' scale rows (few tokens)
+constexpr int kDownScaleLds = 16384;  // LDS bytes for the routed experts' scale rows (few tokens)
+constexpr int kStageLds = 24 * 1024;  // LDS bytes for staged E4M3 activation rows
 
 // Routing of all T tokens into LDS: s_idx / s_w [T*k]. With `logits` (double [T, E]) the
-// top-k + softmax is computed here by every block (wavefront w handles tokens w, w+NW, ...)
+// top-k + softmax is computed here by every block (wavefront w < 4 handles tokens w, w+4, ...)
 // and block 0 also writes it to topk_idx / topk_w; otherwise it is read from them.
-// Then bitmap = the set of routed experts. Ends with a block barrier.
-__device__ void load_routing(const double *logits, int32_t *topk_idx, float *topk_w, int T, int E,
-                             int k, int *s_idx, float *s_w, uint32_t *bitmap) {
-    __shared__ double s_lg[4][kMaxE];
-    __shared__ double s_ex[4][8];
+// The first routing loads are issued before `stage()` (the caller's routing-independent
+// loads), so both latencies overlap. Then bitmap = the set of routed experts. Ends with a
+// block barrier.
+template <bool WITH_LOGITS, typename Stage>
+__device__ __forceinline__ void load_routing(const double *logits, int32_t *topk_idx, float *topk_w, int T, int E,
+                                             int k, int *s_idx, float *s_w, uint32_t *bitmap, Stage &&stage) {
+    constexpr int kPre = 2;                 // routing entries per thread loaded up front
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int nw = blockDim.x / kWave;
     const int N = T * k;
     if (tid < kMaxE / 32) bitmap[tid] = 0u;
-    if (logits) {
-        const bool writer = blockIdx.x == 0;
-        for (int t = wave; t < T; t += nw) {
-            if (wave < 4) {
-                for (int e = lane; e < E; e += kWave) s_lg[wave][e] = logits[static_cast<int64_t>(t) * E + e];
-                __builtin_amdgcn_wave_barrier();
-                topk_softmax_wave(s_lg[wave], E, k, lane, s_idx + t * k, s_w + t * k,
-                                  writer ? topk_idx + t * k : nullptr, writer ? topk_w + t * k : nullptr,
-                                  nullptr, s_ex[wave]);
-            }
+    double lg0[kMaxE / kWave];
+    int32_t pi[kPre];
+    float pw[kPre];
+    if (WITH_LOGITS && logits) {
+#pragma unroll
+        for (int c = 0; c < kMaxE / kWave; ++c) {
+            const int e = lane + kWave * c;
+            lg0[c] = (wave < 4 && wave < T && e < E) ? logits[static_cast<int64_t>(wave) * E + e] : 0.0;
         }
     } else {
-        for (int n = tid; n < N; n += blockDim.x) {
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            const int n = tid + q * static_cast<int>(blockDim.x);
+            pi[q] = n < N ? topk_idx[n] : 0;
+            pw[q] = n < N ? topk_w[n] : 0.f;
+        }
+    }
+    stage();
+    if constexpr (WITH_LOGITS) {
+        __shared__ __attribute__((aligned(16))) uint64_t s_tk[4][kTopkScratch];
+        if (logits && wave < 4) {
+            const bool writer = blockIdx.x == 0;
+            for (int t = wave; t < T; t += 4) {
+                if (t != wave) {
+#pragma unroll
+                    for (int c = 0; c < kMaxE / kWave; ++c) {
+                        const int e = lane + kWave * c;
+                        lg0[c] = e < E ? logits[static_cast<int64_t>(t) * E + e] : 0.0;
+                    }
+                }
+                topk_softmax_values(lg0, E, k, lane, s_idx + t * k, s_w + t * k,
+                                    writer ? topk_idx + t * k : nullptr, writer ? topk_w + t * k : nullptr,
+                                    s_tk[wave]);
+            }
+        }
+    }
+    if (!WITH_LOGITS || !logits) {
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            const int n = tid + q * static_cast<int>(blockDim.x);
+            if (n < N) {
+                s_idx[n] = pi[q];
+                s_w[n] = pw[q];
+            }
+        }
+        for (int n = tid + kPre * static_cast<int>(blockDim.x); n < N; n += blockDim.x) {
             s_idx[n] = topk_idx[n];
             s_w[n] = topk_w[n];
         }
@@ -96,200 +129,296 @@ __device__ void rows_of_expert(const int *s_idx, int N, int e, int *s_rows, int 
     if (lane == 0) *s_nrows = cnt < kMaxRows ? cnt : kMaxRows;
 }
 
-// Copy `nrows` rows (row r = src + row_of(r) * K) into LDS rows of K elements.
-template <typename RowOf>
-__device__ void stage_rows(uint16_t *dst, const uint16_t *src, int nrows, int K, RowOf row_of) {
-    const int per_row = K / 8;
-    for (int q = threadIdx.x; q < nrows * per_row; q += blockDim.x) {
-        const int r = q / per_row, c = q % per_row;
-        *reinterpret_cast<uint4 *>(dst + r * K + 8 * c) =
-            *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(row_of(r)) * K + 8 * c);
+// Copy `bytes` contiguous bytes (a multiple of 16) into LDS; each thread issues up to 4
+// loads before its first LDS store (clamped slots reload and rewrite the last piece).
+__device__ __forceinline__ void stage_bytes(uint8_t *dst, const uint8_t *src, int bytes) {
+    const int total = bytes / 16;
+    const int nt = blockDim.x;
+    auto ld = [&](int q) { return *reinterpret_cast<const uint4 *>(src + 16 * static_cast<int64_t>(q)); };
+    auto st = [&](int q, uint4 v) { *reinterpret_cast<uint4 *>(dst + 16 * q) = v; };
+    for (int base = threadIdx.x; base < total; base += 4 * nt) {
+        const int q0 = base, q1 = min(base + nt, total - 1), q2 = min(base + 2 * nt, total - 1),
+                  q3 = min(base + 3 * nt, total - 1);
+        const uint4 v0 = ld(q0), v1 = ld(q1), v2 = ld(q2), v3 = ld(q3);
+        st(q0, v0);
+        st(q1, v1);
+        st(q2, v2);
+        st(q3, v3);
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// Up-projection. Block = (routing slot, 16 gate/up pairs); 4 wavefronts split the
-// contraction (H) in 128-wide chunks and are reduced through LDS in a fixed order.
-//   hw[n, i] = bf16(w[n] * swiglu(x[t] . Wgu[e, 2i] + bgu[e, 2i], x[t] . Wgu[e, 2i+1] + bgu[e, 2i+1]))
-// for every pair n = t*k + j routed to expert e (the slot-th routed expert).
-// NMT = 16-row m-subtiles (>= rows / 16); UB = chunks per load batch per wavefront; with
-// LDS_A the activation rows are staged in dynamic LDS (rows * H bf16). With `logits` the
-// routing (top-k + softmax) is computed in the prologue, see load_routing.
-template <int NMT, int UB, bool LDS_A>
-__global__ __launch_bounds__(256) void k_up_small(
-    const uint16_t *__restrict__ x, const uint8_t *__restrict__ gu_blocks,
+// Packed-weight tiles. A 16-row tile of a weight matrix (rows of K/2 bytes, one 16-byte
+// block per 32 contraction entries) is read in chunks of 256 contraction entries (8
+// blocks). Each of the two 16-byte loads per lane covers 8 rows x 128 contiguous bytes, so
+// every load instruction touches whole cache lines: lane l loads block 8c + l/8 of row l%8
+// (first) and of row 8 + l%8 (second).
+__device__ __forceinline__ void load_tile_chunk(const uint8_t *rows, int64_t row_bytes, int c, int nblocks,
+                                                int lane, uint4 &first, uint4 &second) {
+    const int kb = min(8 * c + (lane >> 3), nblocks - 1);   // clamped: the tail re-reads a real block
+    const uint8_t *p = rows + (lane & 7) * row_bytes + kb * 16;
+    first = *reinterpret_cast<const uint4 *>(p);
+    second = *reinterpret_cast<const uint4 *>(p + 8 * row_bytes);
+}
+
+__device__ __forceinline__ uint32_t ror8_in_row(uint32_t v) {   // DPP row_ror:8 (lane n <-> n ^ 8)
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xf, 0xf, false));
+}
+
+// Afterwards lane (n = l%16, g = l/16) holds blocks 8c + 2g (lo) and 8c + 2g + 1 (hi) of
+// row n. Lanes n < 8 loaded (row n, block 8c + 2g) and lanes n >= 8 (row n, block 8c + 2g +
+// 1) themselves; the other halves are exchanged between lanes n and n ^ 8 by one rotation
+// within each 16-lane row.
+__device__ __forceinline__ void tile_chunk_to_mfma(const uint4 &first, const uint4 &second, int lane, uint4 &lo,
+                                                   uint4 &hi) {
+    const bool low = (lane & 15) < 8;
+    const uint4 send = low ? second : first;
+    const uint4 recv = make_uint4(ror8_in_row(send.x), ror8_in_row(send.y), ror8_in_row(send.z),
+                                  ror8_in_row(send.w));
+    lo = low ? first : recv;
+    hi = low ? recv : second;
+}
+
+// One block-scaled MFMA over the blocks 8c + 2v + h (v = 0..3) of chunk c, h = 0 or 1: B is
+// the lane's block 8c + 2g + h (from tile_chunk_to_mfma) with scale sb. arow: E4M3 row of the
+// lane's A row m (nullptr: a zero row), asc: its scale row. Blocks past nblocks contribute 0.
+__device__ __forceinline__ f32x4 mx_step(f32x4 acc, const uint8_t *arow, const uint8_t *asc, const i32x8 &bop,
+                                         uint32_t sb, int c, int h, int g, int nblocks) {
+    const int b0 = 8 * c + 2 * (g >> 1) + h;    // A bytes 0-15: virtual block g/2
+    const int b1 = b0 + 4;                      // A bytes 16-31: virtual block 2 + g/2
+    const int kb = 8 * c + 2 * g + h;           // the lane group's own (virtual g) block
+    uint4 f = zero4(), s = zero4();
+    uint32_t sa = 127u;
+    if (arow != nullptr) {
+        if (b0 < nblocks) f = *reinterpret_cast<const uint4 *>(arow + b0 * 32 + 16 * (g & 1));
+        if (b1 < nblocks) s = *reinterpret_cast<const uint4 *>(arow + b1 * 32 + 16 * (g & 1));
+        if (kb < nblocks) sa = asc[kb];
+    }
+    return mfma_mx(mx_a_operand(f, s), bop, acc, sa, sb);
+}
+
+// ---------------------------------------------------------------------------------------
+// Up-projection. Block = (routing slot, 16 gate/up pairs = 32 interleaved rows = two 16-row
+// tiles); wavefront w takes tile w % 2 and every other 256-wide chunk of H (parity w / 2);
+// the two halves are added through LDS.
+//   h[n, i] = w[n] * swiglu(x[t] . Wgu[e, 2i] + bgu[e, 2i], x[t] . Wgu[e, 2i+1] + bgu[e, 2i+1])
+// for every pair n = t*k + j routed to expert e (the slot-th routed expert). Column c of
+// tile q is row 16q + c of the block: pair 8q + c/2, gate for even c, up for odd.
+// h is written as an mx8 matrix of 2 T k rows: row 2n + half holds the block's 16 values
+// (half = (i0 / 16) % 2 of MX block i0 / 32) and zeros in the other half, so every 16
+// values get their own exponent and a block never needs its neighbour's values; the down
+// projection reads 4 A rows (h8 rows 4n .. 4n + 3) per pair.
+// A rows: 2 per routed pair (hi, lo of x8 row 2t, 2t + 1); block y takes the expert's pairs
+// 8 NMT y .. 8 NMT (y + 1) - 1 in NMT 16-row m-tiles; UB chunks per wavefront per load batch
+// (two loads each). With LDS_A the E4M3 token rows are staged in LDS; the token scales
+// always are. With `logits` the routing (top-k + softmax) is computed in the prologue, see
+// load_routing.
+template <int NMT, int UB, bool LDS_A, bool WITH_LOGITS>
+__global__ __launch_bounds__(256) void k_up_mx(
+    const uint8_t *__restrict__ x8, const uint8_t *__restrict__ xs8, const uint8_t *__restrict__ gu_blocks,
     const uint8_t *__restrict__ gu_scales, const uint16_t *__restrict__ gu_bias,
     const double *__restrict__ logits, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
-    int T, int H, int I, int E, int k, float alpha, float limit, uint16_t *__restrict__ hw) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+    int T, int H, int I, int E, int k, float alpha, float limit, uint8_t *__restrict__ h8,
+    uint8_t *__restrict__ hs8) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
     __shared__ uint32_t bitmap[kMaxE / 32];
     __shared__ int s_idx[kMaxRows * 8];
     __shared__ float s_w[kMaxRows * 8];
     __shared__ int s_rows[kMaxRows];
     __shared__ int s_nrows;
-    __shared__ float red[4][NMT * 8][kWave];
+    // chunk-half partial sums, later the slots' SwiGLU outputs [slot][17]
+    constexpr int kRed = 2 * NMT * 4 * kWave > kMaxRows * 17 ? 2 * NMT * 4 * kWave : kMaxRows * 17;
+    __shared__ float s_red[kRed];
     __shared__ __attribute__((aligned(16))) uint8_t s_sc[32 * kMaxScaleCols];   // 32 rows x H/32
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int col = lane & 15, g = lane >> 4;
     const int tiles_i = I / 16;
     const int N = T * k;
-    // every token row into LDS first (independent of the routing, so its latency overlaps it)
-    if (LDS_A) stage_rows(xs, x, T, H, [](int r) { return r; });
-    load_routing(logits, topk_idx, topk_w, T, E, k, s_idx, s_w, bitmap);
+    const int hs = H / 32, sxs = mx8_scale_stride(H);
+    uint8_t *xs_lds = dyn + (LDS_A ? 2 * T * H : 0);
+    // the token rows (E4M3) and their scales into LDS, overlapped with the routing loads
+    load_routing<WITH_LOGITS>(logits, topk_idx, topk_w, T, E, k, s_idx, s_w, bitmap, [&] {
+        if (LDS_A) stage_bytes(dyn, x8, 2 * T * H);
+        stage_bytes(xs_lds, xs8, 2 * T * sxs);
+    });
     const int e = expert_of_slot(bitmap, blockIdx.x / tiles_i);
     if (e < 0) return;  // fewer routed experts than slots (uniform over the block)
     const int i0 = (blockIdx.x % tiles_i) * 16;
 
-    // all packed-weight loads of the first batch; scale bytes stay raw until use so that no
-    // wait is needed before the whole batch is in flight
-    const int64_t grow = static_cast<int64_t>(e) * 2 * I + 2 * (i0 + col);   // gate row
-    const int hb = H / 2, hs = H / 32;
-    const uint8_t *gate_b = gu_blocks + grow * hb;
-    const uint8_t *up_b = gate_b + hb;
-    const int nblocks = H / 32;
-    const int nchunks = (nblocks + 3) / 4;
-    // the block's 32 rows of scales are H contiguous bytes: one 16-byte load per thread,
-    // issued before the weight stream so that waiting for it never waits for the stream
-    const uint8_t *sc_src = gu_scales + (static_cast<int64_t>(e) * 2 * I + 2 * i0) * hs;
+    const int64_t row0 = static_cast<int64_t>(e) * 2 * I + 2 * i0;   // first of the 32 rows
+    const int hb = H / 2;
+    const int nblocks = hs;
+    const int nchunks = (nblocks + 7) / 8;
+    const int q = wave & 1, p = wave >> 1;
+    // the 32 rows' scales are H contiguous bytes: up to two 16-byte loads per thread, issued
+    // before the weight stream so that waiting for it never waits for the stream
     uint4 scv[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int idx = tid + 256 * q;
-        scv[q] = idx < H / 16 ? *reinterpret_cast<const uint4 *>(sc_src + 16 * idx) : zero4();
+    for (int qq = 0; qq < 2; ++qq) {
+        const int idx = tid + 256 * qq;
+        scv[qq] = idx < H / 16 ? *reinterpret_cast<const uint4 *>(gu_scales + row0 * hs + 16 * idx) : zero4();
     }
-    uint4 bg[UB], bu[UB];
-    // loads are unconditional (block index clamped into the row) so that the whole batch is
-    // issued without branches; chunks past the end are neutralised on the activation side
+    const uint8_t *wrows = gu_blocks + (row0 + 16 * q) * hb;
+    uint4 wf[UB], ws[UB];
     auto load_batch = [&](int c0) {
 #pragma unroll
-        for (int u = 0; u < UB; ++u) {
-            const int kb = min(4 * (c0 + 4 * u) + g, nblocks - 1);
-            bg[u] = *reinterpret_cast<const uint4 *>(gate_b + kb * 16);
-            bu[u] = *reinterpret_cast<const uint4 *>(up_b + kb * 16);
-        }
+        for (int u = 0; u < UB; ++u)
+            load_tile_chunk(wrows, hb, min(c0 + 2 * u, nchunks - 1), nblocks, lane, wf[u], ws[u]);
     };
-    load_batch(wave);
+    load_batch(p);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int idx = tid + 256 * q;
-        if (idx < H / 16) *reinterpret_cast<uint4 *>(s_sc + 16 * idx) = scv[q];
+    for (int qq = 0; qq < 2; ++qq) {
+        const int idx = tid + 256 * qq;
+        if (idx < H / 16) *reinterpret_cast<uint4 *>(s_sc + 16 * idx) = scv[qq];
     }
-    const uint32_t bias_pair = *reinterpret_cast<const uint32_t *>(gu_bias + grow);   // gate, up
+    const float bias = bf16_to_f32(gu_bias[row0 + 16 * q + col]);
 
     if (wave == 0) rows_of_expert(s_idx, N, e, s_rows, &s_nrows);
     __syncthreads();
-    const int nrows = s_nrows;
-    const uint16_t *arow[NMT];
+    const int s0 = 8 * NMT * blockIdx.y;       // first slot (routed pair of e) of this block
+    const int nrows = s_nrows - s0;            // slots of this block (may exceed 8 NMT)
+    if (nrows <= 0) return;                    // uniform
+    // A row r = 16 mt + col: slot s0 + r / 2, part r % 2 (hi, lo) -> x8 row 2 t + part
+    const uint8_t *arow[NMT];
+    const uint8_t *asc[NMT];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
         const int r = 16 * mt + col;
-        arow[mt] = r < nrows ? (LDS_A ? xs : x) + static_cast<int64_t>(s_rows[r] / k) * H : nullptr;
+        arow[mt] = nullptr;
+        asc[mt] = nullptr;
+        if ((r >> 1) < nrows) {
+            const int xr = 2 * (s_rows[s0 + (r >> 1)] / k) + (r & 1);
+            arow[mt] = (LDS_A ? dyn : x8) + static_cast<int64_t>(xr) * H;
+            asc[mt] = xs_lds + xr * sxs;
+        }
     }
 
-    f32x4 accg[NMT], accu[NMT];
+    f32x4 acc[NMT];
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-        accg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accu[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int c0 = wave; c0 < nchunks; c0 += 4 * UB) {
-        if (c0 != wave) load_batch(c0);
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = p; c0 < nchunks; c0 += 2 * UB) {
+        if (c0 != p) load_batch(c0);
 #pragma unroll
         for (int u = 0; u < UB; ++u) {
-            const int kb = 4 * (c0 + 4 * u) + g;
-            const bool ok = c0 + 4 * u < nchunks && kb < nblocks;
-            uint4 a[NMT][4];
+            const int c = c0 + 2 * u;
+            if (c >= nchunks) break;   // uniform
+            uint4 lo, hi;
+            tile_chunk_to_mfma(wf[u], ws[u], lane, lo, hi);
 #pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t sb = s_sc[(16 * q + col) * hs + min(8 * c + 2 * g + h, nblocks - 1)];
+                const i32x8 bop = mx_b_operand(h ? hi : lo);
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    a[mt][s] = (ok && arow[mt] != nullptr)
-                                   ? *reinterpret_cast<const uint4 *>(arow[mt] + kb * 32 + 8 * s)
-                                   : zero4();
-            const uint32_t gw[4] = {bg[u].x, bg[u].y, bg[u].z, bg[u].w};
-            const uint32_t uw[4] = {bu[u].x, bu[u].y, bu[u].z, bu[u].w};
-            const int kbc = min(kb, nblocks - 1);
-            const float scg = e8m0_to_f32(s_sc[(2 * col) * hs + kbc]);
-            const float scu = e8m0_to_f32(s_sc[(2 * col + 1) * hs + kbc]);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 wg = mxfp4_word_to_bf16x8(gw[s], scg);
-                const bf16x8 wu = mxfp4_word_to_bf16x8(uw[s], scu);
-#pragma unroll
-                for (int mt = 0; mt < NMT; ++mt) {
-                    if (16 * mt < nrows) {
-                        accg[mt] = mfma16(as_bf16x8(a[mt][s]), wg, accg[mt]);
-                        accu[mt] = mfma16(as_bf16x8(a[mt][s]), wu, accu[mt]);
-                    }
-                }
+                for (int mt = 0; mt < NMT; ++mt)
+                    if (16 * mt < 2 * nrows) acc[mt] = mx_step(acc[mt], arow[mt], asc[mt], bop, sb, c, h, g, nblocks);
             }
         }
     }
 
+    // the second chunk half hands its sums to the first
+    float(*red)[NMT * 4][kWave] = reinterpret_cast<float(*)[NMT * 4][kWave]>(s_red);   // [2] tiles
+    if (p == 1)
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
+        for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            red[wave][mt * 8 + r][lane] = accg[mt][r];
-            red[wave][mt * 8 + 4 + r][lane] = accu[mt][r];
-        }
+            for (int r = 0; r < 4; ++r) red[q][mt * 4 + r][lane] = acc[mt][r];
     __syncthreads();
-    if (wave != 0) return;
-    const int i = i0 + col;
-    const float bgate = bf16_to_f32(static_cast<uint16_t>(bias_pair & 0xffffu));
-    const float bup = bf16_to_f32(static_cast<uint16_t>(bias_pair >> 16));
+    if (p == 0)
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
+        for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * mt + 4 * g + r;
-            if (row >= nrows) continue;
-            float gsum = 0.f, usum = 0.f;
+            for (int r = 0; r < 4; ++r) acc[mt][r] += red[q][mt * 4 + r][lane];
+    __syncthreads();   // s_red is reused for the SwiGLU outputs below
+    float(*s_h)[17] = reinterpret_cast<float(*)[17]>(s_red);
+    if (p == 0) {
+        // D rows 16mt + 4g + r: slot 8mt + 2g + r/2, part r % 2
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                gsum += red[w][mt * 8 + r][lane];
-                usum += red[w][mt * 8 + 4 + r][lane];
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int s = 8 * mt + 2 * g + j;   // local slot
+                const float v = acc[mt][2 * j] + acc[mt][2 * j + 1] + bias;
+                const float other = __shfl_xor(v, 1);
+                if ((col & 1) == 0 && s < nrows)
+                    s_h[s][8 * q + col / 2] = swiglu(v, other, alpha, limit) * s_w[s_rows[s0 + s]];
             }
-            const int n = s_rows[row];
-            const float hval = swiglu(gsum + bgate, usum + bup, alpha, limit) * s_w[n];
-            hw[static_cast<int64_t>(n) * I + i] = f32_to_bf16(hval);
+    }
+    __syncthreads();
+    // each slot's 16 outputs: one half of MX block i0 / 32 of h8 row 2n + half, the other
+    // half zero. 8 threads per slot: thread j < 4 converts values 4j .. 4j + 3, threads
+    // j >= 4 write the zero words; the block exponent comes from the max over the group.
+    {
+        const int half = (i0 / 16) & 1;
+        const int sl = tid >> 3, j = tid & 7;
+        const bool live = sl < nrows && sl < 8 * NMT;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (live && j < 4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = s_h[sl][4 * j + i];
+        float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+        if (live) {
+            const int eb = mx8_block_exponent(m);
+            uint32_t hi = 0u, lo = 0u;
+            if (j < 4) mx8_split4(ldexpf(v[0], -eb), ldexpf(v[1], -eb), ldexpf(v[2], -eb), ldexpf(v[3], -eb), hi, lo);
+            const int64_t r = 2 * (2 * static_cast<int64_t>(s_rows[s0 + sl]) + half);   // hi byte row
+            const int b = i0 / 32;
+            // word w of the 32-byte block: values in words 4 half .. 4 half + 3
+            const int w = j < 4 ? 4 * half + j : 4 * (1 - half) + (j - 4);
+            reinterpret_cast<uint32_t *>(h8 + r * I + 32 * b)[w] = hi;
+            reinterpret_cast<uint32_t *>(h8 + (r + 1) * I + 32 * b)[w] = lo;
+            if (j == 0) {
+                const int ss = mx8_scale_stride(I);
+                hs8[r * ss + b] = static_cast<uint8_t>(127 + eb);
+                hs8[(r + 1) * ss + b] = static_cast<uint8_t>(123 + eb);
+            }
         }
+    }
 }
 
 // ---------------------------------------------------------------------------------------
-// Down-projection with the combine folded in (few tokens). Block = 16 output features d
-// for every token; NW wavefronts share the (routed expert, 128-wide chunk of I) work units.
-// For routed expert e the A operand row of token t is hw[t*k + j] when idx[t, j] == e, else
-// zero, so all experts accumulate into the same per-token tile:
-//   y[t, d] = bf16( sum_{e, i} A_e[t, i] * Wdn[e, d, i]  +  sum_j w[t, j] * bdn[e_tj, d] ).
-// Each wavefront alternates two accumulators (shorter MFMA dependency chains); the partial
-// tiles are reduced through LDS in (wavefront, accumulator) order. With SC_LDS the scale
-// rows of all routed experts are staged in LDS up front (they must fit kDownScaleLds bytes);
-// otherwise each weight load brings its scale byte along.
-template <int UB, int NW, bool LDS_A, bool SC_LDS>
-__global__ __launch_bounds__(NW * 64) void k_down_tokens(
-    const uint16_t *__restrict__ hw, const uint8_t *__restrict__ dn_blocks,
+// Down-projection with the combine folded in (few tokens). Block = one 16-row tile of output
+// features d for every token; NW wavefronts share the (routed expert, 256-wide chunk of I)
+// work units. For routed expert e the A rows of token t are the four h8 rows 4n .. 4n + 3
+// (hi/lo of both halves, see k_up_mx) when pair n = t*k + j has idx[t, j] == e, else zero,
+// so all experts accumulate into the same per-token tile:
+//   y[t, d] = bf16( sum_{e, i} h_e[t, i] * Wdn[e, d, i]  +  sum_j w[t, j] * bdn[e_tj, d] ).
+// (h already carries the routing weight.) The wavefronts' partial tiles are reduced through
+// LDS in wavefront order. A rows 4t + sub, NMT = ceil(T / 4) m-tiles. With LDS_A the h8 rows
+// are staged in LDS; their scales always are. With SC_LDS the weight scale rows of all
+// routed experts are staged in LDS up front (they must fit kDownScaleLds bytes); otherwise
+// each unit loads its scale bytes along with its weights.
+template <int NMT, int NW, int UB, bool LDS_A, bool SC_LDS>
+__global__ __launch_bounds__(NW * 64) void k_down_mx_tokens(
+    const uint8_t *__restrict__ h8, const uint8_t *__restrict__ hs8, const uint8_t *__restrict__ dn_blocks,
     const uint8_t *__restrict__ dn_scales, const uint16_t *__restrict__ dn_bias,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int T, int H, int I, int E, int k,
     uint16_t *__restrict__ y) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t hs_lds[];
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
     __shared__ uint32_t bitmap[kMaxE / 32];
     __shared__ int s_idx[16 * 8];
     __shared__ float s_w[16 * 8];
     __shared__ int s_experts[kMaxE];
     __shared__ int s_rowof[16 * 8][16];     // [routed expert slot][token] -> pair n, or -1
     __shared__ int s_na;
-    __shared__ float red[NW * 2][4][kWave];
+    __shared__ float red[NW][NMT * 4][kWave];
+    __shared__ float s_bprod[16 * 8][16];   // [pair n][feature] w[n] * bdn[e_n, d0 + feature]
     __shared__ __attribute__((aligned(16))) uint8_t s_sc[SC_LDS ? kDownScaleLds : 16];
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int col = lane & 15, g = lane >> 4;
     const int d0 = blockIdx.x * 16;
     const int N = T * k;        // T <= 16 here
-    // every (token, slot) row of hw into LDS first (independent of the routing)
-    if (LDS_A) stage_rows(hs_lds, hw, N, I, [](int r) { return r; });
-    load_routing(nullptr, topk_idx, topk_w, T, E, k, s_idx, s_w, bitmap);
+    const int shs = mx8_scale_stride(I);
+    uint8_t *hs_lds = dyn + (LDS_A ? 4 * N * I : 0);
+    // the h rows (E4M3) and their scales into LDS, overlapped with the routing loads
+    load_routing<false>(nullptr, topk_idx, topk_w, T, E, k, s_idx, s_w, bitmap, [&] {
+        if (LDS_A) stage_bytes(dyn, h8, 4 * N * I);
+        stage_bytes(hs_lds, hs8, 4 * N * shs);
+    });
     if (tid < kMaxE / 32) {
         int before = 0;
         for (int w = 0; w < tid; ++w) before += __popc(bitmap[w]);
@@ -302,8 +431,8 @@ __global__ __launch_bounds__(NW * 64) void k_down_tokens(
     }
     __syncthreads();
     const int na = s_na;
-    for (int q = tid; q < na * 16; q += NW * 64) {
-        const int a = q / 16, t = q % 16;
+    for (int qq = tid; qq < na * 16; qq += NW * 64) {
+        const int a = qq / 16, t = qq % 16;
         int n = -1;
         if (t < T)
             for (int j = 0; j < k; ++j)
@@ -311,105 +440,130 @@ __global__ __launch_bounds__(NW * 64) void k_down_tokens(
         s_rowof[a][t] = n;
     }
     const int nblocks = I / 32;
-    const int nchunks = (nblocks + 3) / 4;
+    const int nchunks = (nblocks + 7) / 8;
     const int nunits = na * nchunks;
-    const int64_t drow = d0 + col;
+    const int is = I / 32;
 
     // the 16 rows of scales of every routed expert (I/2 contiguous bytes each), loaded before
     // the weight stream
-    const int is = I / 32;
     const int nsc = SC_LDS ? na * (I / 32) : 0;     // 16-byte pieces
     uint4 scv[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int idx = tid + NW * 64 * q;
-        scv[q] = zero4();
+    for (int qq = 0; qq < 2; ++qq) {
+        const int idx = tid + NW * 64 * qq;
+        scv[qq] = zero4();
         if (SC_LDS && idx < nsc) {
             const int a = idx / (I / 32), piece = idx % (I / 32);
-            scv[q] = *reinterpret_cast<const uint4 *>(dn_scales + (static_cast<int64_t>(s_experts[a]) * H + d0) * is + 16 * piece);
+            scv[qq] = *reinterpret_cast<const uint4 *>(dn_scales + (static_cast<int64_t>(s_experts[a]) * H + d0) * is + 16 * piece);
         }
     }
+    constexpr int kBiasPer = (16 * 8 * 16 + NW * 64 - 1) / (NW * 64);
+    uint16_t bias_v[kBiasPer];
+#pragma unroll
+    for (int qq = 0; qq < kBiasPer; ++qq) {
+        const int idx = tid + NW * 64 * qq;
+        bias_v[qq] = idx < N * 16 ? dn_bias[static_cast<int64_t>(s_idx[idx / 16]) * H + d0 + idx % 16] : 0;
+    }
     // this wavefront's first batch of packed-weight loads
-    uint4 b[UB];
-    uint32_t sc[UB];
-    int ua[UB], uaa[UB], ukb[UB];
+    uint4 wf[UB], ws[UB];
+    uint32_t sclo[UB], schi[UB];
+    int ua[UB], uaa[UB], ucc[UB];
     auto load_batch = [&](int u0) {
 #pragma unroll
         for (int u = 0; u < UB; ++u) {
-            // unconditional loads at clamped indices; units past the end read a real block and
-            // are neutralised by a zero activation row
+            // unconditional loads at clamped indices; units past the end read a real tile and
+            // are neutralised by zero activation rows
             const int unit = u0 + NW * u;
             const int uc = min(unit, nunits - 1);
-            const int a = uc / nchunks;
-            const int kb = min(4 * (uc % nchunks) + g, nblocks - 1);
-            const bool ok = unit < nunits && 4 * (uc % nchunks) + g < nblocks;
-            const int64_t row = static_cast<int64_t>(s_experts[a]) * H + drow;
-            b[u] = *reinterpret_cast<const uint4 *>(dn_blocks + row * (I / 2) + kb * 16);
-            if (!SC_LDS) sc[u] = dn_scales[row * is + kb];
-            ua[u] = ok ? a : -1;
+            const int a = uc / nchunks, c = uc % nchunks;
+            const int64_t row0 = static_cast<int64_t>(s_experts[a]) * H + d0;
+            load_tile_chunk(dn_blocks + row0 * (I / 2), I / 2, c, nblocks, lane, wf[u], ws[u]);
+            if (!SC_LDS) {
+                const uint8_t *srow = dn_scales + (row0 + col) * is;
+                sclo[u] = srow[min(8 * c + 2 * g, nblocks - 1)];
+                schi[u] = srow[min(8 * c + 2 * g + 1, nblocks - 1)];
+            }
+            ua[u] = unit < nunits ? a : -1;
             uaa[u] = a;
-            ukb[u] = kb;
+            ucc[u] = c;
         }
     };
     load_batch(wave);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int idx = tid + NW * 64 * q;
-        if (SC_LDS && idx < nsc) *reinterpret_cast<uint4 *>(s_sc + 16 * idx) = scv[q];
+    for (int qq = 0; qq < 2; ++qq) {
+        const int idx = tid + NW * 64 * qq;
+        if (SC_LDS && idx < nsc) *reinterpret_cast<uint4 *>(s_sc + 16 * idx) = scv[qq];
     }
-    // bias term of the epilogue rows (wavefront 0): sum_j w[t, j] * bdn[e_tj, d], t = 4g + r
-    float bterm[4] = {0.f, 0.f, 0.f, 0.f};
-    if (wave == 0) {
+    // bias products w[n] * bdn[e_n, d] of every pair n and feature d of the tile (loads issued
+    // before the weight batch, so consuming them does not wait for it)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * g + r;
-            if (t < T)
-                for (int j = 0; j < k; ++j)
-                    bterm[r] += s_w[t * k + j] * bf16_to_f32(dn_bias[static_cast<int64_t>(s_idx[t * k + j]) * H + drow]);
-        }
+    for (int qq = 0; qq < kBiasPer; ++qq) {
+        const int idx = tid + NW * 64 * qq;
+        if (idx < N * 16) s_bprod[idx / 16][idx % 16] = s_w[idx / 16] * bf16_to_f32(bias_v[qq]);
     }
     __syncthreads();
 
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 acc[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int u0 = wave; u0 < nunits; u0 += NW * UB) {
         if (u0 != wave) load_batch(u0);
 #pragma unroll
         for (int u = 0; u < UB; ++u) {
-            const int n = ua[u] >= 0 ? s_rowof[ua[u]][col] : -1;
-            const uint16_t *src = (LDS_A ? hs_lds : hw) + static_cast<int64_t>(n) * I + ukb[u] * 32;
-            const uint32_t ww[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
-            const float scf = e8m0_to_f32(SC_LDS ? s_sc[(uaa[u] * 16 + col) * is + ukb[u]] : sc[u]);
+            // A row r = 16 mt + col: token 4 mt + col / 4, h8 row 4n + col % 4
+            const uint8_t *arow[NMT];
+            const uint8_t *asc[NMT];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint4 av = n >= 0 ? *reinterpret_cast<const uint4 *>(src + 8 * s) : zero4();
-                acc[u & 1] = mfma16(as_bf16x8(av), mxfp4_word_to_bf16x8(ww[s], scf), acc[u & 1]);
+            for (int mt = 0; mt < NMT; ++mt) {
+                const int n = ua[u] >= 0 ? s_rowof[ua[u]][4 * mt + (col >> 2)] : -1;
+                const int hr = 4 * n + (col & 3);
+                arow[mt] = n >= 0 ? (LDS_A ? dyn : h8) + static_cast<int64_t>(hr) * I : nullptr;
+                asc[mt] = n >= 0 ? hs_lds + hr * shs : nullptr;
+            }
+            uint4 lo, hi;
+            tile_chunk_to_mfma(wf[u], ws[u], lane, lo, hi);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t sb = SC_LDS ? s_sc[(uaa[u] * 16 + col) * is + min(8 * ucc[u] + 2 * g + h, nblocks - 1)]
+                                           : (h ? schi[u] : sclo[u]);
+                const i32x8 bop = mx_b_operand(h ? hi : lo);
+#pragma unroll
+                for (int mt = 0; mt < NMT; ++mt)
+                    acc[mt] = mx_step(acc[mt], arow[mt], asc[mt], bop, sb, ucc[u], h, g, nblocks);
             }
         }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        red[2 * wave][r][lane] = acc[0][r];
-        red[2 * wave + 1][r][lane] = acc[1][r];
-    }
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][mt * 4 + r][lane] = acc[mt][r];
     __syncthreads();
     if (wave != 0) return;
+    const int64_t drow = d0 + col;
+    // D rows 16mt + 4g + r: token 4mt + g, its four A rows r
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = 4 * g + r;
-        if (t >= T) continue;
-        float v = 0.f;
-        for (int w = 0; w < 2 * NW; ++w) v += red[w][r][lane];
-        y[static_cast<int64_t>(t) * H + drow] = f32_to_bf16(v + bterm[r]);
+    for (int mt = 0; mt < NMT; ++mt) {
+        const int t = 4 * mt + g;
+        if (t < T) {
+            float v = 0.f;
+            for (int w = 0; w < NW; ++w)
+                v += (red[w][mt * 4][lane] + red[w][mt * 4 + 1][lane]) + (red[w][mt * 4 + 2][lane] + red[w][mt * 4 + 3][lane]);
+            float bterm = 0.f;
+            for (int jj = 0; jj < k; ++jj) bterm += s_bprod[t * k + jj][col];
+            y[static_cast<int64_t>(t) * H + drow] = f32_to_bf16(v + bterm);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// Down-projection for more tokens: block = (routing slot, 16 output features); 4 wavefronts
-// split the contraction. part[n, d] = hw[n] . Wdn[e, d] + w[n] * bdn[e, d] for the pairs n
-// routed to e; a separate combine sums part over the k slots of each token.
+// Down-projection for more tokens: block = (routing slot, one 16-row tile of output
+// features); 4 wavefronts split the contraction in 256-wide chunks.
+// part[n, d] = h[n] . Wdn[e, d] + w[n] * bdn[e, d] for the pairs n routed to e (A rows
+// 4s .. 4s + 3 = h8 rows 4n .. 4n + 3 of the expert's s-th pair; block y takes pairs
+// 4 NMT y ..); a separate combine sums part over the k slots of each token.
 template <int NMT, int UB>
-__global__ __launch_bounds__(256) void k_down_slots(
-    const uint16_t *__restrict__ hw, const uint8_t *__restrict__ dn_blocks,
+__global__ __launch_bounds__(256) void k_down_mx_slots(
+    const uint8_t *__restrict__ h8, const uint8_t *__restrict__ hs8, const uint8_t *__restrict__ dn_blocks,
     const uint8_t *__restrict__ dn_scales, const uint16_t *__restrict__ dn_bias,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int T, int H, int I,
     int E, int k, float *__restrict__ part) {
@@ -425,37 +579,45 @@ __global__ __launch_bounds__(256) void k_down_slots(
     const int col = lane & 15, g = lane >> 4;
     const int tiles_d = H / 16;
     const int N = T * k;
-    load_routing(nullptr, topk_idx, topk_w, T, E, k, s_idx, s_w, bitmap);
+    const int shs = mx8_scale_stride(I);
+    load_routing<false>(nullptr, topk_idx, topk_w, T, E, k, s_idx, s_w, bitmap, [] {});
     const int e = expert_of_slot(bitmap, blockIdx.x / tiles_d);
     if (e < 0) return;
+    const int64_t row0 = static_cast<int64_t>(e) * H + (blockIdx.x % tiles_d) * 16;
     const int d = (blockIdx.x % tiles_d) * 16 + col;
-    const int64_t wrow = static_cast<int64_t>(e) * H + d;
-    const uint8_t *wb = dn_blocks + wrow * (I / 2);
     const int is = I / 32;
     const int nblocks = I / 32;
-    const int nchunks = (nblocks + 3) / 4;
-    // the block's 16 rows of scales: I/2 contiguous bytes, loaded before the weight stream
-    const uint8_t *sc_src = dn_scales + (static_cast<int64_t>(e) * H + (blockIdx.x % tiles_d) * 16) * is;
-    uint4 scv = tid < I / 32 ? *reinterpret_cast<const uint4 *>(sc_src + 16 * tid) : zero4();
-    uint4 b[UB];
+    const int nchunks = (nblocks + 7) / 8;
+    // the tile's 16 rows of scales: I/2 contiguous bytes, loaded before the weight stream
+    const uint4 scv = tid < I / 32 ? *reinterpret_cast<const uint4 *>(dn_scales + row0 * is + 16 * tid) : zero4();
+    const uint8_t *wrows = dn_blocks + row0 * (I / 2);
+    uint4 wf[UB], ws[UB];
     auto load_batch = [&](int c0) {
 #pragma unroll
-        for (int u = 0; u < UB; ++u) {
-            const int kb = min(4 * (c0 + 4 * u) + g, nblocks - 1);   // unconditional, clamped
-            b[u] = *reinterpret_cast<const uint4 *>(wb + kb * 16);
-        }
+        for (int u = 0; u < UB; ++u)
+            load_tile_chunk(wrows, I / 2, min(c0 + 4 * u, nchunks - 1), nblocks, lane, wf[u], ws[u]);
     };
     load_batch(wave);
     if (tid < I / 32) *reinterpret_cast<uint4 *>(s_sc + 16 * tid) = scv;
-    const float bd = bf16_to_f32(dn_bias[wrow]);
+    const float bd = bf16_to_f32(dn_bias[static_cast<int64_t>(e) * H + d]);
     if (wave == 0) rows_of_expert(s_idx, N, e, s_rows, &s_nrows);
     __syncthreads();
-    const int nrows = s_nrows;
-    const uint16_t *arow[NMT];
+    const int s0 = 4 * NMT * blockIdx.y;
+    const int nrows = s_nrows - s0;
+    if (nrows <= 0) return;                    // uniform
+    // A row r = 16 mt + col: the expert's pair s0 + r / 4, h8 row 4n + r % 4
+    const uint8_t *arow[NMT];
+    const uint8_t *asc[NMT];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
         const int r = 16 * mt + col;
-        arow[mt] = r < nrows ? hw + static_cast<int64_t>(s_rows[r]) * I : nullptr;
+        arow[mt] = nullptr;
+        asc[mt] = nullptr;
+        if ((r >> 2) < nrows) {
+            const int64_t hr = 4 * static_cast<int64_t>(s_rows[s0 + (r >> 2)]) + (r & 3);
+            arow[mt] = h8 + hr * I;
+            asc[mt] = hs8 + hr * shs;
+        }
     }
     f32x4 acc[NMT];
 #pragma unroll
@@ -464,22 +626,17 @@ __global__ __launch_bounds__(256) void k_down_slots(
         if (c0 != wave) load_batch(c0);
 #pragma unroll
         for (int u = 0; u < UB; ++u) {
-            const int kb = 4 * (c0 + 4 * u) + g;
-            const bool ok = c0 + 4 * u < nchunks && kb < nblocks;
-            const uint32_t ww[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
-            const float scf = e8m0_to_f32(s_sc[col * is + min(kb, nblocks - 1)]);
+            const int c = c0 + 4 * u;
+            if (c >= nchunks) break;   // uniform
+            uint4 lo, hi;
+            tile_chunk_to_mfma(wf[u], ws[u], lane, lo, hi);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 wv = mxfp4_word_to_bf16x8(ww[s], scf);
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t sb = s_sc[col * is + min(8 * c + 2 * g + h, nblocks - 1)];
+                const i32x8 bop = mx_b_operand(h ? hi : lo);
 #pragma unroll
-                for (int mt = 0; mt < NMT; ++mt) {
-                    if (16 * mt < nrows) {
-                        const uint4 av = (ok && arow[mt] != nullptr)
-                                             ? *reinterpret_cast<const uint4 *>(arow[mt] + kb * 32 + 8 * s)
-                                             : zero4();
-                        acc[mt] = mfma16(as_bf16x8(av), wv, acc[mt]);
-                    }
-                }
+                for (int mt = 0; mt < NMT; ++mt)
+                    if (16 * mt < 4 * nrows) acc[mt] = mx_step(acc[mt], arow[mt], asc[mt], bop, sb, c, h, g, nblocks);
             }
         }
     }
@@ -489,18 +646,19 @@ __global__ __launch_bounds__(256) void k_down_slots(
         for (int r = 0; r < 4; ++r) red[wave][mt * 4 + r][lane] = acc[mt][r];
     __syncthreads();
     if (wave != 0) return;
+    // D rows 16mt + 4g + r: pair 4mt + g, its four A rows r
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * mt + 4 * g + r;
-            if (row >= nrows) continue;
+    for (int mt = 0; mt < NMT; ++mt) {
+        const int s = 4 * mt + g;
+        if (s < nrows) {
             float v = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) v += red[w][mt * 4 + r][lane];
-            const int n = s_rows[row];
+            for (int w = 0; w < 4; ++w)
+                v += (red[w][mt * 4][lane] + red[w][mt * 4 + 1][lane]) + (red[w][mt * 4 + 2][lane] + red[w][mt * 4 + 3][lane]);
+            const int n = s_rows[s0 + s];
             part[static_cast<int64_t>(n) * H + d] = v + s_w[n] * bd;
         }
+    }
 }
 
 // y[t, d] = bf16(sum_{j < k} part[t*k + j, d]) in slot order. Thread = 4 features.
@@ -522,26 +680,38 @@ __global__ __launch_bounds__(256) void k_combine_slots(const float *__restrict__
 
 int slots_of(const Dims &d) { return static_cast<int>(d.T * d.k < d.E ? d.T * d.k : d.E); }
 
-// LDS staging of activation rows when they fit next to other resident blocks.
-bool lds_fits(int64_t rows, int K) { return rows * K * 2 <= 48 * 1024; }
-
-template <int NMT, int UB, bool LDS_A>
-hipError_t up_n(const Dims &d, const uint16_t *x, const uint8_t *gb, const uint8_t *gs,
-                const uint16_t *gbias, const double *logits, int32_t *idx, float *w, uint16_t *hw,
+template <int NMT, int UB, bool LDS_A, bool WITH_LOGITS>
+hipError_t up_n(const Dims &d, const uint8_t *x8, const uint8_t *xs8, const uint8_t *gb, const uint8_t *gs,
+                const uint16_t *gbias, const double *logits, int32_t *idx, float *w, uint8_t *h8, uint8_t *hs8,
                 hipStream_t s) {
     const unsigned blocks = static_cast<unsigned>(slots_of(d) * (d.I / 16));
-    const size_t lds = LDS_A ? static_cast<size_t>(d.T) * d.H * 2 : 0;   // every token row
-    hipLaunchKernelGGL((k_up_small<NMT, UB, LDS_A>), dim3(blocks), dim3(256), lds, s, x, gb, gs, gbias,
-                       logits, idx, w, static_cast<int>(d.T), d.H, d.I, d.E, d.k, d.alpha, d.limit, hw);
+    const unsigned groups = static_cast<unsigned>((d.T + 8 * NMT - 1) / (8 * NMT));   // an expert has <= T pairs
+    const size_t lds = (LDS_A ? static_cast<size_t>(2 * d.T) * d.H : 0) +
+                       static_cast<size_t>(2 * d.T) * mx8_scale_stride(d.H);
+    hipLaunchKernelGGL((k_up_mx<NMT, UB, LDS_A, WITH_LOGITS>), dim3(blocks, groups), dim3(256), lds, s, x8, xs8, gb, gs, gbias,
+                       logits, idx, w, static_cast<int>(d.T), d.H, d.I, d.E, d.k, d.alpha, d.limit, h8, hs8);
     return hipGetLastError();
 }
 
 template <int NMT, int UB>
-hipError_t down_slots_n(const Dims &d, const uint16_t *hw, const uint8_t *db, const uint8_t *ds,
+hipError_t down_slots_n(const Dims &d, const uint8_t *h8, const uint8_t *hs8, const uint8_t *db, const uint8_t *ds,
                         const uint16_t *dbias, int32_t *idx, float *w, float *part, hipStream_t s) {
     const unsigned blocks = static_cast<unsigned>(slots_of(d) * (d.H / 16));
-    hipLaunchKernelGGL((k_down_slots<NMT, UB>), dim3(blocks), dim3(256), 0, s, hw, db, ds, dbias, idx, w,
+    const unsigned groups = static_cast<unsigned>((d.T + 4 * NMT - 1) / (4 * NMT));
+    hipLaunchKernelGGL((k_down_mx_slots<NMT, UB>), dim3(blocks, groups), dim3(256), 0, s, h8, hs8, db, ds, dbias, idx, w,
                        static_cast<int>(d.T), d.H, d.I, d.E, d.k, part);
+    return hipGetLastError();
+}
+
+template <int NMT, int NW, int UB, bool LDS_A, bool SC_LDS>
+hipError_t down_tokens_n(const Dims &d, const uint8_t *h8, const uint8_t *hs8, const uint8_t *db, const uint8_t *ds,
+                         const uint16_t *dbias, int32_t *idx, float *w, uint16_t *y, hipStream_t s) {
+    const int64_t N = d.T * d.k;
+    const size_t lds = (LDS_A ? static_cast<size_t>(4 * N) * d.I : 0) +
+                       static_cast<size_t>(4 * N) * mx8_scale_stride(d.I);
+    hipLaunchKernelGGL((k_down_mx_tokens<NMT, NW, UB, LDS_A, SC_LDS>), dim3(static_cast<unsigned>(d.H / 16)),
+                       dim3(NW * 64), lds, s, h8, hs8, db, ds, dbias, idx, w, static_cast<int>(d.T), d.H, d.I, d.E,
+                       d.k, y);
     return hipGetLastError();
 }
 
@@ -554,52 +724,49 @@ hipError_t launch_combine_decode(const Dims &d, const float *part, uint16_t *y, 
     return hipGetLastError();
 }
 
-hipError_t launch_up_decode(const Dims &d, const uint16_t *x, const uint8_t *gu_blocks,
+hipError_t launch_up_decode(const Dims &d, const uint8_t *x8, const uint8_t *gu_blocks,
                             const uint8_t *gu_scales, const uint16_t *gu_bias, const double *logits,
-                            int32_t *topk_idx, float *topk_w, uint16_t *hw, hipStream_t s) {
-    const int nmt = static_cast<int>((d.T + 15) / 16);
+                            int32_t *topk_idx, float *topk_w, uint8_t *h8, hipStream_t s) {
+    const uint8_t *xs8 = x8 + static_cast<size_t>(2 * d.T) * d.H;
+    uint8_t *hs8 = h8 + static_cast<size_t>(4 * d.T * d.k) * d.I;   // h8: mx8 matrix of 2 T k rows
+    const bool lds_a = mx8_bytes(d.T, d.H) <= static_cast<size_t>(kStageLds);
+    // A rows: 2 per routed pair of the expert, at most 2T
+    const int nmt = static_cast<int>((2 * d.T + 15) / 16);
+    if (logits != nullptr) {   // T <= kDownTokensMaxT: top-k in the prologue
+        if (nmt == 1)
+            return lds_a ? up_n<1, 6, true, true>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, h8, hs8, s)
+                         : up_n<1, 6, false, true>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, h8, hs8, s);
+        return up_n<2, 6, false, true>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, h8, hs8, s);
+    }
     switch (nmt) {
-        case 1:
-            return lds_fits(d.T, d.H)
-                       ? up_n<1, 6, true>(d, x, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, hw, s)
-                       : up_n<1, 3, false>(d, x, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, hw, s);
-        case 2: return up_n<2, 3, false>(d, x, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, hw, s);
-        case 3: return up_n<3, 2, false>(d, x, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, hw, s);
-        default: return up_n<4, 2, false>(d, x, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, hw, s);
+        case 1: return up_n<1, 6, false, false>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, nullptr, topk_idx, topk_w, h8, hs8, s);
+        case 2: return up_n<2, 6, false, false>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, nullptr, topk_idx, topk_w, h8, hs8, s);
+        default: return up_n<4, 4, false, false>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, nullptr, topk_idx, topk_w, h8, hs8, s);
     }
 }
 
-hipError_t launch_down_decode(const Dims &d, const uint16_t *hw, const uint8_t *dn_blocks,
+hipError_t launch_down_decode(const Dims &d, const uint8_t *h8, const uint8_t *dn_blocks,
                               const uint8_t *dn_scales, const uint16_t *dn_bias, int32_t *topk_idx,
                               float *topk_w, float *part, uint16_t *y, hipStream_t s) {
+    const int64_t N = d.T * d.k;
+    const uint8_t *hs8 = h8 + static_cast<size_t>(4 * N) * d.I;   // h8: mx8 matrix of 2N rows
     if (d.T <= kDownTokensMaxT) {
-        constexpr int NW = 16;
-        const unsigned blocks = static_cast<unsigned>(d.H / 16);
-        // scale rows of every routed expert: at most min(T*k, E) experts x 16 rows x I/32 bytes
+        // weight scale rows of every routed expert: at most min(T*k, E) experts x 16 rows x I/32 bytes
         const bool sc_lds = static_cast<int64_t>(slots_of(d)) * (d.I / 2) <= kDownScaleLds;
-        if (lds_fits(d.T * d.k, d.I)) {
-            const size_t lds = static_cast<size_t>(d.T) * d.k * d.I * 2;
+        const bool lds_a = mx8_bytes(2 * N, d.I) <= static_cast<size_t>(kStageLds);
+        if (d.T <= 4) {
+            if (lds_a && sc_lds)
+                return down_tokens_n<1, 16, 3, true, true>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
             if (sc_lds)
-                hipLaunchKernelGGL((k_down_tokens<6, NW, true, true>), dim3(blocks), dim3(NW * 64), lds, s, hw,
-                                   dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, static_cast<int>(d.T),
-                                   d.H, d.I, d.E, d.k, y);
-            else
-                hipLaunchKernelGGL((k_down_tokens<6, NW, true, false>), dim3(blocks), dim3(NW * 64), lds, s, hw,
-                                   dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, static_cast<int>(d.T),
-                                   d.H, d.I, d.E, d.k, y);
-        } else {
-            hipLaunchKernelGGL((k_down_tokens<4, NW, false, false>), dim3(blocks), dim3(NW * 64), 0, s, hw,
-                               dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, static_cast<int>(d.T), d.H,
-                               d.I, d.E, d.k, y);
+                return down_tokens_n<1, 16, 3, false, true>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
+            return down_tokens_n<1, 16, 3, false, false>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
         }
-        return hipGetLastError();
+        if (d.T <= 8)
+            return down_tokens_n<2, 8, 6, false, false>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
+        return down_tokens_n<4, 8, 4, false, false>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
     }
-    const int nmt = static_cast<int>((d.T + 15) / 16);
-    switch (nmt) {
-        case 2: return down_slots_n<2, 3>(d, hw, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, part, s);
-        case 3: return down_slots_n<3, 3>(d, hw, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, part, s);
-        default: return down_slots_n<4, 2>(d, hw, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, part, s);
-    }
+    // pairs of one expert: at most T; blocks of 16 pairs (4 m-tiles of 4 A rows each) along y
+    return down_slots_n<4, 3>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, part, s);
 }
 
 }  // namespace moe

@@ -25,13 +25,15 @@ struct Dims {
 };
 
 // Router logits only (double [T, E]); for few tokens, where the top-k runs in the
-// up-projection. Needs H <= 6144.
+// up-projection. Needs H <= 6144. Also writes x as an mx8 matrix (T rows of H, mx_mfma.h).
 hipError_t launch_logits(const Dims &d, const uint16_t *x, const uint16_t *router_w,
-                         const uint16_t *router_b, double *logits, hipStream_t s);
+                         const uint16_t *router_b, double *logits, uint8_t *x8, hipStream_t s);
 
+// Router, top-k and softmax; with x8 != nullptr (T <= kDecodeMaxT) also writes x as an mx8
+// matrix.
 hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *router_w,
                         const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
-                        float *logits, hipStream_t s);
+                        float *logits, uint8_t *x8, hipStream_t s);
 
 hipError_t launch_permute(const Dims &d, const int32_t *topk_idx, const float *topk_w,
                           int32_t *offsets, int32_t *sorted_token, float *sorted_w,
@@ -55,16 +57,18 @@ hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row
 // workgroup and writes y directly (beyond: per-slot partial sums + a combine kernel).
 constexpr int64_t kDownTokensMaxT = 16;
 
-// up: hw[t*k + j, :] = bf16(w[t, j] * swiglu(x[t] . Wgu[e_tj]^T + bgu[e_tj])). With `logits`
-// (double [T, E], T <= kDownTokensMaxT) every block computes the top-k + softmax itself and
-// block 0 writes it to topk_idx / topk_w; with logits == nullptr they are inputs.
-hipError_t launch_up_decode(const Dims &d, const uint16_t *x, const uint8_t *gu_blocks,
+// up: h[t*k + j, :] = w[t, j] * swiglu(x[t] . Wgu[e_tj]^T + bgu[e_tj]) as the mx8 matrix h8
+// of 2 T k rows of I (row 2n + half: one 16-value half of every MX block of h[n], zeros in
+// the other), from the mx8 matrix x8 (T rows of H). With `logits` (double [T, E],
+// T <= kDownTokensMaxT) every block computes the top-k + softmax itself and block 0 writes
+// it to topk_idx / topk_w; with logits == nullptr they are inputs.
+hipError_t launch_up_decode(const Dims &d, const uint8_t *x8, const uint8_t *gu_blocks,
                             const uint8_t *gu_scales, const uint16_t *gu_bias, const double *logits,
-                            int32_t *topk_idx, float *topk_w, uint16_t *hw, hipStream_t s);
-// down: T <= kDownTokensMaxT: y[t, :] = bf16(sum_j hw[t*k + j] . Wdn[e_tj]^T + w[t, j] * bdn[e_tj]);
-// otherwise part[t*k + j, :] = hw[t*k + j] . Wdn[e_tj]^T + w[t, j] * bdn[e_tj] (fp32, [T*k, H])
+                            int32_t *topk_idx, float *topk_w, uint8_t *h8, hipStream_t s);
+// down: T <= kDownTokensMaxT: y[t, :] = bf16(sum_j h[t*k + j] . Wdn[e_tj]^T + w[t, j] * bdn[e_tj]);
+// otherwise part[t*k + j, :] = h[t*k + j] . Wdn[e_tj]^T + w[t, j] * bdn[e_tj] (fp32, [T*k, H])
 // and launch_combine_decode forms y.
-hipError_t launch_down_decode(const Dims &d, const uint16_t *hw, const uint8_t *dn_blocks,
+hipError_t launch_down_decode(const Dims &d, const uint8_t *h8, const uint8_t *dn_blocks,
                               const uint8_t *dn_scales, const uint16_t *dn_bias, int32_t *topk_idx,
                               float *topk_w, float *part, uint16_t *y, hipStream_t s);
 // y[t, :] = bf16(sum_{j < k} part[t*k + j, :]), slot order.

@@ -10,6 +10,7 @@
 // the identical summation sequence here) resolve to the lower expert index.
 #include "device_common.h"
 #include "kernels.h"
+#include "mx_mfma.h"
 #include "topk.h"
 
 #include <math.h>
@@ -40,10 +41,10 @@ template <int NI>
 __global__ __launch_bounds__(512) void k_route_token(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     const uint16_t *__restrict__ br, int H, int E, int k, int32_t *__restrict__ topk_idx,
-    float *__restrict__ topk_w, float *__restrict__ logits_out) {
+    float *__restrict__ topk_w, float *__restrict__ logits_out, uint8_t *__restrict__ x8, int T) {
     constexpr int kEPW = 4;
     __shared__ double lg[kMaxE];
-    __shared__ double s_ex[8];
+    __shared__ __attribute__((aligned(16))) uint64_t s_tk[kTopkScratch];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t t = blockIdx.x;
     const uint16_t *xr = x + t * H;
@@ -85,21 +86,28 @@ __global__ __launch_bounds__(512) void k_route_token(
     __syncthreads();
     if (wave == 0)
         topk_softmax_wave(lg, E, k, lane, topk_idx + t * k, topk_w + t * k, nullptr, nullptr,
-                          logits_out ? logits_out + t * E : nullptr, s_ex);
+                          logits_out ? logits_out + t * E : nullptr, s_tk);
+    if (x8 != nullptr) write_mx8_row(xr, H, x8, T, t);
 }
 
 // Logits only, for few tokens (the top-k then runs in the up-projection's prologue): block
 // (expert pair, token); its 4 wavefronts split H (lane l of wavefront w covers
 // h = 8l + 512(w + 4i)) and their partial sums are added in wavefront order.
 //   logits[t, e] = sum_h x[t, h] * Wr[e, h] + br[e]     (double)
+// One extra block per token (the last in x) writes the token as an mx8 row of x8 (T rows)
+// for the expert GEMMs.
 template <int NIQ>
 __global__ __launch_bounds__(256) void k_logits(const uint16_t *__restrict__ x,
                                                 const uint16_t *__restrict__ wr,
                                                 const uint16_t *__restrict__ br, int H, int E,
-                                                double *__restrict__ logits) {
+                                                double *__restrict__ logits, uint8_t *__restrict__ x8, int T) {
     __shared__ double part[4][2];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t t = blockIdx.y;
+    if (blockIdx.x == gridDim.x - 1) {   // the extra block: token t as an mx8 row
+        write_mx8_row(x + t * H, H, x8, T, t);
+        return;
+    }
     const int e0 = 2 * blockIdx.x;
     const bool has2 = e0 + 1 < E;
     const uint16_t *xr = x + t * H;
@@ -143,9 +151,10 @@ template <int NW, int TPB>
 __global__ __launch_bounds__(NW * 64) void k_route(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     const uint16_t *__restrict__ br, int64_t T, int H, int E, int k,
-    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ logits_out) {
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ logits_out,
+    uint8_t *__restrict__ x8) {
     __shared__ double lg[TPB][kMaxE];
-    __shared__ double s_ex[NW][8];
+    __shared__ __attribute__((aligned(16))) uint64_t s_tk[NW][kTopkScratch];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TPB;
@@ -181,28 +190,30 @@ __global__ __launch_bounds__(NW * 64) void k_route(
         const int64_t t = t0 + tt;
         if (t >= T) continue;
         topk_softmax_wave(lg[tt], E, k, lane, topk_idx + t * k, topk_w + t * k, nullptr, nullptr,
-                          logits_out ? logits_out + t * E : nullptr, s_ex[wave]);
+                          logits_out ? logits_out + t * E : nullptr, s_tk[wave]);
     }
+    if (x8 != nullptr)
+        for (int tt = 0; tt < TPB && t0 + tt < T; ++tt) write_mx8_row(x + (t0 + tt) * H, H, x8, T, t0 + tt);
 }
 
 template <int NI>
 void launch_token(const Dims &d, const uint16_t *x, const uint16_t *w, const uint16_t *b,
-                  int32_t *idx, float *wt, float *logits, hipStream_t s) {
+                  int32_t *idx, float *wt, float *logits, uint8_t *x8, hipStream_t s) {
     hipLaunchKernelGGL((k_route_token<NI>), dim3(static_cast<unsigned>(d.T)), dim3(512), 0, s, x, w,
-                       b, d.H, d.E, d.k, idx, wt, logits);
+                       b, d.H, d.E, d.k, idx, wt, logits, x8, static_cast<int>(d.T));
 }
 
 }  // namespace
 
 hipError_t launch_logits(const Dims &d, const uint16_t *x, const uint16_t *router_w,
-                         const uint16_t *router_b, double *logits, hipStream_t s) {
+                         const uint16_t *router_b, double *logits, uint8_t *x8, hipStream_t s) {
     if (d.T <= 0) return hipSuccess;
     const int niq = (d.H + 2047) / 2048;
-    const dim3 grid(static_cast<unsigned>((d.E + 1) / 2), static_cast<unsigned>(d.T));
+    const dim3 grid(static_cast<unsigned>((d.E + 1) / 2 + 1), static_cast<unsigned>(d.T));
     switch (niq) {
-        case 1: hipLaunchKernelGGL((k_logits<1>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits); break;
-        case 2: hipLaunchKernelGGL((k_logits<2>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits); break;
-        case 3: hipLaunchKernelGGL((k_logits<3>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits); break;
+        case 1: hipLaunchKernelGGL((k_logits<1>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
+        case 2: hipLaunchKernelGGL((k_logits<2>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
+        case 3: hipLaunchKernelGGL((k_logits<3>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
         default: return hipErrorInvalidValue;   // H > 6144: the caller uses launch_route
     }
     return hipGetLastError();
@@ -210,23 +221,23 @@ hipError_t launch_logits(const Dims &d, const uint16_t *x, const uint16_t *route
 
 hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *router_w,
                         const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
-                        float *logits, hipStream_t s) {
+                        float *logits, uint8_t *x8, hipStream_t s) {
     if (d.T <= 0) return hipSuccess;
     const int ni = (d.H + 511) / 512;
     if (d.T <= kDecodeMaxT && ni <= 7) {
         switch (ni) {
-            case 1: launch_token<1>(d, x, router_w, router_b, topk_idx, topk_w, logits, s); break;
-            case 2: launch_token<2>(d, x, router_w, router_b, topk_idx, topk_w, logits, s); break;
-            case 3: launch_token<3>(d, x, router_w, router_b, topk_idx, topk_w, logits, s); break;
-            case 4: launch_token<4>(d, x, router_w, router_b, topk_idx, topk_w, logits, s); break;
-            case 5: launch_token<5>(d, x, router_w, router_b, topk_idx, topk_w, logits, s); break;
-            case 6: launch_token<6>(d, x, router_w, router_b, topk_idx, topk_w, logits, s); break;
-            default: launch_token<7>(d, x, router_w, router_b, topk_idx, topk_w, logits, s); break;
+            case 1: launch_token<1>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            case 2: launch_token<2>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            case 3: launch_token<3>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            case 4: launch_token<4>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            case 5: launch_token<5>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            case 6: launch_token<6>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            default: launch_token<7>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
         }
     } else {
         const int64_t blocks = (d.T + 3) / 4;
         hipLaunchKernelGGL((k_route<4, 4>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                           x, router_w, router_b, d.T, d.H, d.E, d.k, topk_idx, topk_w, logits);
+                           x, router_w, router_b, d.T, d.H, d.E, d.k, topk_idx, topk_w, logits, x8);
     }
     return hipGetLastError();
 }

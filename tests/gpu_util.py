@@ -62,6 +62,14 @@ def gamma(n: int) -> float:
     return n * U64 / (1 - n * U64)
 
 
+def selection_tolerance(H: int, abs_sum: np.ndarray) -> np.ndarray:
+    """Per-token band within which two logits may be ordered either way by the GPU path:
+    the error bound of any fp64 summation order of H+1 terms, plus the selection key's
+    resolution (logits closer than 2^-44 relative count as equal there; 2^-43 covers both
+    sides)."""
+    return (4 * gamma(H + 1) + 2.0 ** -43) * abs_sum.max(axis=1)
+
+
 def decided_tokens(ref: dict, H: int, k: int) -> np.ndarray:
     """Mask of tokens whose top-k set is fixed beyond the summation-error margin."""
     logits, abs_sum = ref["logits"], ref["abs_sum"]
@@ -70,8 +78,7 @@ def decided_tokens(ref: dict, H: int, k: int) -> np.ndarray:
         return np.ones(logits.shape[0], dtype=bool)
     srt = -np.sort(-logits, axis=1)
     margin = srt[:, k - 1] - srt[:, k]
-    tau = 4 * gamma(H + 1) * abs_sum.max(axis=1)
-    return margin > tau
+    return margin > selection_tolerance(H, abs_sum)
 
 
 def check_selection(gpu_idx: np.ndarray, ref: dict, H: int, k: int):
@@ -79,7 +86,7 @@ def check_selection(gpu_idx: np.ndarray, ref: dict, H: int, k: int):
     of tokens whose outputs can be compared."""
     decided = decided_tokens(ref, H, k)
     np.testing.assert_array_equal(gpu_idx[decided], ref["idx"][decided])
-    tau = 4 * gamma(H + 1) * ref["abs_sum"].max(axis=1)
+    tau = selection_tolerance(H, ref["abs_sum"])
     for t in np.nonzero(~decided)[0]:
         sel = set(gpu_idx[t].tolist())
         assert len(sel) == k
