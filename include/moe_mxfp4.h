@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_MXFP4_ABI_VERSION 1
+#define MOE_MXFP4_ABI_VERSION 2
 
 typedef uint16_t moe_bf16_t;
 
@@ -165,25 +165,49 @@ moe_status_t moe_mxfp4_permute(const moe_mxfp4_shape_t *shape,
                                float *sorted_weight, int32_t *slot_row, void *stream);
 
 /*
- * Steps 3-4 over the sorted rows (grouped gate_up GEMM with fused MXFP4 dequantization,
- * bias and clamped SwiGLU):  h[r, :] = swiglu(x[sorted_token[r]] . Wgu[e]^T + bgu[e])
- * for every row r of expert e. h [T*k, I] bf16 (out). expert_offsets / sorted_token as
- * produced by moe_mxfp4_permute.
+ * mx8 activation matrix: the expert GEMMs' activation format. gfx950's block-scaled MFMA
+ * takes the packed MXFP4 weight blocks as stored (OCP Microscaling Formats v1.0, which the
+ * ZeroModels GPT-OSS page's "MXFP4 experts" item refers to: 32-element blocks with one E8M0
+ * scale) against OCP E4M3 activations carrying their own E8M0 block scales. An activation
+ * row of K values becomes two rows of K bytes: for each 32-element block with largest
+ * magnitude m, eb = floor(log2 m) - 7 (0 for an all-zero block), hi = E4M3(x / 2^eb)
+ * rounded to nearest even, lo = E4M3(16 * (x / 2^eb - hi)), with scales 127 + eb (hi) and
+ * 123 + eb (lo); x = hi * 2^eb + lo * 2^(eb-4), exactly for bf16 x unless lo falls below
+ * E4M3's normal range (elements more than about 2^13 below their block's largest).
+ * Layout for R rows of K values (K a multiple of 32): 2R rows of K bytes (row 2r = hi,
+ * row 2r+1 = lo of row r), then 2R rows of S = roundup(K/32, 16) scale bytes (row-major;
+ * bytes past K/32 in a row are unused). Total moe_mxfp4_mx8_bytes(R, K) = 2R (K + S).
+ */
+size_t moe_mxfp4_mx8_bytes(int64_t rows, int32_t cols);
+
+/*
+ * bf16 [rows, cols] -> mx8 (layout above). q8 needs moe_mxfp4_mx8_bytes(rows, cols)
+ * bytes, 16-byte aligned. cols must be a positive multiple of 32; rows >= 0.
+ */
+moe_status_t moe_mxfp4_quantize_act(const moe_bf16_t *x, int64_t rows, int32_t cols,
+                                    uint8_t *q8, void *stream);
+
+/*
+ * Steps 3-4 over the sorted rows (grouped gate_up GEMM on the block-scaled MFMA, bias,
+ * clamped SwiGLU): h[r, :] = swiglu(x[sorted_token[r]] . Wgu[e]^T + bgu[e]) for every row r
+ * of expert e. x8: x as an mx8 matrix of T rows of H (from moe_mxfp4_quantize_act);
+ * h8 (out): h as an mx8 matrix of T*k rows of I (moe_mxfp4_mx8_bytes(T*k, I) bytes),
+ * rows in sorted order. expert_offsets / sorted_token as produced by moe_mxfp4_permute.
  */
 moe_status_t moe_mxfp4_expert_up(const moe_mxfp4_shape_t *shape,
-                                 const moe_bf16_t *x,
+                                 const uint8_t *x8,
                                  const uint8_t *gu_blocks, const uint8_t *gu_scales,
                                  const moe_bf16_t *gu_bias,
                                  const int32_t *expert_offsets, const int32_t *sorted_token,
-                                 moe_bf16_t *h, void *stream);
+                                 uint8_t *h8, void *stream);
 
 /*
- * Step 5 over the sorted rows (grouped down GEMM with fused dequantization and bias),
- * scaled by the row's routing weight: o[r, :] = sorted_weight[r] * (h[r] . Wdn[e]^T + bdn[e]).
- * o [T*k, H] fp32 (out).
+ * Step 5 over the sorted rows (grouped down GEMM on the block-scaled MFMA, bias), scaled
+ * by the row's routing weight: o[r, :] = sorted_weight[r] * (h[r] . Wdn[e]^T + bdn[e]).
+ * h8: an mx8 matrix of T*k rows of I; o [T*k, H] fp32 (out).
  */
 moe_status_t moe_mxfp4_expert_down(const moe_mxfp4_shape_t *shape,
-                                   const moe_bf16_t *h,
+                                   const uint8_t *h8,
                                    const uint8_t *dn_blocks, const uint8_t *dn_scales,
                                    const moe_bf16_t *dn_bias,
                                    const int32_t *expert_offsets, const float *sorted_weight,

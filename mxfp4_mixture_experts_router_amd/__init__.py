@@ -24,7 +24,8 @@ import torch
 __all__ = [
     "MoeError", "MoeLibraryMissing", "library_path", "load_library", "abi_version",
     "workspace_bytes", "moe_forward", "route", "permute", "expert_up", "expert_down",
-    "combine", "dequant", "DECODE_MAX_T", "DECODE_MAX_K", "uses_decode_path",
+    "combine", "dequant", "DECODE_MAX_T", "DECODE_MAX_K", "uses_decode_path", "mx8_bytes",
+    "quantize_act",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -76,6 +77,8 @@ _SIGS = {
     "moe_mxfp4_expert_down": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 8),
     "moe_mxfp4_combine": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 4),
     "moe_mxfp4_dequant": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp]),
+    "moe_mxfp4_mx8_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
+    "moe_mxfp4_quantize_act": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp]),
 }
 
 
@@ -224,34 +227,49 @@ def permute(topk_idx, topk_w, E: int, stream=None):
     return offsets, sorted_token, sorted_w, slot_row
 
 
-def expert_up(x, gu_blocks, gu_scales, gu_bias, offsets, sorted_token, k: int,
-              alpha: float = 1.702, limit: float = 7.0, stream=None):
-    """Grouped gate_up GEMM + SwiGLU over sorted rows. Returns h [T*k, I] bf16."""
-    T, H = x.shape
-    E, I2, _ = gu_blocks.shape
-    I = I2 // 2
+def mx8_bytes(rows: int, cols: int) -> int:
+    """Bytes of an mx8 activation matrix of rows x cols values (see moe_mxfp4.h)."""
+    return int(load_library().moe_mxfp4_mx8_bytes(rows, cols))
+
+
+def quantize_act(x, stream=None):
+    """bf16 [R, K] -> mx8 matrix (flat uint8 tensor of mx8_bytes(R, K) bytes)."""
+    R, K = x.shape
     dev = x.device
-    _need(x, "x", _BF16, (T, H), dev)
+    _need(x, "x", _BF16, (R, K), dev)
+    q8 = torch.empty(mx8_bytes(R, K), dtype=torch.uint8, device=dev)
+    _check(load_library().moe_mxfp4_quantize_act(_ptr(x), R, K, _ptr(q8), _stream(stream)))
+    return q8
+
+
+def expert_up(x8, T: int, gu_blocks, gu_scales, gu_bias, offsets, sorted_token, k: int,
+              alpha: float = 1.702, limit: float = 7.0, stream=None):
+    """Grouped gate_up GEMM + SwiGLU over sorted rows, from x8 (mx8, T rows of H). Returns
+    h8: the mx8 matrix of T*k rows of I (flat uint8)."""
+    E, I2, Hh = gu_blocks.shape
+    I, H = I2 // 2, 2 * Hh
+    dev = gu_blocks.device
+    _need(x8, "x8", _U8, (mx8_bytes(T, H),), dev)
     _need(gu_blocks, "gu_blocks", _U8, (E, 2 * I, H // 2), dev)
     _need(gu_scales, "gu_scales", _U8, (E, 2 * I, H // 32), dev)
     _need(gu_bias, "gu_bias", _BF16, (E, 2 * I), dev)
     _need(offsets, "offsets", (torch.int32,), (E + 1,), dev)
     _need(sorted_token, "sorted_token", (torch.int32,), (T * k,), dev)
-    h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+    h8 = torch.empty(mx8_bytes(T * k, I), dtype=torch.uint8, device=dev)
     shape = _shape(T, H, I, E, k, alpha, limit)
-    _check(load_library().moe_mxfp4_expert_up(ctypes.byref(shape), _ptr(x), _ptr(gu_blocks),
+    _check(load_library().moe_mxfp4_expert_up(ctypes.byref(shape), _ptr(x8), _ptr(gu_blocks),
                                                _ptr(gu_scales), _ptr(gu_bias), _ptr(offsets),
-                                               _ptr(sorted_token), _ptr(h), _stream(stream)))
-    return h
+                                               _ptr(sorted_token), _ptr(h8), _stream(stream)))
+    return h8
 
 
-def expert_down(h, dn_blocks, dn_scales, dn_bias, offsets, sorted_weight, k: int, stream=None):
-    """Grouped down GEMM + bias, times the row's routing weight. Returns o [T*k, H] fp32."""
-    N, I = h.shape
-    E, H, _ = dn_blocks.shape
-    T = N // k
-    dev = h.device
-    _need(h, "h", _BF16, (N, I), dev)
+def expert_down(h8, T: int, dn_blocks, dn_scales, dn_bias, offsets, sorted_weight, k: int, stream=None):
+    """Grouped down GEMM + bias, times the row's routing weight, from h8 (mx8, T*k rows of I).
+    Returns o [T*k, H] fp32."""
+    E, H, Ih = dn_blocks.shape
+    I, N = 2 * Ih, T * k
+    dev = dn_blocks.device
+    _need(h8, "h8", _U8, (mx8_bytes(N, I),), dev)
     _need(dn_blocks, "dn_blocks", _U8, (E, H, I // 2), dev)
     _need(dn_scales, "dn_scales", _U8, (E, H, I // 32), dev)
     _need(dn_bias, "dn_bias", _BF16, (E, H), dev)
@@ -259,7 +277,7 @@ def expert_down(h, dn_blocks, dn_scales, dn_bias, offsets, sorted_weight, k: int
     _need(sorted_weight, "sorted_weight", (torch.float32,), (N,), dev)
     o = torch.empty((N, H), dtype=torch.float32, device=dev)
     shape = _shape(T, H, I, E, k)
-    _check(load_library().moe_mxfp4_expert_down(ctypes.byref(shape), _ptr(h), _ptr(dn_blocks),
+    _check(load_library().moe_mxfp4_expert_down(ctypes.byref(shape), _ptr(h8), _ptr(dn_blocks),
                                                  _ptr(dn_scales), _ptr(dn_bias), _ptr(offsets),
                                                  _ptr(sorted_weight), _ptr(o), _stream(stream)))
     return o

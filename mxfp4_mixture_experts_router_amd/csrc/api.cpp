@@ -58,7 +58,7 @@ moe::Dims dims_of(const moe_mxfp4_shape_t *s) {
 
 // Workspace regions (each 256-byte aligned), in order.
 struct Layout {
-    size_t idx, w, logits, offsets, sorted_token, sorted_w, slot_row, h, o, part, x8, h8, total;
+    size_t idx, w, logits, offsets, sorted_token, sorted_w, slot_row, o, part, x8, h8, total;
 };
 
 size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -78,15 +78,16 @@ Layout layout_of(const moe_mxfp4_shape_t *s) {
         L.part = p;
         if (s->T > moe::kDownTokensMaxT) p += round_up(N * static_cast<size_t>(s->H) * 4);
         L.logits = p;   p += round_up(static_cast<size_t>(s->T) * s->E * 8);
-        L.h = L.offsets = L.sorted_token = L.sorted_w = L.slot_row = L.o = 0;
+        L.offsets = L.sorted_token = L.sorted_w = L.slot_row = L.o = 0;
     } else {
         L.offsets = p;      p += round_up((static_cast<size_t>(s->E) + 1) * 4);
         L.sorted_token = p; p += round_up(N * 4);
         L.sorted_w = p;     p += round_up(N * 4);
         L.slot_row = p;     p += round_up(N * 4);
-        L.h = p;            p += round_up(N * static_cast<size_t>(s->I) * 2);
+        L.x8 = p;           p += round_up(moe::mx8_bytes(s->T, s->H));
+        L.h8 = p;           p += round_up(moe::mx8_bytes(static_cast<int64_t>(N), s->I));
         L.o = p;            p += round_up(N * static_cast<size_t>(s->H) * 4);
-        L.part = L.x8 = L.h8 = 0;
+        L.part = 0;
     }
     L.total = p;
     return L;
@@ -178,7 +179,6 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     int32_t *idx = topk_idx ? topk_idx : reinterpret_cast<int32_t *>(ws + L.idx);
     float *w = topk_w ? topk_w : reinterpret_cast<float *>(ws + L.w);
-    uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
     int launched = 0;
     auto mark = [&]() -> moe_status_t {
         if (!events) return MOE_OK;
@@ -212,15 +212,16 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
         if (shape->T > moe::kDownTokensMaxT) STEP(moe::launch_combine_decode(d, part, y, s), "combine (decode)");
         return ok();
     }
-    STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, nullptr, s), "route");
+    uint8_t *x8 = ws + L.x8, *h8 = ws + L.h8;
+    STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, x8, s), "route");
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
     int32_t *sorted_token = reinterpret_cast<int32_t *>(ws + L.sorted_token);
     float *sorted_w = reinterpret_cast<float *>(ws + L.sorted_w);
     int32_t *slot_row = reinterpret_cast<int32_t *>(ws + L.slot_row);
     float *o = reinterpret_cast<float *>(ws + L.o);
     STEP(moe::launch_permute(d, idx, w, offsets, sorted_token, sorted_w, slot_row, s), "permute");
-    STEP(moe::launch_up_grouped(d, x, gu_blocks, gu_scales, gu_bias, offsets, sorted_token, h, s), "up");
-    STEP(moe::launch_down_grouped(d, h, dn_blocks, dn_scales, dn_bias, offsets, sorted_w, o, s), "down");
+    STEP(moe::launch_up_grouped(d, x8, gu_blocks, gu_scales, gu_bias, offsets, sorted_token, h8, s), "up");
+    STEP(moe::launch_down_grouped(d, h8, dn_blocks, dn_scales, dn_bias, offsets, sorted_w, o, s), "down");
     STEP(moe::launch_combine(d, o, slot_row, y, s), "combine");
 #undef STEP
     return ok();
@@ -287,40 +288,55 @@ MOE_EXPORT moe_status_t moe_mxfp4_permute(const moe_mxfp4_shape_t *shape, const 
     return ok();
 }
 
-MOE_EXPORT moe_status_t moe_mxfp4_expert_up(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
+MOE_EXPORT size_t moe_mxfp4_mx8_bytes(int64_t rows, int32_t cols) {
+    return rows > 0 && cols > 0 ? moe::mx8_bytes(rows, cols) : 0;
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_quantize_act(const moe_bf16_t *x, int64_t rows, int32_t cols,
+                                               uint8_t *q8, void *stream) {
+    if (rows < 0) return fail(MOE_EINVAL, "rows must be >= 0 (got %lld)", static_cast<long long>(rows));
+    if (cols <= 0 || cols % 32 != 0) return fail(MOE_ESHAPE, "cols must be a positive multiple of 32 (got %d)", cols);
+    if (rows == 0) return ok();
+    REQUIRE16(x, "x");
+    REQUIRE16(q8, "q8");
+    LAUNCH(moe::launch_quantize(x, rows, cols, q8, static_cast<hipStream_t>(stream)), "quantize");
+    return ok();
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_expert_up(const moe_mxfp4_shape_t *shape, const uint8_t *x8,
                                             const uint8_t *gu_blocks, const uint8_t *gu_scales,
                                             const moe_bf16_t *gu_bias, const int32_t *expert_offsets,
-                                            const int32_t *sorted_token, moe_bf16_t *h, void *stream) {
+                                            const int32_t *sorted_token, uint8_t *h8, void *stream) {
     moe_status_t st = check_shape(shape, true);
     if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
-    REQUIRE16(x, "x");
+    REQUIRE16(x8, "x8");
     REQUIRE16(gu_blocks, "gu_blocks");
     REQUIRE(gu_scales, "gu_scales");
     REQUIRE(gu_bias, "gu_bias");
     REQUIRE(expert_offsets, "expert_offsets");
     REQUIRE(sorted_token, "sorted_token");
-    REQUIRE16(h, "h");
-    LAUNCH(moe::launch_up_grouped(dims_of(shape), x, gu_blocks, gu_scales, gu_bias, expert_offsets,
-                                  sorted_token, h, static_cast<hipStream_t>(stream)), "up");
+    REQUIRE16(h8, "h8");
+    LAUNCH(moe::launch_up_grouped(dims_of(shape), x8, gu_blocks, gu_scales, gu_bias, expert_offsets,
+                                  sorted_token, h8, static_cast<hipStream_t>(stream)), "up");
     return ok();
 }
 
-MOE_EXPORT moe_status_t moe_mxfp4_expert_down(const moe_mxfp4_shape_t *shape, const moe_bf16_t *h,
+MOE_EXPORT moe_status_t moe_mxfp4_expert_down(const moe_mxfp4_shape_t *shape, const uint8_t *h8,
                                               const uint8_t *dn_blocks, const uint8_t *dn_scales,
                                               const moe_bf16_t *dn_bias, const int32_t *expert_offsets,
                                               const float *sorted_weight, float *o, void *stream) {
     moe_status_t st = check_shape(shape, true);
     if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
-    REQUIRE16(h, "h");
+    REQUIRE16(h8, "h8");
     REQUIRE16(dn_blocks, "dn_blocks");
     REQUIRE(dn_scales, "dn_scales");
     REQUIRE(dn_bias, "dn_bias");
     REQUIRE(expert_offsets, "expert_offsets");
     REQUIRE(sorted_weight, "sorted_weight");
     REQUIRE16(o, "o");
-    LAUNCH(moe::launch_down_grouped(dims_of(shape), h, dn_blocks, dn_scales, dn_bias, expert_offsets,
+    LAUNCH(moe::launch_down_grouped(dims_of(shape), h8, dn_blocks, dn_scales, dn_bias, expert_offsets,
                                     sorted_weight, o, static_cast<hipStream_t>(stream)), "down");
     return ok();
 }

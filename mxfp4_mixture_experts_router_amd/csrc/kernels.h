@@ -39,12 +39,15 @@ hipError_t launch_permute(const Dims &d, const int32_t *topk_idx, const float *t
                           int32_t *offsets, int32_t *sorted_token, float *sorted_w,
                           int32_t *slot_row, hipStream_t s);
 
-hipError_t launch_up_grouped(const Dims &d, const uint16_t *x, const uint8_t *gu_blocks,
+// up (prefill): h[r] = swiglu(x[sorted_token[r]] . Wgu[e]^T + bgu[e]) for the sorted rows r of
+// every expert e, from the mx8 matrix x8 (T rows of H) into the mx8 matrix h8 (T k rows of I).
+hipError_t launch_up_grouped(const Dims &d, const uint8_t *x8, const uint8_t *gu_blocks,
                              const uint8_t *gu_scales, const uint16_t *gu_bias,
                              const int32_t *offsets, const int32_t *sorted_token,
-                             uint16_t *h, hipStream_t s);
+                             uint8_t *h8, hipStream_t s);
 
-hipError_t launch_down_grouped(const Dims &d, const uint16_t *h, const uint8_t *dn_blocks,
+// down (prefill): o[r] = sorted_w[r] * (h[r] . Wdn[e]^T + bdn[e]) (fp32 [T k, H]) from h8.
+hipError_t launch_down_grouped(const Dims &d, const uint8_t *h8, const uint8_t *dn_blocks,
                                const uint8_t *dn_scales, const uint16_t *dn_bias,
                                const int32_t *offsets, const float *sorted_w, float *o,
                                hipStream_t s);
@@ -73,6 +76,9 @@ hipError_t launch_down_decode(const Dims &d, const uint8_t *h8, const uint8_t *d
                               float *topk_w, float *part, uint16_t *y, hipStream_t s);
 // y[t, :] = bf16(sum_{j < k} part[t*k + j, :]), slot order.
 hipError_t launch_combine_decode(const Dims &d, const float *part, uint16_t *y, hipStream_t s);
+
+// bf16 [rows, cols] -> mx8 matrix (mx_mfma.h).
+hipError_t launch_quantize(const uint16_t *x, int64_t rows, int cols, uint8_t *q8, hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t *blocks, const uint8_t *scales, int64_t rows, int cols,
                           uint16_t *out, hipStream_t s);

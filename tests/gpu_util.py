@@ -58,6 +58,31 @@ def host_permutation(idx: np.ndarray, E: int):
     return offsets, sorted_token, order, slot_row.astype(np.int32)
 
 
+def _e4m3_table() -> np.ndarray:
+    """Values of the 256 OCP E4M3 codes (0x7f / 0xff: NaN)."""
+    t = np.empty(256, dtype=np.float64)
+    for b in range(256):
+        s, e, m = b >> 7, (b >> 3) & 15, b & 7
+        mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        t[b] = np.nan if (b & 0x7F) == 0x7F else (-mag if s else mag)
+    return t
+
+
+E4M3 = _e4m3_table()
+
+
+def decode_mx8(q8, R: int, K: int) -> np.ndarray:
+    """Values [R, K] of an mx8 activation matrix (layout in moe_mxfp4.h): per 32-element
+    block, hi * 2^(s_hi - 127) + lo * 2^(s_lo - 127)."""
+    q = np.asarray(q8.cpu().numpy() if hasattr(q8, "cpu") else q8, dtype=np.uint8)
+    S = ((K // 32) + 15) // 16 * 16
+    data = q[: 2 * R * K].reshape(2 * R, K)
+    sc = q[2 * R * K: 2 * R * K + 2 * R * S].reshape(2 * R, S)[:, : K // 32].astype(np.int64)
+    mult = np.ldexp(1.0, np.repeat(sc, 32, axis=1) - 127)
+    v = E4M3[data] * mult
+    return v[0::2] + v[1::2]
+
+
 def gamma(n: int) -> float:
     return n * U64 / (1 - n * U64)
 

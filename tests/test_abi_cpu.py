@@ -29,7 +29,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_mxfp4_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_mxfp4_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_function(lib):
@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert moe.abi_version() == 1
-    assert "#define MOE_MXFP4_ABI_VERSION 1" in open(HEADER).read()
+    assert moe.abi_version() == 2
+    assert "#define MOE_MXFP4_ABI_VERSION 2" in open(HEADER).read()
 
 
 def shape(T=1, H=2880, I=2880, E=32, k=4, alpha=1.702, limit=7.0):
@@ -78,9 +78,9 @@ def test_workspace_sizes(lib, T, H, I, E, k):
     n = moe.workspace_bytes(T, H, I, E, k)
     N = T * k
     if moe.uses_decode_path(T, H, I):
-        assert n >= N * I * 2 + 2 * N * 4
+        assert n >= 4 * N * I + 2 * T * H + 2 * N * 4        # mx8 h (half-block rows) and x
     else:
-        assert n >= N * (I * 2 + H * 4) + 3 * N * 4
+        assert n >= N * (2 * I + H * 4) + 2 * T * H + 3 * N * 4   # mx8 h and x, fp32 o
     assert n % 256 == 0
 
 
@@ -139,6 +139,18 @@ def test_stage_entry_points_validate(lib):
     assert lib.moe_mxfp4_combine(ctypes.byref(s), A, A, None, None) == EINVAL
     bad = shape(E=300)
     assert lib.moe_mxfp4_permute(ctypes.byref(bad), A, A, A, A, A, A, None) == ESHAPE
+
+
+def test_mx8_format_entry_points(lib):
+    # 2R (K + roundup16(K/32)) bytes; validation only (no device work)
+    assert lib.moe_mxfp4_mx8_bytes(3, 2880) == 2 * 3 * (2880 + 96)
+    assert lib.moe_mxfp4_mx8_bytes(1, 32) == 2 * (32 + 16)
+    assert lib.moe_mxfp4_mx8_bytes(0, 64) == 0
+    assert lib.moe_mxfp4_quantize_act(A, 4, 48, A, None) == ESHAPE
+    assert lib.moe_mxfp4_quantize_act(A, -1, 64, A, None) == EINVAL
+    assert lib.moe_mxfp4_quantize_act(A, 4, 64, None, None) == EINVAL
+    assert lib.moe_mxfp4_quantize_act(A + 2, 4, 64, A, None) == EALIGN
+    assert lib.moe_mxfp4_quantize_act(None, 0, 64, None, None) == 0
 
 
 def test_dequant_validates(lib):

@@ -17,8 +17,8 @@ import mxfp4_mixture_experts_router_amd as moe
 import oracle
 from workloads import CONFIGS, make_inputs, f32_from_bf16_bits, bf16_bits_from_f32
 
-from gpu_util import (assert_close_rows, bf16_bits, bf16_to_f64, check_selection, host_permutation,
-                      to_dev, upload)
+from gpu_util import (assert_close_rows, bf16_bits, bf16_to_f64, check_selection, decode_mx8,
+                      host_permutation, to_dev, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -181,23 +181,45 @@ def test_expert_up_and_down_grouped(name, T, H, I, E, k):
     inp, tokens, ref, idx, w = _grouped_case(cfg, T, seed=7, n_sample=24)
     offsets, sorted_token, order, slot_row = host_permutation(idx, E)
     d = upload(inp)
-    h = moe.expert_up(d["x"], d["gu_blocks"], d["gu_scales"], d["gu_bias"], to_dev(offsets),
-                      to_dev(sorted_token), k, cfg.alpha, cfg.limit)
+    x8 = moe.quantize_act(d["x"])
+    h8 = moe.expert_up(x8, T, d["gu_blocks"], d["gu_scales"], d["gu_bias"], to_dev(offsets),
+                       to_dev(sorted_token), k, cfg.alpha, cfg.limit)
     rows = slot_row.reshape(T, k)[tokens]                      # [n, k] sorted rows of the sample
-    h_np = bf16_to_f64(h)
+    h_np = decode_mx8(h8, T * k, I)
     assert_close_rows(h_np[rows.reshape(-1)], ref["h"].reshape(-1, I), "h")
-    # down: feed the oracle's h (rounded to bf16) so this step is checked on its own
+    # down: feed the oracle's h (rounded to bf16, then to mx8 on the GPU) so this step is
+    # checked on its own
     h_in = np.zeros((T * k, I), dtype=np.uint16)
     h_in[rows.reshape(-1)] = bf16_bits_from_f32(ref["h"].reshape(-1, I).astype(np.float32))
     sorted_w = w.reshape(-1)[order].astype(np.float32)
-    o = moe.expert_down(to_dev(h_in), d["dn_blocks"], d["dn_scales"], d["dn_bias"], to_dev(offsets),
-                        to_dev(sorted_w), k)
+    o = moe.expert_down(moe.quantize_act(to_dev(h_in)), T, d["dn_blocks"], d["dn_scales"], d["dn_bias"],
+                        to_dev(offsets), to_dev(sorted_w), k)
     o_np = o.cpu().numpy().astype(np.float64)[rows.reshape(-1)]
     want = (ref["o"] * ref["w"][:, :, None]).reshape(-1, H)
     assert_close_rows(o_np, want, "o")
     # combine of the GPU's o: the sampled tokens' y against the oracle
     y = bf16_to_f64(moe.combine(o, to_dev(slot_row), k))
     assert_close_rows(y[tokens], ref["y"], "y from combine")
+
+
+@pytest.mark.parametrize("R,K", [(1, 32), (37, 96), (300, 2880)])
+def test_quantize_act_is_exact_for_bf16(R, K):
+    """hi + lo reproduces every bf16 value whose block's largest magnitude is within 2^13 of
+    it; the rest (far below the block maximum) keep their error under 2^-21 of that maximum."""
+    rng = np.random.default_rng(R * 1000 + K)
+    x = (rng.standard_normal((R, K // 32, 32)) * np.exp2(rng.integers(-20, 20, size=(R, K // 32, 1)))).reshape(R, K)
+    x[0, :32] = 0.0                                            # an all-zero block
+    if K >= 64:
+        x[0, 32:64] *= np.exp2(rng.integers(-24, 1, size=32))  # a wide dynamic range
+    bits = bf16_bits_from_f32(x.astype(np.float32))
+    xv = f32_from_bf16_bits(bits).astype(np.float64)
+    q8 = moe.quantize_act(to_dev(bits))
+    got = decode_mx8(q8, R, K)
+    bmax = np.abs(xv.reshape(R, K // 32, 32)).max(axis=2, keepdims=True)
+    bmax = np.repeat(bmax, 32, axis=2).reshape(R, K)
+    near = np.abs(xv) >= bmax * 2.0 ** -13
+    assert np.array_equal(got[near], xv[near])
+    assert np.all(np.abs(got - xv) <= bmax * 2.0 ** -21)
 
 
 # ----------------------------------------------------------------------------- whole layer
