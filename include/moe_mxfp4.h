@@ -59,8 +59,11 @@ typedef enum {
     MOE_OK = 0,
     MOE_EINVAL = 1,      /* NULL pointer where one is required, T < 0, non-finite alpha/limit */
     MOE_ESHAPE = 2,      /* H or I not a positive multiple of 32, k < 1, k > E, k > 8, E > 256,
-                            E < 1, sizes too large for 32-bit row indexing */
-    MOE_EALIGN = 3,      /* a tensor pointer not 16-byte aligned (scale pointers: any alignment) */
+                            E < 1, T > 2^24, or the T k activation rows as an mx8 matrix
+                            (moe_mxfp4_mx8_bytes(T k, max(H, I))) or one expert's packed
+                            gate_up weights reaching 4 GiB (32-bit operand offsets) */
+    MOE_EALIGN = 3,      /* a tensor pointer not 16-byte aligned; the two expert scale
+                            pointers need 4-byte alignment; biases, router bias: any */
     MOE_EWORKSPACE = 4,  /* workspace NULL or smaller than moe_mxfp4_workspace_bytes() */
     MOE_EHIP = 5         /* a HIP launch failed */
 } moe_status_t;

@@ -47,6 +47,15 @@ moe_status_t check_shape(const moe_mxfp4_shape_t *s, bool need_experts) {
     if (s->T > (static_cast<int64_t>(1) << 24))
         return fail(MOE_ESHAPE, "T = %lld exceeds the supported 2^24 tokens per call",
                     static_cast<long long>(s->T));
+    if (need_experts) {
+        // the grouped GEMMs address their operands with 32-bit offsets
+        const int K = s->H > s->I ? s->H : s->I;
+        const uint64_t act = moe::mx8_bytes(s->T * s->k, K);
+        const uint64_t wgt = static_cast<uint64_t>(2 * s->I) * (s->H / 2);
+        if (act >= (static_cast<uint64_t>(1) << 32) || wgt >= (static_cast<uint64_t>(1) << 32))
+            return fail(MOE_ESHAPE, "T * k = %lld rows of %d (or one expert's weights) exceed 4 GiB; split the batch",
+                        static_cast<long long>(s->T * s->k), K);
+    }
     if (need_experts && (!std::isfinite(s->swiglu_alpha) || !std::isfinite(s->swiglu_limit)))
         return fail(MOE_EINVAL, "swiglu_alpha / swiglu_limit must be finite");
     return MOE_OK;
@@ -107,6 +116,12 @@ moe_status_t hip_status(hipError_t e, const char *what) {
         if (!(ptr)) return fail(MOE_EINVAL, "%s is NULL", name);                      \
         if (!aligned16(ptr)) return fail(MOE_EALIGN, "%s is not 16-byte aligned", name); \
     } while (0)
+#define REQUIRE4(ptr, name)                                                           \
+    do {                                                                              \
+        if (!(ptr)) return fail(MOE_EINVAL, "%s is NULL", name);                      \
+        if (reinterpret_cast<uintptr_t>(ptr) & 3u)                                     \
+            return fail(MOE_EALIGN, "%s is not 4-byte aligned", name);                \
+    } while (0)
 #define LAUNCH(call, what)                                                            \
     do {                                                                              \
         moe_status_t st_ = hip_status((call), what);                                  \
@@ -161,10 +176,10 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
     REQUIRE16(router_w, "router_w");
     REQUIRE(router_b, "router_b");
     REQUIRE16(gu_blocks, "gu_blocks");
-    REQUIRE(gu_scales, "gu_scales");
+    REQUIRE4(gu_scales, "gu_scales");
     REQUIRE(gu_bias, "gu_bias");
     REQUIRE16(dn_blocks, "dn_blocks");
-    REQUIRE(dn_scales, "dn_scales");
+    REQUIRE4(dn_scales, "dn_scales");
     REQUIRE(dn_bias, "dn_bias");
     REQUIRE16(y, "y");
     const Layout L = layout_of(shape);
@@ -312,7 +327,7 @@ MOE_EXPORT moe_status_t moe_mxfp4_expert_up(const moe_mxfp4_shape_t *shape, cons
     if (shape->T == 0) return ok();
     REQUIRE16(x8, "x8");
     REQUIRE16(gu_blocks, "gu_blocks");
-    REQUIRE(gu_scales, "gu_scales");
+    REQUIRE4(gu_scales, "gu_scales");
     REQUIRE(gu_bias, "gu_bias");
     REQUIRE(expert_offsets, "expert_offsets");
     REQUIRE(sorted_token, "sorted_token");
@@ -331,7 +346,7 @@ MOE_EXPORT moe_status_t moe_mxfp4_expert_down(const moe_mxfp4_shape_t *shape, co
     if (shape->T == 0) return ok();
     REQUIRE16(h8, "h8");
     REQUIRE16(dn_blocks, "dn_blocks");
-    REQUIRE(dn_scales, "dn_scales");
+    REQUIRE4(dn_scales, "dn_scales");
     REQUIRE(dn_bias, "dn_bias");
     REQUIRE(expert_offsets, "expert_offsets");
     REQUIRE(sorted_weight, "sorted_weight");

@@ -15,26 +15,76 @@
 // mg % 8 == XCD, walking all n-tiles of one m-tile before the next, so an m-tile's
 // activations are fetched into one XCD's L2 and reused across its n-tiles.
 //
-// Block tile: BM = 128 activation rows (256 A rows: hi, lo) x BN = 192 output columns, BK =
-// 128 (one MFMA step) per LDS stage, two LDS stages (the next stage's global loads are in
-// flight while the current one is multiplied). 8 wavefronts stacked along M; each owns 32 A
-// rows x 192 columns = 2 x 12 MFMA tiles (96 accumulator registers; 192 columns = 96 gate/up
-// pairs = 3 whole MX blocks of h). Within a stage lane group g takes scale block g.
+// Block tile: BM = 128 activation rows (256 A rows: hi, lo) x BN = 256 output columns; the
+// contraction advances BK = 128 (one MFMA step = four scale blocks) per stage. Eight
+// wavefronts, two per SIMD, in a 4 x 2 arrangement: wavefront (wm, wn) owns A rows
+// 64 wm .. 64 wm + 63 and columns 128 wn .. 128 wn + 127, i.e. 4 x 8 MFMA tiles (128
+// accumulators). Operands go from global memory straight into LDS (global_load_lds: each
+// lane's 16 or 4 bytes land at the instruction's LDS base + lane * size) into a ring of
+// three stage buffers; a stage's loads are issued two stages before it is multiplied, and
+// one barrier per stage both publishes the stage and retires the buffer the next issue
+// overwrites. The loads are issued from inline assembly: the compiler then neither knows of
+// them nor inserts its own (all-draining) waits before LDS reads; the kernel waits for
+// exactly the stage it needs with vmcnt and publishes it with a barrier.
+//
+// Stage buffer layout (bytes):
+//   A   [256 rows][128]: row R = 2 * (tile row) + part; its eight 16-byte chunks c are stored
+//       at slot c ^ (R & 7) (conflict-free operand reads).
+//   B   [256 rows][64]: the stage's four packed MXFP4 blocks of weight row n, block c at
+//       slot c ^ ((n >> 1) & 3).
+//   AS  [256 rows] 4 bytes: the E8M0 scales of the stage's four blocks of A row R.
+//   BS  [256 rows] 8 bytes: the 4-byte-aligned 8 bytes of the weight scale row holding the
+//       stage's four scale bytes (weight scale rows are K / 32 bytes long, not 4-aligned).
 #include "device_common.h"
 #include "kernels.h"
 #include "mx_mfma.h"
 
+
 namespace moe {
 namespace {
 
-constexpr int kBM = 128;                 // activation rows per tile (2 A rows each)
-constexpr int kBN = 192;                 // output columns (weight rows) per tile
-constexpr int kBK = 128;                 // contraction per stage (4 scale blocks)
-constexpr int kAStride = kBK + 16;       // bytes per LDS A row (padded)
-constexpr int kBStride = kBK / 2 + 16;   // bytes per LDS packed weight row (padded)
+constexpr int kBM = 128;                       // activation rows per tile
+constexpr int kAR = 2 * kBM;                   // A rows per tile (hi, lo)
+constexpr int kBN = 256;                       // output columns (weight rows) per tile
+constexpr int kBK = 128;                       // contraction per stage
+constexpr int kThreads = 512;
+constexpr int kOffB = kAR * kBK;               // 32768
+constexpr int kOffAS = kOffB + kBN * kBK / 2;  // 49152
+constexpr int kOffBS = kOffAS + kAR * 4;       // 50176
+constexpr int kStage = kOffBS + kBN * 8;       // 52224
+constexpr int kOps = 8;                        // global_load_lds per wavefront per stage
+constexpr int kHS = 65;                        // up epilogue: padded row of 64 fp32 pairs
+
+__shared__ __attribute__((aligned(16))) uint8_t g_stages[3 * kStage];
+
+// global_load_lds (saddr form): lane l's 16 (or 4) bytes at base + voff land at LDS byte
+// address lds + 16 l (4 l). base and lds are wavefront-uniform. M0 is set in the same
+// statement; nothing else in these kernels keeps a value in M0.
+__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t *base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (N <= 63), other counters untouched; the empty asm statements keep the
+// compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void barrier_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 template <bool UP>
-__global__ __launch_bounds__(512) void k_gemm_mx(
+__global__ __launch_bounds__(kThreads) void k_gemm_mx(
     const uint8_t *__restrict__ a8, int64_t a_rows,  // mx8 activations: up x8 (T rows), down h8 (T k rows)
     const int32_t *__restrict__ sorted_token,        // up only
     const float *__restrict__ sorted_w,              // down only
@@ -45,17 +95,12 @@ __global__ __launch_bounds__(512) void k_gemm_mx(
     float *__restrict__ o_out) {                     // down
     __shared__ int s_off[kMaxE + 1];
     __shared__ int s_mcum[kMaxE + 1];
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][2 * kBM * kAStride];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][kBN * kBStride];
-    __shared__ __attribute__((aligned(16))) uint32_t sAS[2][2 * kBM];   // 4 E8M0 bytes per A row
-    __shared__ __attribute__((aligned(16))) uint32_t sBS[2][kBN];
 
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int col = lane & 15, g = lane >> 4;
-
-    for (int e = tid; e <= E; e += 512) s_off[e] = offsets[e];
+    const int tid0 = threadIdx.x;
+    for (int e = tid0; e <= E; e += kThreads) s_off[e] = offsets[e];
     __syncthreads();
-    if (wave == 0) {
+    if (tid0 < kWave) {
+        const int lane = tid0;
         // m-tile prefix over experts (E <= 256: four per lane)
         int v[4], local = 0;
 #pragma unroll
@@ -85,6 +130,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(
     const int mtiles = s_mcum[E];
     const int nkb = K / 32;                      // scale blocks per row
     const int kt_total = (nkb + 3) / 4;
+    const int kt_last = kt_total - 1;
     const int kbytes = K / 2;
     const int ass = mx8_scale_stride(K);
     const uint8_t *a_sc = a8 + static_cast<size_t>(2 * a_rows) * K;
@@ -94,7 +140,7 @@ __global__ __launch_bounds__(512) void k_gemm_mx(
     const int my_tiles = my_m * ntn;
 
     for (int it = lb; it < my_tiles; it += nb) {
-        const int mg = xcd + 8 * (it / ntn), nt = it % ntn;
+        const int mg = xcd + 8 * (it / ntn), nt_tile = it % ntn;
         int lo = 0, hi = E - 1;                       // last e with s_mcum[e] <= mg
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -103,163 +149,197 @@ __global__ __launch_bounds__(512) void k_gemm_mx(
         const int e = lo;
         const int row0 = s_off[e] + (mg - s_mcum[e]) * kBM;
         const int rows = min(kBM, s_off[e + 1] - row0);
-        const int n0 = nt * kBN;
+        const int n0 = nt_tile * kBN;
 
-        // this thread's staged pieces: A rows (tid + 512 i) / 8, 16-byte piece tid % 8;
-        // B rows (tid + 512 i) / 4 (i = 1 only for tid < 256), piece tid % 4; scales of A row
-        // tid (< 256) and B row tid (< 192).
-        int arow[4];      // A byte row (2 src + part) of the staged pieces, -1 past the tile
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (tid + 512 * i) >> 3;       // A row: activation row r / 2, part r % 2
-            arow[i] = -1;
-            if ((r >> 1) < rows) arow[i] = 2 * (UP ? sorted_token[row0 + (r >> 1)] : row0 + (r >> 1)) + (r & 1);
-        }
-        int ascr = -1;    // A scale row of thread tid < 256
-        if (tid < 2 * kBM && (tid >> 1) < rows) ascr = 2 * (UP ? sorted_token[row0 + (tid >> 1)] : row0 + (tid >> 1)) + (tid & 1);
-        const uint8_t *wbase = wblocks + static_cast<int64_t>(e) * Nrows * kbytes;   // uniform
-        const uint8_t *sbase = wscales + static_cast<int64_t>(e) * Nrows * nkb;
-        int brow[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) brow[i] = min(n0 + ((tid + 512 * i) >> 2), Nrows - 1);
-        const int bscr = min(n0 + tid, Nrows - 1);
+        // Per-lane values are derived from an opaque copy of the thread index in every tile,
+        // so that the compiler recomputes them here instead of keeping them live (spilled)
+        // across the whole loop.
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+        const int m = lane & 15, g = lane >> 4;
+        const int wm = wave & 3, wn = wave >> 2;
 
-        // raw staged values; the scale bytes are assembled at stash time so that issuing a
-        // stage's loads never waits for them
-        uint4 ra[4], rb[2];
-        uint32_t rsa = 0x7f7f7f7fu, rsb[4] = {127u, 127u, 127u, 127u};
-        auto fetch = [&](int kt) {
-            const int pa = tid & 7;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kk = kt * kBK + 16 * pa;
-                ra[i] = (arow[i] >= 0 && kk < K)
-                            ? *reinterpret_cast<const uint4 *>(a8 + static_cast<int64_t>(arow[i]) * K + kk)
-                            : zero4();
-            }
-            const int pb = tid & 3;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int kb = 4 * kt + pb;
-                rb[i] = (kb < nkb && tid + 512 * i < 4 * kBN)
-                            ? *reinterpret_cast<const uint4 *>(wbase + static_cast<int64_t>(brow[i]) * kbytes + 16 * kb)
-                            : zero4();
-            }
-            // A scale rows are padded to 16 bytes: the 4 bytes of this stage are in bounds
-            if (ascr >= 0) rsa = *reinterpret_cast<const uint32_t *>(a_sc + static_cast<int64_t>(ascr) * ass + 4 * kt);
-            if (tid < kBN) {
-                const uint8_t *bs = sbase + static_cast<int64_t>(bscr) * nkb;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) rsb[q] = 4 * kt + q < nkb ? bs[4 * kt + q] : 127u;
-            }
+        // --- loads. Global addresses are a uniform base plus a 32-bit per-lane offset (the
+        // host keeps every operand below 4 GiB). A chunk or block past K (last stage only)
+        // loads chunk / block 0 instead: finite data whose contribution the multiply zeroes.
+        const int a_c = (lane & 7) ^ ((lane >> 3) & 7);
+        const int b_c = (lane & 3) ^ ((lane >> 3) & 3);
+        const int a_vc = (K - kBK * kt_last) / 16;   // valid chunks in the last stage (2..8)
+        const int b_vb = nkb - 4 * kt_last;          // valid blocks in the last stage (1..4)
+        const uint32_t a_ch = 16 * a_c, a_ch_last = a_c < a_vc ? 16 * a_c : 0;
+        const uint32_t b_ch = 16 * b_c, b_ch_last = b_c < b_vb ? 16 * b_c : 0;
+        // source byte row of tile A row R (activation row R / 2, part R % 2); rows past the
+        // tile read the tile's first row (finite data, results never stored)
+        auto a_src = [&](int R) -> uint32_t {
+            const int ar = (R >> 1) < rows ? (R >> 1) : 0;
+            const int src = UP ? sorted_token[row0 + ar] : row0 + ar;
+            return static_cast<uint32_t>(2 * src + (R & 1));
         };
-        auto stash = [&](int buf, int kt) {
+        // A: instruction i of wavefront w fills A rows 32 w + 8 i + lane / 8
+        uint32_t a_off[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int idx = tid + 512 * i;
-                *reinterpret_cast<uint4 *>(&sA[buf][(idx >> 3) * kAStride + (idx & 7) * 16]) = ra[i];
-            }
+        for (int i = 0; i < 4; ++i) a_off[i] = a_src(32 * wave + 8 * i + (lane >> 3)) * static_cast<uint32_t>(K);
+        // A scales: wavefront w fills rows 64 (w % 4) + lane (w and w + 4 load the same bytes)
+        const uint32_t as_off = a_src(64 * (wave & 3) + lane) * static_cast<uint32_t>(ass);
+        // B: instruction i fills weight rows 32 w + 16 i + lane / 4 (clamped to the matrix)
+        const uint8_t *wblk = wblocks + static_cast<int64_t>(e) * Nrows * kbytes;
+        uint32_t b_off[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int idx = tid + 512 * i;
-                if (idx < 4 * kBN) *reinterpret_cast<uint4 *>(&sB[buf][(idx >> 2) * kBStride + (idx & 3) * 16]) = rb[i];
-            }
-            if (tid < 2 * kBM) {
-                // bytes past the row's nkb blocks (never written) become 127 (their data is 0)
-                uint32_t v = ascr >= 0 ? rsa : 0x7f7f7f7fu;
+        for (int i = 0; i < 2; ++i) b_off[i] = min(n0 + 32 * wave + 16 * i + (lane >> 2), Nrows - 1) * kbytes;
+        // B scales, read as aligned dwords: the pair at (p & ~3) holds the stage's bytes
+        // p .. p + 3; a second dword past the tensor's end holds no valid byte and reads the
+        // last dword instead. Wavefront w fills rows 32 w + lane / 2, dword lane % 2.
+        const uint8_t *wsc = wscales + static_cast<int64_t>(e) * Nrows * nkb;
+        const int64_t sc_len = static_cast<int64_t>(E - e) * Nrows * nkb;   // to the tensor's end
+        const uint32_t last4 = static_cast<uint32_t>(min<int64_t>(sc_len, 0x7fffffff) - 4);
+        const uint32_t bs_off = (min(n0 + 32 * wave + (lane >> 1), Nrows - 1) * nkb & ~3) + 4 * (lane & 1);
+
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)g_stages;
+        auto issue = [&](int buf, int kt) {
+            const uint32_t ach = kt == kt_last ? a_ch_last : a_ch;
+            const uint32_t bch = kt == kt_last ? b_ch_last : b_ch;
+            const uint8_t *a_k = a8 + kBK * kt;          // uniform bases
+            const uint8_t *b_k = wblk + 64 * kt;
+            const uint32_t lb = lds0 + buf * kStage;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (4 * kt + q >= nkb) v = (v & ~(0xffu << (8 * q))) | (127u << (8 * q));
-                sAS[buf][tid] = v;
-            }
-            if (tid < kBN) sBS[buf][tid] = rsb[0] | (rsb[1] << 8) | (rsb[2] << 16) | (rsb[3] << 24);
+            for (int i = 0; i < 4; ++i) dma16(a_k, a_off[i] + ach, lb + (4 * wave + i) * 1024);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) dma16(b_k, b_off[i] + bch, lb + kOffB + (2 * wave + i) * 1024);
+            dma4(a_sc + 4 * kt, as_off, lb + kOffAS + 256 * (wave & 3));
+            dma4(wsc, min(bs_off + 4 * kt, last4), lb + kOffBS + 256 * wave);
         };
 
-        f32x4 acc[2][12];
+        // --- multiply. Byte of the 8-byte scale window holding this lane's scale (block g)
+        // of each of its eight B columns.
+        int sbyte[8];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 12; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < 8; ++nt) sbyte[nt] = ((min(n0 + 128 * wn + 16 * nt + m, Nrows - 1) * nkb) & 3) + g;
 
-        __syncthreads();   // the previous tile's last stage is no longer read
-        fetch(0);
-        stash(0, 0);
-        __syncthreads();
+        f32x4 acc[4][8];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // B fragments and scales of the wavefront's eight column tiles are read first and
+        // kept; A fragments are then streamed one row tile at a time (8 MFMAs each). Blocks
+        // past K (vb < 4: the last stage of a contraction whose block count is not a
+        // multiple of 4) get zero A data and unit scales, so they add exactly 0. LDS
+        // addresses are one per-lane base per operand plus constants.
+        const uint32_t lb_b = 8192 * wn + 64 * m + 16 * (g ^ ((m >> 1) & 3));
+        const uint32_t lb_bs = 1024 * wn + 8 * m;
+        const uint32_t lb_a = 8192 * wm + 128 * m + 16 * (g ^ (m & 7));
+        const uint32_t lb_as = 256 * wm + 4 * m;
+        auto compute = [&](const uint8_t *buf, int kt) {
+            const int vb = nkb - 4 * kt;
+            const bool ok_sc = g < vb;
+            const uint32_t m_lo = (g >> 1) < vb ? ~0u : 0u, m_hi = 2 + (g >> 1) < vb ? ~0u : 0u;
+            const uint32_t ob = lb_b, obs = lb_bs, oa = lb_a, oas = lb_as;
+            const uint8_t *pb = buf + kOffB + ob;
+            const uint8_t *pbs = buf + kOffBS + obs;
+            const uint8_t *pa = buf + oa;
+            const uint8_t *pa2 = buf + (oa ^ 64u);          // chunk g + 4: slot s0 ^ 4
+            const uint8_t *pas = buf + kOffAS + oas;
+            i32x8 bop[8];
+            uint32_t sb[8];
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                bop[nt] = mx_b_operand(*reinterpret_cast<const uint4 *>(pb + 1024 * nt));
+                const uint2 sv = *reinterpret_cast<const uint2 *>(pbs + 128 * nt);
+                const uint32_t word = sbyte[nt] < 4 ? sv.x : sv.y;
+                const uint32_t v = (word >> (8 * (sbyte[nt] & 3))) & 0xffu;
+                sb[nt] = ok_sc ? v : 127u;
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                uint4 lo16 = *reinterpret_cast<const uint4 *>(pa + 2048 * mt);
+                uint4 hi16 = *reinterpret_cast<const uint4 *>(pa2 + 2048 * mt);
+                const uint32_t v = (*reinterpret_cast<const uint32_t *>(pas + 64 * mt) >> (8 * g)) & 0xffu;
+                lo16.x &= m_lo; lo16.y &= m_lo; lo16.z &= m_lo; lo16.w &= m_lo;
+                hi16.x &= m_hi; hi16.y &= m_hi; hi16.z &= m_hi; hi16.w &= m_hi;
+                const i32x8 af = mx_a_operand(lo16, hi16);
+                const uint32_t sa = ok_sc ? v : 127u;
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = mfma_mx(af, bop[nt], acc[mt][nt], sa, sb[nt]);
+            }
+        };
+
+        // stage kt (buffer kt % 3): wait for its loads (stage kt + 1's stay in flight),
+        // publish it to all wavefronts, refill the buffer stage kt - 1 used with stage
+        // kt + 2, multiply.
+        __syncthreads();   // the previous tile's epilogue is done with LDS
+        issue(0, 0);
+        if (kt_total > 1) issue(1, 1);
+        int buf = 0;
         for (int kt = 0; kt < kt_total; ++kt) {
-            const int buf = kt & 1;
-            if (kt + 1 < kt_total) fetch(kt + 1);
-            // A fragments of this wave's 2 m-tiles, B fragments of its 12 n-tiles
-            i32x8 af[2];
-            uint32_t sa[2];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int ar = wave * 32 + 16 * mt + col;
-                const uint8_t *p = &sA[buf][ar * kAStride];
-                af[mt] = mx_a_operand(*reinterpret_cast<const uint4 *>(p + 16 * g),
-                                      *reinterpret_cast<const uint4 *>(p + 64 + 16 * g));
-                sa[mt] = (sAS[buf][ar] >> (8 * g)) & 0xffu;
-            }
-#pragma unroll
-            for (int nt2 = 0; nt2 < 12; ++nt2) {
-                const int br = 16 * nt2 + col;
-                const i32x8 bop = mx_b_operand(*reinterpret_cast<const uint4 *>(&sB[buf][br * kBStride + 16 * g]));
-                const uint32_t sb = (sBS[buf][br] >> (8 * g)) & 0xffu;
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) acc[mt][nt2] = mfma_mx(af[mt], bop, acc[mt][nt2], sa[mt], sb);
-            }
-            if (kt + 1 < kt_total) stash(buf ^ 1, kt + 1);
-            __syncthreads();
+            if (kt + 1 < kt_total) wait_vm<kOps>(); else wait_vm<0>();
+            barrier_only();
+            const int buf2 = buf == 0 ? 2 : buf - 1;     // (kt + 2) % 3
+            if (kt + 2 < kt_total) issue(buf2, kt + 2);
+            compute(g_stages + buf * kStage, kt);
+            buf = buf == 2 ? 0 : buf + 1;
         }
+        __syncthreads();   // every wavefront is done with the stage buffers
 
-        // epilogue. D rows 16 mt + 4g + r of the wave's A rows: activation row
-        // 16 wave + 8 mt + 2g + r/2 (part r % 2) -> value = D[.., 2j] + D[.., 2j + 1].
+        // --- epilogue. Lane (m, g) of MFMA tile (mt, nt) holds column 16 nt + m of A rows
+        // 16 mt + 4g + r: activation row 8 mt + 2g (r = 0, 1: hi, lo) and 8 mt + 2g + 1
+        // (r = 2, 3) of the wavefront's 32; value = D[hi] + D[lo].
         if (UP) {
-            // h of the tile's 128 rows x 96 pairs (fp32) into LDS,
-            // then one thread per (row, MX block of 32 pairs) quantizes it into h8
-            constexpr int kHS = kBN / 2 + 1;                   // padded row of pairs
-            float *s_h = reinterpret_cast<float *>(&sA[0][0]);
-            __syncthreads();
+            // h of the wavefront's 32 rows x 64 pairs (fp32) into LDS (wavefront (wm, wn) at
+            // stage buffer wn, offset wm), then each lane quantizes one (row, MX block) item
+            float *s_h = reinterpret_cast<float *>(g_stages + wn * kStage) + wm * (32 * kHS);
 #pragma unroll
-            for (int nt2 = 0; nt2 < 12; ++nt2) {
-                const int wr = n0 + 16 * nt2 + col;
+            for (int nt = 0; nt < 8; ++nt) {
+                const int wr = n0 + 128 * wn + 16 * nt + m;
                 const float bias = wr < Nrows ? bf16_to_f32(wbias[static_cast<int64_t>(e) * Nrows + wr]) : 0.f;
+                const int pair = 8 * nt + (m >> 1);
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int lr = wave * 16 + 8 * mt + 2 * g + j;
-                        const float v = acc[mt][nt2][2 * j] + acc[mt][nt2][2 * j + 1] + bias;
-                        const float other = __shfl_xor(v, 1);
-                        if ((col & 1) == 0) s_h[lr * kHS + 8 * nt2 + col / 2] = swiglu(v, other, alpha, limit);
-                    }
+                for (int mt = 0; mt < 4; ++mt) {
+                    const float v0 = acc[mt][nt][0] + acc[mt][nt][1] + bias;
+                    const float v1 = acc[mt][nt][2] + acc[mt][nt][3] + bias;
+                    // even lane (gate column) keeps row 8mt + 2g, odd lane (up) row 8mt + 2g + 1
+                    const float other = __shfl_xor((m & 1) ? v0 : v1, 1);
+                    const float gate = (m & 1) ? other : v0;
+                    const float up = (m & 1) ? v1 : other;
+                    s_h[(8 * mt + 2 * g + (m & 1)) * kHS + pair] = swiglu(gate, up, alpha, limit);
+                }
             }
             __syncthreads();
             const int Iw = Nrows / 2;
             const int is8 = mx8_scale_stride(Iw);
             uint8_t *h_sc = h8 + static_cast<size_t>(2 * h_rows) * Iw;
-            for (int item = tid; item < kBM * (kBN / 64); item += 512) {
-                const int r = item / (kBN / 64), q = item % (kBN / 64);
-                const int ib = n0 / 64 + q;                       // MX block of i
-                if (r >= rows || 64 * ib >= Nrows) continue;
+            const int r = lane >> 1, blk = lane & 1;
+            const int R = 32 * wm + r;                        // tile activation row
+            const int ib = (n0 + 128 * wn) / 64 + blk;        // MX block of h
+            if (R < rows && 64 * ib < Nrows) {
                 float v[32];
 #pragma unroll
-                for (int i = 0; i < 32; ++i) v[i] = s_h[r * kHS + 32 * q + i];
-                store_mx8_block(v, h8, h_sc, static_cast<int64_t>(row0 + r), Iw, is8, ib);
+                for (int i = 0; i < 32; ++i) v[i] = s_h[r * kHS + 32 * blk + i];
+                store_mx8_block(v, h8, h_sc, static_cast<int64_t>(row0 + R), Iw, is8, ib);
             }
         } else {
+            float wrow[4][2];
 #pragma unroll
-            for (int nt2 = 0; nt2 < 12; ++nt2) {
-                const int d = n0 + 16 * nt2 + col;
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int lr = 32 * wm + 8 * mt + 2 * g + j;
+                    wrow[mt][j] = lr < rows ? sorted_w[row0 + lr] : 0.f;
+                }
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const int d = n0 + 128 * wn + 16 * nt + m;
                 if (d >= Nrows) continue;
                 const float bd = bf16_to_f32(wbias[static_cast<int64_t>(e) * Nrows + d]);
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
+                for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        const int lr = wave * 16 + 8 * mt + 2 * g + j;
+                        const int lr = 32 * wm + 8 * mt + 2 * g + j;
                         if (lr >= rows) continue;
-                        const float v = acc[mt][nt2][2 * j] + acc[mt][nt2][2 * j + 1];
-                        o_out[static_cast<int64_t>(row0 + lr) * Nrows + d] = (v + bd) * sorted_w[row0 + lr];
+                        const float v = acc[mt][nt][2 * j] + acc[mt][nt][2 * j + 1];
+                        o_out[static_cast<int64_t>(row0 + lr) * Nrows + d] = (v + bd) * wrow[mt][j];
                     }
             }
         }
@@ -346,7 +426,7 @@ hipError_t launch_up_grouped(const Dims &d, const uint8_t *x8, const uint8_t *gu
                              const uint8_t *gu_scales, const uint16_t *gu_bias,
                              const int32_t *offsets, const int32_t *sorted_token,
                              uint8_t *h8, hipStream_t s) {
-    hipLaunchKernelGGL((k_gemm_mx<true>), dim3(persistent_blocks()), dim3(512), 0, s, x8, d.T, sorted_token,
+    hipLaunchKernelGGL((k_gemm_mx<true>), dim3(persistent_blocks()), dim3(kThreads), 0, s, x8, d.T, sorted_token,
                        nullptr, gu_blocks, gu_scales, gu_bias, offsets, d.E, d.H, 2 * d.I, d.alpha, d.limit,
                        h8, d.T * d.k, nullptr);
     return hipGetLastError();
@@ -356,7 +436,7 @@ hipError_t launch_down_grouped(const Dims &d, const uint8_t *h8, const uint8_t *
                                const uint8_t *dn_scales, const uint16_t *dn_bias,
                                const int32_t *offsets, const float *sorted_w, float *o,
                                hipStream_t s) {
-    hipLaunchKernelGGL((k_gemm_mx<false>), dim3(persistent_blocks()), dim3(512), 0, s, h8, d.T * d.k, nullptr,
+    hipLaunchKernelGGL((k_gemm_mx<false>), dim3(persistent_blocks()), dim3(kThreads), 0, s, h8, d.T * d.k, nullptr,
                        sorted_w, dn_blocks, dn_scales, dn_bias, offsets, d.E, d.I, d.H, d.alpha, d.limit,
                        nullptr, 0, o);
     return hipGetLastError();
