@@ -14,6 +14,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kBatch = 16;   // rounds of 64 pairs whose loads are issued together
+constexpr int kStageCap = 16384;   // pairs whose sorted rows fit the LDS staging area
 
 // Exclusive scan of cnt[0..E) by one wavefront (E <= 256: four entries per lane).
 __device__ void wave_exclusive_scan(const int *cnt, int *out, int E, int lane) {
@@ -41,61 +43,116 @@ __device__ void wave_exclusive_scan(const int *cnt, int *out, int E, int lane) {
     if (lane == kWave - 1) out[E] = incl;   // total
 }
 
+// Lanes of the wavefront whose expert equals this lane's (E <= 256: eight bit ballots).
+__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool valid) {
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    return peers;
+}
+
+// Wavefront w owns the contiguous pairs [w * per, (w + 1) * per) and walks them 64 at a
+// time twice: first counting its pairs per expert, then, after the block has turned the
+// counts into each wavefront's starting position per expert, scattering them. Within a
+// round the pairs of one expert are ranked by lane (ballot match), so the order is by pair
+// index throughout.
 __global__ __launch_bounds__(kThreads) void k_permute(
     const int32_t *__restrict__ topk_idx, const float *__restrict__ topk_w, int32_t N, int E,
     int k, int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_token,
     float *__restrict__ sorted_w, int32_t *__restrict__ slot_row) {
+    __shared__ int wcnt[kWaves][kMaxE];   // per-wavefront counts, then starting positions
+    __shared__ int32_t st_tok[kStageCap];  // sorted rows staged in LDS (N <= kStageCap), so that
+    __shared__ float st_w[kStageCap];      // the scattered writes stay on chip
     __shared__ int cnt[kMaxE];
     __shared__ int cursor[kMaxE + 1];
-    __shared__ int wcnt[kWaves][kMaxE];
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
+    const int per = ((N + kWaves - 1) / kWaves + kWave - 1) & ~(kWave - 1);
+    const bool staged = N <= kStageCap;
+    const int n_begin = wave * per;
+    const int n_end = min(N, n_begin + per);
 
-    for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
+    for (int e = lane; e < E; e += kWave) wcnt[wave][e] = 0;
+    __builtin_amdgcn_wave_barrier();
+    // the expert indices of up to kBatch rounds are loaded at once (their latency overlaps)
+    for (int nb = n_begin; nb < n_end; nb += kBatch * kWave) {
+        int eb[kBatch];
+#pragma unroll
+        for (int r = 0; r < kBatch; ++r) {
+            const int n = nb + r * kWave + lane;
+            eb[r] = n < n_end ? topk_idx[n] : -1;
+        }
+#pragma unroll
+        for (int r = 0; r < kBatch; ++r) {
+            const int e = eb[r];
+            const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+            const uint64_t peers = same_expert_lanes(e, valid);
+            if (valid && (peers & lanemask_lt()) == 0) wcnt[wave][e] += __popcll(peers);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
     __syncthreads();
-    for (int n = tid; n < N; n += kThreads) {
-        const int e = topk_idx[n];
-        if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&cnt[e], 1);
+    for (int e = tid; e < E; e += kThreads) {
+        int total = 0;
+        for (int w = 0; w < kWaves; ++w) total += wcnt[w][e];
+        cnt[e] = total;
     }
     __syncthreads();
     if (wave == 0) wave_exclusive_scan(cnt, cursor, E, lane);
     __syncthreads();
     for (int e = tid; e <= E; e += kThreads) offsets[e] = cursor[e];
-
-    for (int base = 0; base < N; base += kThreads) {
-        for (int i = tid; i < kWaves * kMaxE; i += kThreads) (&wcnt[0][0])[i] = 0;
-        const int n = base + tid;
-        const int e = n < N ? topk_idx[n] : -1;
-        const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
-        __syncthreads();
-        // group the wavefront's lanes by expert: peers = lanes holding the same expert
-        uint64_t peers = 0;
-        uint64_t rest = __ballot(valid);
-        while (rest) {
-            const int leader = __ffsll(static_cast<unsigned long long>(rest)) - 1;
-            const int le = __shfl(e, leader);
-            const uint64_t m = __ballot(valid && e == le);
-            if (valid && e == le) peers = m;
-            rest &= ~m;
+    for (int e = tid; e < E; e += kThreads) {
+        int run = cursor[e];
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = wcnt[w][e];
+            wcnt[w][e] = run;
+            run += c;
         }
-        const int rank = __popcll(peers & lanemask_lt());
-        if (valid && rank == 0) wcnt[wave][e] = __popcll(peers);
-        __syncthreads();
-        if (valid) {
-            int pos = cursor[e] + rank;
-            for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
-            sorted_token[pos] = n / k;
-            sorted_w[pos] = topk_w[n];
-            slot_row[n] = pos;
+    }
+    __syncthreads();
+    for (int nb = n_begin; nb < n_end; nb += kBatch * kWave) {
+        int eb[kBatch];
+        float wb[kBatch];
+#pragma unroll
+        for (int r = 0; r < kBatch; ++r) {
+            const int n = nb + r * kWave + lane;
+            eb[r] = n < n_end ? topk_idx[n] : -1;
+            wb[r] = n < n_end ? topk_w[n] : 0.f;
         }
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += kThreads) {
-            int add = 0;
-            for (int w = 0; w < kWaves; ++w) add += wcnt[w][ee];
-            cursor[ee] += add;
+#pragma unroll
+        for (int r = 0; r < kBatch; ++r) {
+            const int n = nb + r * kWave + lane;
+            const int e = eb[r];
+            const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+            const uint64_t peers = same_expert_lanes(e, valid);
+            const int base = valid ? wcnt[wave][e] : 0;
+            __builtin_amdgcn_wave_barrier();
+            if (valid) {
+                const int pos = base + __popcll(peers & lanemask_lt());
+                if (staged) {
+                    st_tok[pos] = n / k;
+                    st_w[pos] = wb[r];
+                } else {
+                    sorted_token[pos] = n / k;
+                    sorted_w[pos] = wb[r];
+                }
+                slot_row[n] = pos;
+                if ((peers & lanemask_lt()) == 0) wcnt[wave][e] = base + __popcll(peers);
+            }
+            __builtin_amdgcn_wave_barrier();
         }
+    }
+    if (staged) {
         __syncthreads();
+        for (int i = tid; i < N; i += kThreads) {
+            sorted_token[i] = st_tok[i];
+            sorted_w[i] = st_w[i];
+        }
     }
 }
 

@@ -145,55 +145,138 @@ __global__ __launch_bounds__(256) void k_logits(const uint16_t *__restrict__ x,
     }
 }
 
-// Throughput router for many tokens: block = NW wavefronts handling TPB consecutive
-// tokens; (token, expert-pair) work items are spread over the wavefronts.
-template <int NW, int TPB>
-__global__ __launch_bounds__(NW * 64) void k_route(
+// Throughput router for many tokens on the fp64 MFMA (16 x 16 x 4 per instruction): block =
+// 8 wavefronts and 16 consecutive tokens, 16 NT experts. Wavefront w takes the 32-element
+// chunks c = w, w + 8, .. of H (up to three chunks' loads in flight at a time). For chunk c, lane (m, g) (m = lane % 16, g = lane / 16)
+// loads elements 32c + 8g .. 32c + 8g + 7 of token m and of experts 16 nt + m; MFMA step j
+// (0..7) multiplies element j of every lane, so that lane group g supplies contraction index
+// g of the step and A and B agree on the element. Products of bf16 values are exact in
+// double, so the partial sums carry only the accumulation's rounding. The wavefronts'
+// partial logits are then added in wavefront order in LDS. The same chunk loads write the
+// tokens as mx8 rows (a 32-element block = lanes m, m + 16, m + 32, m + 48).
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kRT = 16;             // tokens per block
+constexpr int kRouteThreads = 512;  // 8 wavefronts split H
+
+// Eight bf16 values (one uint4) as doubles.
+__device__ __forceinline__ void bf16x8_to_f64(const uint4 &u, double (&d)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        d[2 * q] = static_cast<double>(__uint_as_float(w[q] << 16));
+        d[2 * q + 1] = static_cast<double>(__uint_as_float(w[q] & 0xffff0000u));
+    }
+}
+
+// Elements h .. h + 7 of mx8 row t (of R rows, K columns): this lane's quarter of a
+// 32-element block whose other quarters are in lanes lane ^ 16, lane ^ 32, lane ^ 48 (all
+// four active together); the lane with g == 0 writes the two scales.
+__device__ __forceinline__ void mx8_store_quarter(const uint4 &u, uint8_t *q8, int64_t R, int K, int64_t t,
+                                                  int h, bool first) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float v[8];
+    float m = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(w[q] << 16);
+        v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        m = fmaxf(m, fmaxf(fabsf(v[2 * q]), fabsf(v[2 * q + 1])));
+    }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const int eb = mx8_block_exponent(m);
+    uint32_t hi0, lo0, hi1, lo1;
+    mx8_split4(ldexpf(v[0], -eb), ldexpf(v[1], -eb), ldexpf(v[2], -eb), ldexpf(v[3], -eb), hi0, lo0);
+    mx8_split4(ldexpf(v[4], -eb), ldexpf(v[5], -eb), ldexpf(v[6], -eb), ldexpf(v[7], -eb), hi1, lo1);
+    *reinterpret_cast<uint2 *>(q8 + (2 * t) * K + h) = make_uint2(hi0, hi1);
+    *reinterpret_cast<uint2 *>(q8 + (2 * t + 1) * K + h) = make_uint2(lo0, lo1);
+    if (first) {
+        const int ss = mx8_scale_stride(K);
+        uint8_t *qs = q8 + static_cast<size_t>(2 * R) * K;
+        qs[(2 * t) * ss + h / 32] = static_cast<uint8_t>(127 + eb);
+        qs[(2 * t + 1) * ss + h / 32] = static_cast<uint8_t>(123 + eb);
+    }
+}
+
+template <int NT>
+__global__ __launch_bounds__(kRouteThreads) void k_route(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     const uint16_t *__restrict__ br, int64_t T, int H, int E, int k,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ logits_out,
     uint8_t *__restrict__ x8) {
-    __shared__ double lg[TPB][kMaxE];
+    constexpr int NW = kRouteThreads / kWave;
+    constexpr int kAhead = NT >= 16 ? 1 : (NT >= 8 ? 2 : 3);   // chunks loaded together (registers)
+    constexpr int LS = 16 * NT + 1;   // LDS row of one token's logits (padded)
+    __shared__ double lg[kRT * LS];
     __shared__ __attribute__((aligned(16))) uint64_t s_tk[NW][kTopkScratch];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TPB;
-    const int egroups = (E + 1) / 2;
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRT;
+    const int64_t tm = t0 + m;
+    const uint16_t *xrow = x + min(tm, T - 1) * H;      // past T: a duplicate row
+    const uint16_t *wrow[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) wrow[nt] = wr + static_cast<int64_t>(min(16 * nt + m, E - 1)) * H;
+    const bool quant = x8 != nullptr && tm < T;
+    const int nch = H / 32;
 
-    for (int p = wave; p < TPB * egroups; p += NW) {
-        const int tt = p / egroups;
-        const int e0 = 2 * (p % egroups);
-        const int64_t t = t0 + tt;
-        if (t >= T) continue;
-        const bool has2 = (e0 + 1) < E;
-        const uint16_t *xr = x + t * H;
-        const uint16_t *w0 = wr + static_cast<int64_t>(e0) * H;
-        const uint16_t *w1 = wr + static_cast<int64_t>(has2 ? e0 + 1 : e0) * H;
-        double acc0 = 0.0, acc1 = 0.0;
-        for (int h = lane * 8; h < H; h += 8 * kWave) {
-            const uint4 xv = *reinterpret_cast<const uint4 *>(xr + h);
-            acc0 = dot8(xv, *reinterpret_cast<const uint4 *>(w0 + h), acc0);
-            acc1 = dot8(xv, *reinterpret_cast<const uint4 *>(w1 + h), acc1);
+    f64x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f64x4{0.0, 0.0, 0.0, 0.0};
+    // chunks c = wave + NW i, loaded kAhead at a time so that their latencies overlap
+    for (int c0 = wave; c0 < nch; c0 += kAhead * NW) {
+        uint4 xv[kAhead], wv[kAhead][NT];
+#pragma unroll
+        for (int a = 0; a < kAhead; ++a) {
+            const int c = min(c0 + a * NW, nch - 1);      // past the end: reloads the last chunk
+            const int h = 32 * c + 8 * g;
+            xv[a] = *reinterpret_cast<const uint4 *>(xrow + h);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) wv[a][nt] = *reinterpret_cast<const uint4 *>(wrow[nt] + h);
         }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            acc0 += __shfl_xor(acc0, off);
-            acc1 += __shfl_xor(acc1, off);
+        for (int a = 0; a < kAhead; ++a) {
+            const int c = c0 + a * NW;
+            if (c >= nch) break;
+            if (quant) mx8_store_quarter(xv[a], x8, T, H, tm, 32 * c + 8 * g, g == 0);
+            double xd[8];
+            bf16x8_to_f64(xv[a], xd);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                double wd[8];
+                bf16x8_to_f64(wv[a][nt], wd);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[j], wd[j], acc[nt], 0, 0, 0);
+            }
         }
-        if (lane == 0) {
-            lg[tt][e0] = acc0 + static_cast<double>(bf16_to_f32(br[e0]));
-            if (has2) lg[tt][e0 + 1] = acc1 + static_cast<double>(bf16_to_f32(br[e0 + 1]));
+    }
+    // lane (n, g) holds D[g + 4i][n] of each expert tile: token g + 4i, expert 16 nt + n;
+    // the wavefronts' partial sums are added in wavefront order
+    for (int w = 0; w < NW; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    double *dst = &lg[(g + 4 * i) * LS + 16 * nt + m];
+                    *dst = w == 0 ? acc[nt][i] : *dst + acc[nt][i];
+                }
         }
+        __syncthreads();
+    }
+    for (int i = threadIdx.x; i < kRT * E; i += kRouteThreads) {
+        const int j = i / E, e = i % E;
+        lg[j * LS + e] += static_cast<double>(bf16_to_f32(br[e]));
     }
     __syncthreads();
-    for (int tt = wave; tt < TPB; tt += NW) {
-        const int64_t t = t0 + tt;
-        if (t >= T) continue;
-        topk_softmax_wave(lg[tt], E, k, lane, topk_idx + t * k, topk_w + t * k, nullptr, nullptr,
-                          logits_out ? logits_out + t * E : nullptr, s_tk[wave]);
+    for (int j = wave; j < kRT; j += NW) {
+        const int64_t t = t0 + j;
+        if (t < T)
+            topk_softmax_wave(&lg[j * LS], E, k, lane, topk_idx + t * k, topk_w + t * k, nullptr, nullptr,
+                              logits_out ? logits_out + t * E : nullptr, s_tk[wave]);
     }
-    if (x8 != nullptr)
-        for (int tt = 0; tt < TPB && t0 + tt < T; ++tt) write_mx8_row(x + (t0 + tt) * H, H, x8, T, t0 + tt);
 }
 
 template <int NI>
@@ -235,9 +318,15 @@ hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *router
             default: launch_token<7>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
         }
     } else {
-        const int64_t blocks = (d.T + 3) / 4;
-        hipLaunchKernelGGL((k_route<4, 4>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                           x, router_w, router_b, d.T, d.H, d.E, d.k, topk_idx, topk_w, logits, x8);
+        const dim3 grid(static_cast<unsigned>((d.T + kRT - 1) / kRT));
+#define MOE_ROUTE(NT) hipLaunchKernelGGL((k_route<NT>), grid, dim3(kRouteThreads), 0, s, x, router_w, router_b, d.T, \
+                                         d.H, d.E, d.k, topk_idx, topk_w, logits, x8)
+        if (d.E <= 16) MOE_ROUTE(1);
+        else if (d.E <= 32) MOE_ROUTE(2);
+        else if (d.E <= 64) MOE_ROUTE(4);
+        else if (d.E <= 128) MOE_ROUTE(8);
+        else MOE_ROUTE(16);
+#undef MOE_ROUTE
     }
     return hipGetLastError();
 }

@@ -148,8 +148,9 @@ def _random_routing(T, E, k, seed, skew=0.0):
 
 @pytest.mark.parametrize("T,E,k,skew", [(1, 32, 4, 0.0), (64, 32, 4, 2.0), (4096, 32, 4, 0.0),
                                         (2048, 128, 4, 1.0), (333, 256, 8, 3.0), (1025, 4, 4, 0.0),
-                                        (500, 16, 1, 5.0)])
+                                        (500, 16, 1, 5.0), (4097, 32, 4, 0.0), (5000, 64, 4, 1.0)])
 def test_permute_is_a_stable_sort(T, E, k, skew):
+    # T k = 16384 pairs and fewer are sorted in LDS; 16388 and 20000 take the direct path
     idx, w = _random_routing(T, E, k, seed=T + E, skew=skew)
     offsets, sorted_token, order, slot_row = host_permutation(idx, E)
     g_off, g_tok, g_w, g_slot = moe.permute(to_dev(idx), to_dev(w), E)
