@@ -15,8 +15,8 @@ By default the K steps are replayed from a HIP graph captured over one rotation
 (--mode eager launches every call from Python instead).
 
 Also reported, in the same JSON line:
-* roofline: the dominant kernel's average duration, measured with HIP events
-  recorded between the kernels of moe_mxfp4_forward_timed calls, turned into
+* roofline: the dominant kernel's average duration, measured with the start / end HIP
+  events each kernel of a moe_mxfp4_forward_timed call records around itself, turned into
   achieved GB/s (HBM-bound decode) or TFLOP/s (MFMA-bound prefill) from its
   algorithmic bytes or flops per launch, against MI355X's published peak;
   `traffic` comes from the committed rocprofv3 counter summary for that kernel
@@ -232,12 +232,13 @@ def run_timed(wl: Workload, steps: int, warmup: int, mode: str):
 
 
 def run_per_kernel(wl: Workload, steps: int, hip: Hip):
-    """Average duration of each kernel of the layer, from events recorded between them."""
+    """Average duration of each kernel of the layer, from the start / end events each kernel
+    records around its own execution (moe_mxfp4_forward_timed), on the stream it runs on."""
     import torch
     import mxfp4_mixture_experts_router_amd as moe
     lib = wl.lib
     stream = torch.cuda.current_stream()
-    n_ev = moe.MAX_LAUNCHES + 1
+    n_ev = 2 * moe.MAX_LAUNCHES
     events = [[hip.event() for _ in range(n_ev)] for _ in range(steps)]
     arrays = [(ctypes.c_void_p * n_ev)(*evs) for evs in events]
     n_launch = ctypes.c_int(0)
@@ -252,7 +253,7 @@ def run_per_kernel(wl: Workload, steps: int, hip: Hip):
     sums = [0.0] * n
     for evs in events:
         for j in range(n):
-            sums[j] += hip.elapsed_ms(evs[j], evs[j + 1])
+            sums[j] += hip.elapsed_ms(evs[2 * j], evs[2 * j + 1])
     for evs in events:
         for ev in evs:
             hip.destroy(ev)

@@ -118,15 +118,16 @@ moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape,
 
 /*
  * moe_mxfp4_forward with timing instrumentation for profilers and benchmarks: the same
- * validation, kernels and results, plus hipEventRecord calls on `stream` between the
- * launches. `events` holds at least MOE_MXFP4_MAX_LAUNCHES + 1 hipEvent_t handles created
- * by the caller (timing enabled); events[0] is recorded before the first kernel and
- * events[i] right after the i-th. *n_launches receives the number of kernels launched.
- * With H <= 4096 and I <= 4096: 3 for T <= 16 (route, up-projection, down-projection with
- * the combine folded in), 4 for 16 < T <= 64 (route, up-projection, down-projection,
- * combine); 5 for T > 64 or a larger H or I (route, permute, up-projection,
- * down-projection, combine). MOE_EINVAL if
- * events, an events[i] or n_launches is NULL, or n_events is too small.
+ * validation, kernels and results, with every kernel launched through hipExtLaunchKernel so
+ * that it records two events at the start and at the end of its own execution. `events`
+ * holds at least 2 * MOE_MXFP4_MAX_LAUNCHES hipEvent_t handles created by the caller
+ * (timing enabled); launch i records events[2i] and events[2i + 1], so that
+ * hipEventElapsedTime(events[2i], events[2i + 1]) is that kernel's duration.
+ * *n_launches receives the number of kernels launched. With H <= 4096 and I <= 4096: 3 for
+ * T <= 16 (route, up-projection, down-projection with the combine folded in), 4 for
+ * 16 < T <= 64 (route, up-projection, down-projection, combine); 5 for T > 64 or a larger H
+ * or I (route, permute, up-projection, down-projection, combine). MOE_EINVAL if events, an
+ * events[i] or n_launches is NULL, or n_events is too small.
  */
 moe_status_t moe_mxfp4_forward_timed(const moe_mxfp4_shape_t *shape,
                                      const moe_bf16_t *x,

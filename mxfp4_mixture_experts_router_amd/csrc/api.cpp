@@ -151,8 +151,8 @@ MOE_EXPORT moe_status_t moe_mxfp4_workspace_bytes(const moe_mxfp4_shape_t *shape
 namespace {
 
 // Validation + launch sequence shared by moe_mxfp4_forward and moe_mxfp4_forward_timed.
-// With `events`, events[0] is recorded before the first launch and events[i] after the
-// i-th launch, on the same stream.
+// With `events`, launch i records events[2i] and events[2i + 1] at the start and the end of
+// its kernel's execution (hipExtLaunchKernel).
 moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
                          const moe_bf16_t *router_w, const moe_bf16_t *router_b,
                          const uint8_t *gu_blocks, const uint8_t *gu_scales,
@@ -163,10 +163,10 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
     moe_status_t st = check_shape(shape, true);
     if (st != MOE_OK) return st;
     if (events) {
-        if (n_events < MOE_MXFP4_MAX_LAUNCHES + 1)
+        if (n_events < 2 * MOE_MXFP4_MAX_LAUNCHES)
             return fail(MOE_EINVAL, "n_events = %d, at least %d needed", n_events,
-                        MOE_MXFP4_MAX_LAUNCHES + 1);
-        for (int i = 0; i <= MOE_MXFP4_MAX_LAUNCHES; ++i)
+                        2 * MOE_MXFP4_MAX_LAUNCHES);
+        for (int i = 0; i < 2 * MOE_MXFP4_MAX_LAUNCHES; ++i)
             if (!events[i]) return fail(MOE_EINVAL, "events[%d] is NULL", i);
         REQUIRE(n_launches, "n_launches");
         *n_launches = 0;
@@ -195,22 +195,23 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
     int32_t *idx = topk_idx ? topk_idx : reinterpret_cast<int32_t *>(ws + L.idx);
     float *w = topk_w ? topk_w : reinterpret_cast<float *>(ws + L.w);
     int launched = 0;
-    auto mark = [&]() -> moe_status_t {
-        if (!events) return MOE_OK;
-        hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[launched]), s);
-        if (e != hipSuccess) return fail(MOE_EHIP, "hipEventRecord: %s", hipGetErrorString(e));
-        *n_launches = launched;
-        return MOE_OK;
+    // the event pair of the next launch (cleared again however this function returns)
+    struct EventGuard {
+        ~EventGuard() { moe::launch_events() = moe::LaunchEvents{}; }
+    } guard;
+    auto arm = [&]() {
+        if (events)
+            moe::launch_events() = moe::LaunchEvents{static_cast<hipEvent_t>(events[2 * launched]),
+                                                     static_cast<hipEvent_t>(events[2 * launched + 1])};
     };
 #define STEP(call, what)                                 \
     do {                                                 \
+        arm();                                           \
         LAUNCH(call, what);                              \
         ++launched;                                      \
-        moe_status_t m_ = mark();                        \
-        if (m_ != MOE_OK) return m_;                     \
+        if (n_launches) *n_launches = launched;          \
     } while (0)
 
-    if (moe_status_t m0 = mark(); m0 != MOE_OK) return m0;
     if (moe::use_decode_path(shape->T, shape->H, shape->I)) {
         float *part = reinterpret_cast<float *>(ws + L.part);
         uint8_t *x8 = ws + L.x8, *h8 = ws + L.h8;

@@ -688,7 +688,7 @@ hipError_t up_n(const Dims &d, const uint8_t *x8, const uint8_t *xs8, const uint
     const unsigned groups = static_cast<unsigned>((d.T + 8 * NMT - 1) / (8 * NMT));   // an expert has <= T pairs
     const size_t lds = (LDS_A ? static_cast<size_t>(2 * d.T) * d.H : 0) +
                        static_cast<size_t>(2 * d.T) * mx8_scale_stride(d.H);
-    hipLaunchKernelGGL((k_up_mx<NMT, UB, LDS_A, WITH_LOGITS>), dim3(blocks, groups), dim3(256), lds, s, x8, xs8, gb, gs, gbias,
+    MOE_LAUNCH((k_up_mx<NMT, UB, LDS_A, WITH_LOGITS>), dim3(blocks, groups), dim3(256), lds, s, x8, xs8, gb, gs, gbias,
                        logits, idx, w, static_cast<int>(d.T), d.H, d.I, d.E, d.k, d.alpha, d.limit, h8, hs8);
     return hipGetLastError();
 }
@@ -698,7 +698,7 @@ hipError_t down_slots_n(const Dims &d, const uint8_t *h8, const uint8_t *hs8, co
                         const uint16_t *dbias, int32_t *idx, float *w, float *part, hipStream_t s) {
     const unsigned blocks = static_cast<unsigned>(slots_of(d) * (d.H / 16));
     const unsigned groups = static_cast<unsigned>((d.T + 4 * NMT - 1) / (4 * NMT));
-    hipLaunchKernelGGL((k_down_mx_slots<NMT, UB>), dim3(blocks, groups), dim3(256), 0, s, h8, hs8, db, ds, dbias, idx, w,
+    MOE_LAUNCH((k_down_mx_slots<NMT, UB>), dim3(blocks, groups), dim3(256), 0, s, h8, hs8, db, ds, dbias, idx, w,
                        static_cast<int>(d.T), d.H, d.I, d.E, d.k, part);
     return hipGetLastError();
 }
@@ -709,7 +709,7 @@ hipError_t down_tokens_n(const Dims &d, const uint8_t *h8, const uint8_t *hs8, c
     const int64_t N = d.T * d.k;
     const size_t lds = (LDS_A ? static_cast<size_t>(4 * N) * d.I : 0) +
                        static_cast<size_t>(4 * N) * mx8_scale_stride(d.I);
-    hipLaunchKernelGGL((k_down_mx_tokens<NMT, NW, UB, LDS_A, SC_LDS>), dim3(static_cast<unsigned>(d.H / 16)),
+    MOE_LAUNCH((k_down_mx_tokens<NMT, NW, UB, LDS_A, SC_LDS>), dim3(static_cast<unsigned>(d.H / 16)),
                        dim3(NW * 64), lds, s, h8, hs8, db, ds, dbias, idx, w, static_cast<int>(d.T), d.H, d.I, d.E,
                        d.k, y);
     return hipGetLastError();
@@ -719,7 +719,7 @@ hipError_t down_tokens_n(const Dims &d, const uint8_t *h8, const uint8_t *hs8, c
 
 hipError_t launch_combine_decode(const Dims &d, const float *part, uint16_t *y, hipStream_t s) {
     const unsigned blocks = static_cast<unsigned>((d.T * (d.H / 4) + 255) / 256);
-    hipLaunchKernelGGL(k_combine_slots, dim3(blocks), dim3(256), 0, s, part, static_cast<int>(d.T), d.H,
+    MOE_LAUNCH(k_combine_slots, dim3(blocks), dim3(256), 0, s, part, static_cast<int>(d.T), d.H,
                        d.k, y);
     return hipGetLastError();
 }

@@ -426,7 +426,7 @@ hipError_t launch_up_grouped(const Dims &d, const uint8_t *x8, const uint8_t *gu
                              const uint8_t *gu_scales, const uint16_t *gu_bias,
                              const int32_t *offsets, const int32_t *sorted_token,
                              uint8_t *h8, hipStream_t s) {
-    hipLaunchKernelGGL((k_gemm_mx<true>), dim3(persistent_blocks()), dim3(kThreads), 0, s, x8, d.T, sorted_token,
+    MOE_LAUNCH((k_gemm_mx<true>), dim3(persistent_blocks()), dim3(kThreads), 0, s, x8, d.T, sorted_token,
                        nullptr, gu_blocks, gu_scales, gu_bias, offsets, d.E, d.H, 2 * d.I, d.alpha, d.limit,
                        h8, d.T * d.k, nullptr);
     return hipGetLastError();
@@ -436,7 +436,7 @@ hipError_t launch_down_grouped(const Dims &d, const uint8_t *h8, const uint8_t *
                                const uint8_t *dn_scales, const uint16_t *dn_bias,
                                const int32_t *offsets, const float *sorted_w, float *o,
                                hipStream_t s) {
-    hipLaunchKernelGGL((k_gemm_mx<false>), dim3(persistent_blocks()), dim3(kThreads), 0, s, h8, d.T * d.k, nullptr,
+    MOE_LAUNCH((k_gemm_mx<false>), dim3(persistent_blocks()), dim3(kThreads), 0, s, h8, d.T * d.k, nullptr,
                        sorted_w, dn_blocks, dn_scales, dn_bias, offsets, d.E, d.I, d.H, d.alpha, d.limit,
                        nullptr, 0, o);
     return hipGetLastError();
@@ -444,7 +444,7 @@ hipError_t launch_down_grouped(const Dims &d, const uint8_t *h8, const uint8_t *
 
 hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row, uint16_t *y,
                           hipStream_t s) {
-    hipLaunchKernelGGL(k_combine, dim3(grid_for(d.T * (d.H / 4))), dim3(256), 0, s, o, slot_row,
+    MOE_LAUNCH(k_combine, dim3(grid_for(d.T * (d.H / 4))), dim3(256), 0, s, o, slot_row,
                        d.T, d.H, d.k, y);
     return hipGetLastError();
 }
@@ -452,7 +452,7 @@ hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int cols, uint8_t *q8, hipStream_t s) {
     const int64_t nblk = rows * (cols / 32);
     if (nblk == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_quantize, dim3(grid_for(nblk)), dim3(256), 0, s, x, rows, cols, q8);
+    MOE_LAUNCH(k_quantize, dim3(grid_for(nblk)), dim3(256), 0, s, x, rows, cols, q8);
     return hipGetLastError();
 }
 
@@ -460,7 +460,7 @@ hipError_t launch_dequant(const uint8_t *blocks, const uint8_t *scales, int64_t 
                           uint16_t *out, hipStream_t s) {
     const int64_t nblk = rows * (cols / 32);
     if (nblk == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_dequant, dim3(grid_for(nblk)), dim3(256), 0, s, blocks, scales,
+    MOE_LAUNCH(k_dequant, dim3(grid_for(nblk)), dim3(256), 0, s, blocks, scales,
                        nblk, out);
     return hipGetLastError();
 }

@@ -2,10 +2,26 @@
 // Each returns hipSuccess or the launch error; none synchronises.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Events that the next kernel launch of this thread records around the kernel itself (start
+// and end of its execution, from the dispatch); both null outside the timed forward call.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+inline LaunchEvents &launch_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+
+// Every launcher launches through this macro (one kernel per launcher call).
+#define MOE_LAUNCH(kernel, grid, block, shmem, stream, ...)                                   \
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ::moe::launch_events().start,   \
+                          ::moe::launch_events().stop, 0, __VA_ARGS__)
 
 // Token count up to which the forward pass takes the decode path (route -> fused
 // up-projection -> fused down-projection + combine, no sorted permutation in memory).

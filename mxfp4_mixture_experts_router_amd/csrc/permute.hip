@@ -162,7 +162,7 @@ hipError_t launch_permute(const Dims &d, const int32_t *topk_idx, const float *t
                           int32_t *offsets, int32_t *sorted_token, float *sorted_w,
                           int32_t *slot_row, hipStream_t s) {
     const int32_t N = static_cast<int32_t>(d.T * d.k);
-    hipLaunchKernelGGL(k_permute, dim3(1), dim3(kThreads), 0, s, topk_idx, topk_w, N, d.E, d.k,
+    MOE_LAUNCH(k_permute, dim3(1), dim3(kThreads), 0, s, topk_idx, topk_w, N, d.E, d.k,
                        offsets, sorted_token, sorted_w, slot_row);
     return hipGetLastError();
 }

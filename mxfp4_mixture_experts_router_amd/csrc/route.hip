@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
 template <int NI>
 void launch_token(const Dims &d, const uint16_t *x, const uint16_t *w, const uint16_t *b,
                   int32_t *idx, float *wt, float *logits, uint8_t *x8, hipStream_t s) {
-    hipLaunchKernelGGL((k_route_token<NI>), dim3(static_cast<unsigned>(d.T)), dim3(512), 0, s, x, w,
+    MOE_LAUNCH((k_route_token<NI>), dim3(static_cast<unsigned>(d.T)), dim3(512), 0, s, x, w,
                        b, d.H, d.E, d.k, idx, wt, logits, x8, static_cast<int>(d.T));
 }
 
@@ -294,9 +294,9 @@ hipError_t launch_logits(const Dims &d, const uint16_t *x, const uint16_t *route
     const int niq = (d.H + 2047) / 2048;
     const dim3 grid(static_cast<unsigned>((d.E + 1) / 2 + 1), static_cast<unsigned>(d.T));
     switch (niq) {
-        case 1: hipLaunchKernelGGL((k_logits<1>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
-        case 2: hipLaunchKernelGGL((k_logits<2>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
-        case 3: hipLaunchKernelGGL((k_logits<3>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
+        case 1: MOE_LAUNCH((k_logits<1>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
+        case 2: MOE_LAUNCH((k_logits<2>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
+        case 3: MOE_LAUNCH((k_logits<3>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
         default: return hipErrorInvalidValue;   // H > 6144: the caller uses launch_route
     }
     return hipGetLastError();
@@ -319,7 +319,7 @@ hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *router
         }
     } else {
         const dim3 grid(static_cast<unsigned>((d.T + kRT - 1) / kRT));
-#define MOE_ROUTE(NT) hipLaunchKernelGGL((k_route<NT>), grid, dim3(kRouteThreads), 0, s, x, router_w, router_b, d.T, \
+#define MOE_ROUTE(NT) MOE_LAUNCH((k_route<NT>), grid, dim3(kRouteThreads), 0, s, x, router_w, router_b, d.T, \
                                          d.H, d.E, d.k, topk_idx, topk_w, logits, x8)
         if (d.E <= 16) MOE_ROUTE(1);
         else if (d.E <= 32) MOE_ROUTE(2);

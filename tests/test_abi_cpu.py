@@ -117,6 +117,19 @@ def test_forward_workspace_checks(lib):
     assert fwd(lib, s, ws=0x100010) == EALIGN
 
 
+def test_forward_timed_validates_events(lib):
+    s = shape()
+    base = [ctypes.byref(s)] + [A] * 10 + [None, None, 0x100000, 1 << 40, None]
+    n = ctypes.c_int(-1)
+    evs = (ctypes.c_void_p * (2 * moe.MAX_LAUNCHES))(*([A] * (2 * moe.MAX_LAUNCHES)))
+    assert lib.moe_mxfp4_forward_timed(*base, None, 2 * moe.MAX_LAUNCHES, ctypes.byref(n)) == EINVAL
+    assert lib.moe_mxfp4_forward_timed(*base, evs, 2 * moe.MAX_LAUNCHES - 1, ctypes.byref(n)) == EINVAL
+    assert "n_events" in lib.moe_mxfp4_last_error().decode()
+    evs[3] = None
+    assert lib.moe_mxfp4_forward_timed(*base, evs, 2 * moe.MAX_LAUNCHES, ctypes.byref(n)) == EINVAL
+    assert "events[3]" in lib.moe_mxfp4_last_error().decode()
+
+
 def test_forward_bad_shape_before_pointers(lib):
     s = shape(k=0)
     assert fwd(lib, s, x=None) == ESHAPE

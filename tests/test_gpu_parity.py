@@ -288,6 +288,76 @@ def test_forward_tie_fixture(T):
     assert_close_rows(bf16_to_f64(y)[tokens], ref["y"], "tie fixture")
 
 
+class _HipEvents:
+    """hipEvent_t handles from the HIP runtime this process already loaded."""
+
+    def __init__(self):
+        import ctypes
+        import re
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                m = re.search(r"(/\S*libamdhip64\.so\S*)", line)
+                if m:
+                    path = m.group(1)
+                    break
+        self.c = ctypes
+        self.lib = ctypes.CDLL(path or "libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            ev = self.c.c_void_p()
+            assert self.lib.hipEventCreate(self.c.byref(ev)) == 0
+            evs.append(ev.value)
+        return evs
+
+    def elapsed_ms(self, a, b):
+        ms = self.c.c_float()
+        assert self.lib.hipEventElapsedTime(self.c.byref(ms), self.c.c_void_p(a), self.c.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, evs):
+        for ev in evs:
+            self.lib.hipEventDestroy(self.c.c_void_p(ev))
+
+
+@pytest.mark.parametrize("T,launches", [(1, 3), (17, 4), (65, 5)])
+def test_forward_timed_matches_forward(T, launches):
+    import ctypes
+    cfg = CONFIGS["tiny"]
+    inp = upload(make_inputs(cfg, seed=5, T=T))
+    y_ref = _forward(inp, cfg.k, cfg)
+    H, I, E = cfg.H, cfg.I, cfg.E
+    shape = moe._shape(T, H, I, E, cfg.k, cfg.alpha, cfg.limit)
+    ws = torch.empty(max(moe.workspace_bytes(T, H, I, E, cfg.k), 256), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(y_ref)
+    hip = _HipEvents()
+    evs = hip.create(2 * moe.MAX_LAUNCHES)
+    arr = (ctypes.c_void_p * len(evs))(*evs)
+    n = ctypes.c_int(-1)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = moe.load_library().moe_mxfp4_forward_timed(
+        ctypes.byref(shape), P(inp["x"]), P(inp["router_w"]), P(inp["router_b"]), P(inp["gu_blocks"]),
+        P(inp["gu_scales"]), P(inp["gu_bias"]), P(inp["dn_blocks"]), P(inp["dn_scales"]),
+        P(inp["dn_bias"]), P(y), None, None, P(ws), ws.numel(),
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), arr, len(evs), ctypes.byref(n))
+    assert st == 0, moe.load_library().moe_mxfp4_last_error()
+    torch.cuda.synchronize()
+    assert n.value == launches
+    # each kernel's own start / end events: positive durations, in launch order
+    for i in range(n.value):
+        assert hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) > 0
+        if i:
+            assert hip.elapsed_ms(evs[2 * i - 1], evs[2 * i]) >= 0
+    hip.destroy(evs)
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+
+
 def test_forward_zero_tokens():
     cfg = CONFIGS["tiny"]
     inp = upload(make_inputs(cfg, T=0))
