@@ -9,17 +9,18 @@
 //        matrix h8 (T k rows of I, sorted-row order)
 //  down: o[r, d] = w[r] * (h[r] . Wdn[e, d] + bdn[e, d])    (orientation [E, H, I], same page)
 //
-// Work list: every expert's rows [offsets[e], offsets[e+1]) are cut into BM-row tiles; the
-// (m-tile, n-tile) pairs of all experts form one flattened list. The grid is persistent and
-// XCD-aware: the blocks of one XCD (block b runs on XCD b % 8) take the m-tiles mg with
-// mg % 8 == XCD, walking all n-tiles of one m-tile before the next, so an m-tile's
-// activations are fetched into one XCD's L2 and reused across its n-tiles.
+// Work list: every expert's rows [offsets[e], offsets[e+1]) are cut into BM-row tiles; each
+// expert's (n-tile, m-tile) pairs, m-tile innermost, form one flattened list over all
+// experts. The grid is persistent (one block per CU) and XCD-aware: chunk c of 32
+// consecutive items runs on XCD c % 8 (block b runs on XCD b % 8), one item per block, so
+// that the blocks running together on an XCD share an expert's weight tiles (read from HBM
+// once, then from that XCD's L2) and its activation tiles.
 //
 // Block tile: BM = 128 activation rows (256 A rows: hi, lo) x BN = 256 output columns; the
-// contraction advances BK = 128 (one MFMA step = four scale blocks) per stage. Eight
-// wavefronts, two per SIMD, in a 4 x 2 arrangement: wavefront (wm, wn) owns A rows
-// 64 wm .. 64 wm + 63 and columns 128 wn .. 128 wn + 127, i.e. 4 x 8 MFMA tiles (128
-// accumulators). Operands go from global memory straight into LDS (global_load_lds: each
+// contraction advances BK = 128 (one MFMA step = four scale blocks) per stage. Four
+// wavefronts, one per SIMD, in a 2 x 2 arrangement: wavefront (wm, wn) owns A rows
+// 128 wm .. 128 wm + 127 and columns 128 wn .. 128 wn + 127, i.e. 8 x 8 MFMA tiles (256
+// accumulators, in the accumulation registers). Operands go from global memory straight into LDS (global_load_lds: each
 // lane's 16 or 4 bytes land at the instruction's LDS base + lane * size) into a ring of
 // three stage buffers; a stage's loads are issued two stages before it is multiplied, and
 // one barrier per stage both publishes the stage and retires the buffer the next issue
@@ -40,6 +41,7 @@
 #include "mx_mfma.h"
 
 
+
 namespace moe {
 namespace {
 
@@ -47,12 +49,13 @@ constexpr int kBM = 128;                       // activation rows per tile
 constexpr int kAR = 2 * kBM;                   // A rows per tile (hi, lo)
 constexpr int kBN = 256;                       // output columns (weight rows) per tile
 constexpr int kBK = 128;                       // contraction per stage
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
+constexpr int kChunk = 32;                     // items per XCD chunk (= blocks per XCD)
 constexpr int kOffB = kAR * kBK;               // 32768
 constexpr int kOffAS = kOffB + kBN * kBK / 2;  // 49152
 constexpr int kOffBS = kOffAS + kAR * 4;       // 50176
 constexpr int kStage = kOffBS + kBN * 8;       // 52224
-constexpr int kOps = 8;                        // global_load_lds per wavefront per stage
+constexpr int kOps = 15;                       // global_load_lds per wavefront per stage
 constexpr int kHS = 65;                        // up epilogue: padded row of 64 fp32 pairs
 
 __shared__ __attribute__((aligned(16))) uint8_t g_stages[3 * kStage];
@@ -84,7 +87,7 @@ __device__ __forceinline__ void barrier_only() {
 }
 
 template <bool UP>
-__global__ __launch_bounds__(kThreads) void k_gemm_mx(
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
     const uint8_t *__restrict__ a8, int64_t a_rows,  // mx8 activations: up x8 (T rows), down h8 (T k rows)
     const int32_t *__restrict__ sorted_token,        // up only
     const float *__restrict__ sorted_w,              // down only
@@ -94,19 +97,21 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
     uint8_t *__restrict__ h8, int64_t h_rows,        // up: mx8 output (T k rows of Nrows / 2)
     float *__restrict__ o_out) {                     // down
     __shared__ int s_off[kMaxE + 1];
-    __shared__ int s_mcum[kMaxE + 1];
+    __shared__ int s_icum[kMaxE + 1];               // item prefix over experts
 
+    const int ntn = (Nrows + kBN - 1) / kBN;
     const int tid0 = threadIdx.x;
     for (int e = tid0; e <= E; e += kThreads) s_off[e] = offsets[e];
     __syncthreads();
     if (tid0 < kWave) {
         const int lane = tid0;
-        // m-tile prefix over experts (E <= 256: four per lane)
+        // item prefix: expert e has ceil(rows / BM) m-tiles x ntn n-tiles (E <= 256: four
+        // per lane)
         int v[4], local = 0;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int e = 4 * lane + c;
-            v[c] = e < E ? (s_off[e + 1] - s_off[e] + kBM - 1) / kBM : 0;
+            v[c] = e < E ? ntn * ((s_off[e + 1] - s_off[e] + kBM - 1) / kBM) : 0;
             local += v[c];
         }
         int incl = local;
@@ -119,35 +124,37 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int e = 4 * lane + c;
-            if (e < E) s_mcum[e] = run;
+            if (e < E) s_icum[e] = run;
             run += v[c];
         }
-        if (lane == kWave - 1) s_mcum[E] = incl;
+        if (lane == kWave - 1) s_icum[E] = incl;
     }
     __syncthreads();
 
-    const int ntn = (Nrows + kBN - 1) / kBN;
-    const int mtiles = s_mcum[E];
+    const int items = s_icum[E];
     const int nkb = K / 32;                      // scale blocks per row
     const int kt_total = (nkb + 3) / 4;
     const int kt_last = kt_total - 1;
     const int kbytes = K / 2;
     const int ass = mx8_scale_stride(K);
     const uint8_t *a_sc = a8 + static_cast<size_t>(2 * a_rows) * K;
-    // XCD-aware walk: this block's XCD owns m-tiles mg = xcd + 8j
-    const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nb = gridDim.x >> 3;
-    const int my_m = mtiles > xcd ? (mtiles - xcd + 7) / 8 : 0;
-    const int my_tiles = my_m * ntn;
+    // XCD-aware walk over chunks of kChunk consecutive items: chunk c runs on XCD c % 8,
+    // item c kChunk + j on that XCD's j-th block
+    const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3;
 
-    for (int it = lb; it < my_tiles; it += nb) {
-        const int mg = xcd + 8 * (it / ntn), nt_tile = it % ntn;
-        int lo = 0, hi = E - 1;                       // last e with s_mcum[e] <= mg
+    for (int c = xcd; c * kChunk < items; c += 8) {
+        const int item = c * kChunk + lb;
+        if (item >= items) continue;
+        int lo = 0, hi = E - 1;                       // last e with s_icum[e] <= item
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (s_mcum[mid] <= mg) lo = mid; else hi = mid - 1;
+            if (s_icum[mid] <= item) lo = mid; else hi = mid - 1;
         }
         const int e = lo;
-        const int row0 = s_off[e] + (mg - s_mcum[e]) * kBM;
+        const int mt_e = (s_off[e + 1] - s_off[e] + kBM - 1) / kBM;
+        const int local_item = item - s_icum[e];
+        const int nt_tile = local_item / mt_e, mg = local_item % mt_e;
+        const int row0 = s_off[e] + mg * kBM;
         const int rows = min(kBM, s_off[e + 1] - row0);
         const int n0 = nt_tile * kBN;
 
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
         asm volatile("" : "+v"(tid));
         const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
         const int m = lane & 15, g = lane >> 4;
-        const int wm = wave & 3, wn = wave >> 2;
+        const int wm = wave & 1, wn = wave >> 1;
 
         // --- loads. Global addresses are a uniform base plus a 32-bit per-lane offset (the
         // host keeps every operand below 4 GiB). A chunk or block past K (last stage only)
@@ -176,98 +183,108 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
             const int src = UP ? sorted_token[row0 + ar] : row0 + ar;
             return static_cast<uint32_t>(2 * src + (R & 1));
         };
-        // A: instruction i of wavefront w fills A rows 32 w + 8 i + lane / 8
-        uint32_t a_off[4];
+        // A: instruction i of wavefront w fills A rows 64 w + 8 i + lane / 8
+        uint32_t a_off[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a_off[i] = a_src(32 * wave + 8 * i + (lane >> 3)) * static_cast<uint32_t>(K);
-        // A scales: wavefront w fills rows 64 (w % 4) + lane (w and w + 4 load the same bytes)
-        const uint32_t as_off = a_src(64 * (wave & 3) + lane) * static_cast<uint32_t>(ass);
-        // B: instruction i fills weight rows 32 w + 16 i + lane / 4 (clamped to the matrix)
+        for (int i = 0; i < 8; ++i) a_off[i] = a_src(64 * wave + 8 * i + (lane >> 3)) * static_cast<uint32_t>(K);
+        // A scales: wavefront w fills rows 64 w + lane
+        const uint32_t as_off = a_src(64 * wave + lane) * static_cast<uint32_t>(ass);
+        // B: instruction i fills weight rows 64 w + 16 i + lane / 4 (clamped to the matrix)
         const uint8_t *wblk = wblocks + static_cast<int64_t>(e) * Nrows * kbytes;
-        uint32_t b_off[2];
+        uint32_t b_off[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) b_off[i] = min(n0 + 32 * wave + 16 * i + (lane >> 2), Nrows - 1) * kbytes;
+        for (int i = 0; i < 4; ++i) b_off[i] = min(n0 + 64 * wave + 16 * i + (lane >> 2), Nrows - 1) * kbytes;
         // B scales, read as aligned dwords: the pair at (p & ~3) holds the stage's bytes
         // p .. p + 3; a second dword past the tensor's end holds no valid byte and reads the
-        // last dword instead. Wavefront w fills rows 32 w + lane / 2, dword lane % 2.
+        // last dword instead. Instruction j of wavefront w fills rows 64 w + 32 j + lane / 2,
+        // dword lane % 2.
         const uint8_t *wsc = wscales + static_cast<int64_t>(e) * Nrows * nkb;
         const int64_t sc_len = static_cast<int64_t>(E - e) * Nrows * nkb;   // to the tensor's end
         const uint32_t last4 = static_cast<uint32_t>(min<int64_t>(sc_len, 0x7fffffff) - 4);
-        const uint32_t bs_off = (min(n0 + 32 * wave + (lane >> 1), Nrows - 1) * nkb & ~3) + 4 * (lane & 1);
+        uint32_t bs_off[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            bs_off[j] = (min(n0 + 64 * wave + 32 * j + (lane >> 1), Nrows - 1) * nkb & ~3) + 4 * (lane & 1);
 
         const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)g_stages;
-        auto issue = [&](int buf, int kt) {
+        // the loads of stage kt into buffer buf, in parts issued between the row tiles'
+        // MFMAs of the current stage, so that no wavefront stalls on a burst of them
+        auto issue_part = [&](int part, int buf, int kt) {
+            const uint32_t lbuf = lds0 + buf * kStage;
             const uint32_t ach = kt == kt_last ? a_ch_last : a_ch;
             const uint32_t bch = kt == kt_last ? b_ch_last : b_ch;
             const uint8_t *a_k = a8 + kBK * kt;          // uniform bases
             const uint8_t *b_k = wblk + 64 * kt;
-            const uint32_t lb = lds0 + buf * kStage;
+            if (part < 4) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dma16(a_k, a_off[i] + ach, lb + (4 * wave + i) * 1024);
+                for (int i = 2 * part; i < 2 * part + 2; ++i) dma16(a_k, a_off[i] + ach, lbuf + (8 * wave + i) * 1024);
+                if (part == 0) dma4(a_sc + 4 * kt, as_off, lbuf + kOffAS + 256 * wave);
+            } else if (part < 6) {
+                const int j = part - 4;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) dma16(b_k, b_off[i] + bch, lb + kOffB + (2 * wave + i) * 1024);
-            dma4(a_sc + 4 * kt, as_off, lb + kOffAS + 256 * (wave & 3));
-            dma4(wsc, min(bs_off + 4 * kt, last4), lb + kOffBS + 256 * wave);
+                for (int i = 2 * j; i < 2 * j + 2; ++i) dma16(b_k, b_off[i] + bch, lbuf + kOffB + (4 * wave + i) * 1024);
+                dma4(wsc, min(bs_off[j] + 4 * kt, last4), lbuf + kOffBS + (2 * wave + j) * 256);
+            }
+        };
+        auto issue = [&](int buf, int kt) {
+#pragma unroll
+            for (int part = 0; part < 6; ++part) issue_part(part, buf, kt);
         };
 
-        // --- multiply. Byte of the 8-byte scale window holding this lane's scale (block g)
-        // of each of its eight B columns.
-        int sbyte[8];
+        f32x4 acc[8][8];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) sbyte[nt] = ((min(n0 + 128 * wn + 16 * nt + m, Nrows - 1) * nkb) & 3) + g;
-
-        f32x4 acc[4][8];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 8; ++a)
 #pragma unroll
             for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // B fragments and scales of the wavefront's eight column tiles are read first and
-        // kept; A fragments are then streamed one row tile at a time (8 MFMAs each). Blocks
-        // past K (vb < 4: the last stage of a contraction whose block count is not a
-        // multiple of 4) get zero A data and unit scales, so they add exactly 0. LDS
-        // addresses are one per-lane base per operand plus constants.
-        const uint32_t lb_b = 8192 * wn + 64 * m + 16 * (g ^ ((m >> 1) & 3));
-        const uint32_t lb_bs = 1024 * wn + 8 * m;
-        const uint32_t lb_a = 8192 * wm + 128 * m + 16 * (g ^ (m & 7));
-        const uint32_t lb_as = 256 * wm + 4 * m;
-        auto compute = [&](const uint8_t *buf, int kt) {
-            const int vb = nkb - 4 * kt;
-            const bool ok_sc = g < vb;
-            const uint32_t m_lo = (g >> 1) < vb ? ~0u : 0u, m_hi = 2 + (g >> 1) < vb ? ~0u : 0u;
-            const uint32_t ob = lb_b, obs = lb_bs, oa = lb_a, oas = lb_as;
-            const uint8_t *pb = buf + kOffB + ob;
-            const uint8_t *pbs = buf + kOffBS + obs;
-            const uint8_t *pa = buf + oa;
-            const uint8_t *pa2 = buf + (oa ^ 64u);          // chunk g + 4: slot s0 ^ 4
-            const uint8_t *pas = buf + kOffAS + oas;
+        // --- multiply. B fragments and scales of the wavefront's eight column tiles are read
+        // first and kept; A fragments are then streamed one row tile at a time (8 MFMAs
+        // each). LDS addresses are one per-lane base per operand plus constants. The scales
+        // are read as single bytes: A row R's block g, and weight row n's block g at byte
+        // (n K/32) % 4 + g of its 8-byte window (the same for all eight column tiles: they
+        // are 16 rows apart).
+        const uint32_t lb_b = kOffB + 8192 * wn + 64 * m + 16 * (g ^ ((m >> 1) & 3));
+        const uint32_t lb_bs = kOffBS + 1024 * wn + 8 * m + (((n0 + 128 * wn + m) * nkb) & 3) + g;
+        const uint32_t lb_a = 16384 * wm + 128 * m + 16 * (g ^ (m & 7));
+        const uint32_t lb_as = kOffAS + 512 * wm + 4 * m + g;
+        // In the last stage of a contraction whose block count is not a multiple of 4
+        // (vb < 4, a uniform branch), blocks past K get zero A data and unit scales, so they
+        // add exactly 0. Stage kt + 2's loads (if any) go out between the row tiles.
+        auto compute = [&](int buf, int kt, bool refill, int buf2) {
+            const uint8_t *base = g_stages + buf * kStage;
             i32x8 bop[8];
             uint32_t sb[8];
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
-                bop[nt] = mx_b_operand(*reinterpret_cast<const uint4 *>(pb + 1024 * nt));
-                const uint2 sv = *reinterpret_cast<const uint2 *>(pbs + 128 * nt);
-                const uint32_t word = sbyte[nt] < 4 ? sv.x : sv.y;
-                const uint32_t v = (word >> (8 * (sbyte[nt] & 3))) & 0xffu;
-                sb[nt] = ok_sc ? v : 127u;
+                bop[nt] = mx_b_operand(*reinterpret_cast<const uint4 *>(base + lb_b + 1024 * nt));
+                sb[nt] = base[lb_bs + 128 * nt];
+            }
+            const int vb = nkb - 4 * kt;
+            if (vb < 4) {
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) sb[nt] = g < vb ? sb[nt] : 127u;
             }
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                uint4 lo16 = *reinterpret_cast<const uint4 *>(pa + 2048 * mt);
-                uint4 hi16 = *reinterpret_cast<const uint4 *>(pa2 + 2048 * mt);
-                const uint32_t v = (*reinterpret_cast<const uint32_t *>(pas + 64 * mt) >> (8 * g)) & 0xffu;
-                lo16.x &= m_lo; lo16.y &= m_lo; lo16.z &= m_lo; lo16.w &= m_lo;
-                hi16.x &= m_hi; hi16.y &= m_hi; hi16.z &= m_hi; hi16.w &= m_hi;
+            for (int mt = 0; mt < 8; ++mt) {
+                uint4 lo16 = *reinterpret_cast<const uint4 *>(base + lb_a + 2048 * mt);
+                uint4 hi16 = *reinterpret_cast<const uint4 *>(base + (lb_a ^ 64u) + 2048 * mt);   // chunk g + 4
+                uint32_t sa = base[lb_as + 64 * mt];
+                if (vb < 4) {
+                    // lane group g carries blocks g / 2 (low half) and 2 + g / 2 (high half)
+                    if ((g >> 1) >= vb) lo16 = zero4();
+                    if (2 + (g >> 1) >= vb) hi16 = zero4();
+                    if (g >= vb) sa = 127u;
+                }
                 const i32x8 af = mx_a_operand(lo16, hi16);
-                const uint32_t sa = ok_sc ? v : 127u;
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = mfma_mx(af, bop[nt], acc[mt][nt], sa, sb[nt]);
+                if (refill && mt < 6) issue_part(mt, buf2, kt + 2);
             }
         };
 
         // stage kt (buffer kt % 3): wait for its loads (stage kt + 1's stay in flight),
-        // publish it to all wavefronts, refill the buffer stage kt - 1 used with stage
-        // kt + 2, multiply.
+        // publish it to all wavefronts, multiply while refilling the buffer stage kt - 1 used
+        // with stage kt + 2.
         __syncthreads();   // the previous tile's epilogue is done with LDS
         issue(0, 0);
         if (kt_total > 1) issue(1, 1);
@@ -276,26 +293,25 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
             if (kt + 1 < kt_total) wait_vm<kOps>(); else wait_vm<0>();
             barrier_only();
             const int buf2 = buf == 0 ? 2 : buf - 1;     // (kt + 2) % 3
-            if (kt + 2 < kt_total) issue(buf2, kt + 2);
-            compute(g_stages + buf * kStage, kt);
+            compute(buf, kt, kt + 2 < kt_total, buf2);
             buf = buf == 2 ? 0 : buf + 1;
         }
         __syncthreads();   // every wavefront is done with the stage buffers
 
         // --- epilogue. Lane (m, g) of MFMA tile (mt, nt) holds column 16 nt + m of A rows
         // 16 mt + 4g + r: activation row 8 mt + 2g (r = 0, 1: hi, lo) and 8 mt + 2g + 1
-        // (r = 2, 3) of the wavefront's 32; value = D[hi] + D[lo].
+        // (r = 2, 3) of the wavefront's 64; value = D[hi] + D[lo].
         if (UP) {
-            // h of the wavefront's 32 rows x 64 pairs (fp32) into LDS (wavefront (wm, wn) at
-            // stage buffer wn, offset wm), then each lane quantizes one (row, MX block) item
-            float *s_h = reinterpret_cast<float *>(g_stages + wn * kStage) + wm * (32 * kHS);
+            // h of the wavefront's 64 rows x 64 pairs (fp32) into LDS (region 2 wn + wm of 64 kHS
+            // floats), then each lane quantizes two (row, MX block) items
+            float *s_h = reinterpret_cast<float *>(g_stages) + (2 * wn + wm) * (64 * kHS);
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
                 const int wr = n0 + 128 * wn + 16 * nt + m;
                 const float bias = wr < Nrows ? bf16_to_f32(wbias[static_cast<int64_t>(e) * Nrows + wr]) : 0.f;
                 const int pair = 8 * nt + (m >> 1);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
+                for (int mt = 0; mt < 8; ++mt) {
                     const float v0 = acc[mt][nt][0] + acc[mt][nt][1] + bias;
                     const float v1 = acc[mt][nt][2] + acc[mt][nt][3] + bias;
                     // even lane (gate column) keeps row 8mt + 2g, odd lane (up) row 8mt + 2g + 1
@@ -309,22 +325,26 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
             const int Iw = Nrows / 2;
             const int is8 = mx8_scale_stride(Iw);
             uint8_t *h_sc = h8 + static_cast<size_t>(2 * h_rows) * Iw;
-            const int r = lane >> 1, blk = lane & 1;
-            const int R = 32 * wm + r;                        // tile activation row
-            const int ib = (n0 + 128 * wn) / 64 + blk;        // MX block of h
-            if (R < rows && 64 * ib < Nrows) {
-                float v[32];
 #pragma unroll
-                for (int i = 0; i < 32; ++i) v[i] = s_h[r * kHS + 32 * blk + i];
-                store_mx8_block(v, h8, h_sc, static_cast<int64_t>(row0 + R), Iw, is8, ib);
+            for (int q = 0; q < 2; ++q) {
+                const int item = lane + 64 * q;
+                const int r = item >> 1, blk = item & 1;
+                const int R = 64 * wm + r;                        // tile activation row
+                const int ib = (n0 + 128 * wn) / 64 + blk;        // MX block of h
+                if (R < rows && 64 * ib < Nrows) {
+                    float v[32];
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) v[i] = s_h[r * kHS + 32 * blk + i];
+                    store_mx8_block(v, h8, h_sc, static_cast<int64_t>(row0 + R), Iw, is8, ib);
+                }
             }
         } else {
-            float wrow[4][2];
+            float wrow[8][2];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const int lr = 32 * wm + 8 * mt + 2 * g + j;
+                    const int lr = 64 * wm + 8 * mt + 2 * g + j;
                     wrow[mt][j] = lr < rows ? sorted_w[row0 + lr] : 0.f;
                 }
 #pragma unroll
@@ -333,10 +353,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
                 if (d >= Nrows) continue;
                 const float bd = bf16_to_f32(wbias[static_cast<int64_t>(e) * Nrows + d]);
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        const int lr = 32 * wm + 8 * mt + 2 * g + j;
+                        const int lr = 64 * wm + 8 * mt + 2 * g + j;
                         if (lr >= rows) continue;
                         const float v = acc[mt][nt][2 * j] + acc[mt][nt][2 * j + 1];
                         o_out[static_cast<int64_t>(row0 + lr) * Nrows + d] = (v + bd) * wrow[mt][j];
