@@ -56,7 +56,8 @@ constexpr int kOffAS = kOffB + kBN * kBK / 2;  // 49152
 constexpr int kOffBS = kOffAS + kAR * 4;       // 50176
 constexpr int kStage = kOffBS + kBN * 8;       // 52224
 constexpr int kOps = 15;                       // global_load_lds per wavefront per stage
-constexpr int kHS = 65;                        // up epilogue: padded row of 64 fp32 pairs
+constexpr int kHS = 67;                        // up epilogue: padded row of 64 fp32 pairs
+constexpr int kOS = 132;                       // down epilogue: padded row of 128 fp32 outputs
 
 __shared__ __attribute__((aligned(16))) uint8_t g_stages[3 * kStage];
 
@@ -98,6 +99,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
     float *__restrict__ o_out) {                     // down
     __shared__ int s_off[kMaxE + 1];
     __shared__ int s_icum[kMaxE + 1];               // item prefix over experts
+    __shared__ uint16_t s_bias[kBN];                // the tile's biases (bf16)
+    __shared__ float s_rw[kBM];                     // down: the tile rows' routing weights
 
     const int ntn = (Nrows + kBN - 1) / kBN;
     const int tid0 = threadIdx.x;
@@ -285,6 +288,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         // stage kt (buffer kt % 3): wait for its loads (stage kt + 1's stay in flight),
         // publish it to all wavefronts, multiply while refilling the buffer stage kt - 1 used
         // with stage kt + 2.
+        // the epilogue's bias and routing-weight loads go out now (their latency hides behind
+        // the contraction) and land in LDS after it
+        const int bcol = min(n0 + tid, Nrows - 1);
+        const uint16_t bias_v = tid < kBN ? wbias[static_cast<int64_t>(e) * Nrows + bcol] : 0;
+        const float rw_v = !UP && tid < kBM ? sorted_w[row0 + min(tid, rows - 1)] : 0.f;
         __syncthreads();   // the previous tile's epilogue is done with LDS
         issue(0, 0);
         if (kt_total > 1) issue(1, 1);
@@ -296,6 +304,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             compute(buf, kt, kt + 2 < kt_total, buf2);
             buf = buf == 2 ? 0 : buf + 1;
         }
+        if (tid < kBN) s_bias[tid] = bias_v;
+        if (!UP && tid < kBM) s_rw[tid] = rw_v;
         __syncthreads();   // every wavefront is done with the stage buffers
 
         // --- epilogue. Lane (m, g) of MFMA tile (mt, nt) holds column 16 nt + m of A rows
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
                 const int wr = n0 + 128 * wn + 16 * nt + m;
-                const float bias = wr < Nrows ? bf16_to_f32(wbias[static_cast<int64_t>(e) * Nrows + wr]) : 0.f;
+                const float bias = wr < Nrows ? bf16_to_f32(s_bias[wr - n0]) : 0.f;
                 const int pair = 8 * nt + (m >> 1);
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt) {
@@ -339,28 +349,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
                 }
             }
         } else {
+            // o of the wavefront's 64 rows x 128 columns (bias added, weighted) through LDS
+            // (region `wave`, rows of kOS floats), so that each store writes 16 contiguous
+            // bytes per lane
+            float *s_o = reinterpret_cast<float *>(g_stages) + wave * (64 * kOS);
             float wrow[8][2];
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int lr = 64 * wm + 8 * mt + 2 * g + j;
-                    wrow[mt][j] = lr < rows ? sorted_w[row0 + lr] : 0.f;
+                    wrow[mt][j] = lr < rows ? s_rw[lr] : 0.f;
                 }
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
                 const int d = n0 + 128 * wn + 16 * nt + m;
                 if (d >= Nrows) continue;
-                const float bd = bf16_to_f32(wbias[static_cast<int64_t>(e) * Nrows + d]);
+                const float bd = bf16_to_f32(s_bias[d - n0]);
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        const int lr = 64 * wm + 8 * mt + 2 * g + j;
-                        if (lr >= rows) continue;
                         const float v = acc[mt][nt][2 * j] + acc[mt][nt][2 * j + 1];
-                        o_out[static_cast<int64_t>(row0 + lr) * Nrows + d] = (v + bd) * wrow[mt][j];
+                        s_o[(8 * mt + 2 * g + j) * kOS + 16 * nt + m] = (v + bd) * wrow[mt][j];
                     }
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int it = 0; it < 32; ++it) {
+                const int lrow = 2 * it + (lane >> 5);       // wavefront row
+                const int c4 = 4 * (lane & 31);              // first of 4 columns
+                const int lr = 64 * wm + lrow;               // tile row
+                const int d = n0 + 128 * wn + c4;
+                if (lr < rows && d < Nrows)
+                    *reinterpret_cast<float4 *>(o_out + static_cast<int64_t>(row0 + lr) * Nrows + d) =
+                        *reinterpret_cast<const float4 *>(s_o + lrow * kOS + c4);
             }
         }
     }
