@@ -18,9 +18,10 @@
 //
 // Block tile: BM = 128 activation rows (256 A rows: hi, lo) x BN = 256 output columns; the
 // contraction advances BK = 128 (one MFMA step = four scale blocks) per stage. Four
-// wavefronts, one per SIMD, in a 2 x 2 arrangement: wavefront (wm, wn) owns A rows
-// 128 wm .. 128 wm + 127 and columns 128 wn .. 128 wn + 127, i.e. 8 x 8 MFMA tiles (256
-// accumulators, in the accumulation registers). Operands go from global memory straight into LDS (global_load_lds: each
+// wavefronts, one per SIMD, in a 2 x 2 arrangement: wavefront (wm, wn) owns the 16-row A
+// tiles 2 i + wm (i < 8; interleaved so that the rows of a partly filled tile are shared
+// evenly, and tiles past the expert's rows are skipped) and columns 128 wn .. 128 wn + 127,
+// i.e. 8 x 8 MFMA tiles (256 accumulators, in the accumulation registers). Operands go from global memory straight into LDS (global_load_lds: each
 // lane's 16 or 4 bytes land at the instruction's LDS base + lane * size) into a ring of
 // three stage buffers; a stage's loads are issued two stages before it is multiplied, and
 // one barrier per stage both publishes the stage and retires the buffer the next issue
@@ -44,6 +45,8 @@
 
 namespace moe {
 namespace {
+
+template <int N> struct IntC { static constexpr int value = N; };
 
 constexpr int kBM = 128;                       // activation rows per tile
 constexpr int kAR = 2 * kBM;                   // A rows per tile (hi, lo)
@@ -234,9 +237,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             for (int part = 0; part < 6; ++part) issue_part(part, buf, kt);
         };
 
+        // The tile body, for NL = the wavefront's row tiles that hold valid rows (rounded up
+        // to 2, 4, 6 or 8; a compile-time constant, so that skipped tiles cost no branches
+        // and the accumulators stay in their registers).
+        auto tile_body = [&](auto nl_tag) {
+        constexpr int NL = decltype(nl_tag)::value;
         f32x4 acc[8][8];
 #pragma unroll
-        for (int a = 0; a < 8; ++a)
+        for (int a = 0; a < NL; ++a)
 #pragma unroll
             for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -248,8 +256,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         // are 16 rows apart).
         const uint32_t lb_b = kOffB + 8192 * wn + 64 * m + 16 * (g ^ ((m >> 1) & 3));
         const uint32_t lb_bs = kOffBS + 1024 * wn + 8 * m + (((n0 + 128 * wn + m) * nkb) & 3) + g;
-        const uint32_t lb_a = 16384 * wm + 128 * m + 16 * (g ^ (m & 7));
-        const uint32_t lb_as = kOffAS + 512 * wm + 4 * m + g;
+        const uint32_t lb_a = 2048 * wm + 128 * m + 16 * (g ^ (m & 7));
+        const uint32_t lb_as = kOffAS + 64 * wm + 4 * m + g;
+        // the wavefront's row tiles are the tile's 16-row tiles 2 mt + wm (interleaved, so
+        // that a partly filled tile splits its rows evenly); only the first NL are multiplied
         // In the last stage of a contraction whose block count is not a multiple of 4
         // (vb < 4, a uniform branch), blocks past K get zero A data and unit scales, so they
         // add exactly 0. Stage kt + 2's loads (if any) go out between the row tiles.
@@ -269,18 +279,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             }
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) {
-                uint4 lo16 = *reinterpret_cast<const uint4 *>(base + lb_a + 2048 * mt);
-                uint4 hi16 = *reinterpret_cast<const uint4 *>(base + (lb_a ^ 64u) + 2048 * mt);   // chunk g + 4
-                uint32_t sa = base[lb_as + 64 * mt];
-                if (vb < 4) {
-                    // lane group g carries blocks g / 2 (low half) and 2 + g / 2 (high half)
-                    if ((g >> 1) >= vb) lo16 = zero4();
-                    if (2 + (g >> 1) >= vb) hi16 = zero4();
-                    if (g >= vb) sa = 127u;
-                }
-                const i32x8 af = mx_a_operand(lo16, hi16);
+                if (mt < NL) {
+                    uint4 lo16 = *reinterpret_cast<const uint4 *>(base + lb_a + 4096 * mt);
+                    uint4 hi16 = *reinterpret_cast<const uint4 *>(base + (lb_a ^ 64u) + 4096 * mt);   // chunk g + 4
+                    uint32_t sa = base[lb_as + 128 * mt];
+                    if (vb < 4) {
+                        // lane group g carries blocks g / 2 (low half) and 2 + g / 2 (high half)
+                        if ((g >> 1) >= vb) lo16 = zero4();
+                        if (2 + (g >> 1) >= vb) hi16 = zero4();
+                        if (g >= vb) sa = 127u;
+                    }
+                    const i32x8 af = mx_a_operand(lo16, hi16);
 #pragma unroll
-                for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = mfma_mx(af, bop[nt], acc[mt][nt], sa, sb[nt]);
+                    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = mfma_mx(af, bop[nt], acc[mt][nt], sa, sb[nt]);
+                }
                 if (refill && mt < 6) issue_part(mt, buf2, kt + 2);
             }
         };
@@ -308,9 +320,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         if (!UP && tid < kBM) s_rw[tid] = rw_v;
         __syncthreads();   // every wavefront is done with the stage buffers
 
-        // --- epilogue. Lane (m, g) of MFMA tile (mt, nt) holds column 16 nt + m of A rows
-        // 16 mt + 4g + r: activation row 8 mt + 2g (r = 0, 1: hi, lo) and 8 mt + 2g + 1
-        // (r = 2, 3) of the wavefront's 64; value = D[hi] + D[lo].
+        // --- epilogue. Lane (m, g) of MFMA tile (mt, nt) holds column 16 nt + m of the
+        // wavefront's A rows 16 mt + 4g + r: its activation row 8 mt + 2g (r = 0, 1: hi, lo)
+        // and 8 mt + 2g + 1 (r = 2, 3); value = D[hi] + D[lo]. The wavefront's activation row
+        // r is the tile's row 16 (r / 8) + 8 wm + r % 8.
         if (UP) {
             // h of the wavefront's 64 rows x 64 pairs (fp32) into LDS (region 2 wn + wm of 64 kHS
             // floats), then each lane quantizes two (row, MX block) items
@@ -321,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
                 const float bias = wr < Nrows ? bf16_to_f32(s_bias[wr - n0]) : 0.f;
                 const int pair = 8 * nt + (m >> 1);
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt) {
+                for (int mt = 0; mt < NL; ++mt) {
                     const float v0 = acc[mt][nt][0] + acc[mt][nt][1] + bias;
                     const float v1 = acc[mt][nt][2] + acc[mt][nt][3] + bias;
                     // even lane (gate column) keeps row 8mt + 2g, odd lane (up) row 8mt + 2g + 1
@@ -339,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             for (int q = 0; q < 2; ++q) {
                 const int item = lane + 64 * q;
                 const int r = item >> 1, blk = item & 1;
-                const int R = 64 * wm + r;                        // tile activation row
+                const int R = 16 * (r >> 3) + 8 * wm + (r & 7);   // tile activation row
                 const int ib = (n0 + 128 * wn) / 64 + blk;        // MX block of h
                 if (R < rows && 64 * ib < Nrows) {
                     float v[32];
@@ -355,10 +368,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             float *s_o = reinterpret_cast<float *>(g_stages) + wave * (64 * kOS);
             float wrow[8][2];
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+            for (int mt = 0; mt < NL; ++mt)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const int lr = 64 * wm + 8 * mt + 2 * g + j;
+                    const int lr = 16 * mt + 8 * wm + 2 * g + j;
                     wrow[mt][j] = lr < rows ? s_rw[lr] : 0.f;
                 }
 #pragma unroll
@@ -367,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
                 if (d >= Nrows) continue;
                 const float bd = bf16_to_f32(s_bias[d - n0]);
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt)
+                for (int mt = 0; mt < NL; ++mt)
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         const float v = acc[mt][nt][2 * j] + acc[mt][nt][2 * j + 1];
@@ -379,13 +392,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             for (int it = 0; it < 32; ++it) {
                 const int lrow = 2 * it + (lane >> 5);       // wavefront row
                 const int c4 = 4 * (lane & 31);              // first of 4 columns
-                const int lr = 64 * wm + lrow;               // tile row
+                const int lr = 16 * (lrow >> 3) + 8 * wm + (lrow & 7);   // tile row
                 const int d = n0 + 128 * wn + c4;
                 if (lr < rows && d < Nrows)
                     *reinterpret_cast<float4 *>(o_out + static_cast<int64_t>(row0 + lr) * Nrows + d) =
                         *reinterpret_cast<const float4 *>(s_o + lrow * kOS + c4);
             }
         }
+        };
+        // the wavefront's row tiles holding valid rows (of the (rows + 7) / 8 that do)
+        const int nloc = ((rows + 7) / 8 - wm + 1) / 2;
+        if (nloc > 6) tile_body(IntC<8>{});
+        else if (nloc > 4) tile_body(IntC<6>{});
+        else if (nloc > 2) tile_body(IntC<4>{});
+        else tile_body(IntC<2>{});
     }
 }
 
