@@ -46,15 +46,23 @@ LLC_BYTES = 256 << 20            # MI355X Infinity Cache
 KERNEL_SOURCES = {               # kernel -> files whose text defines it
     "route": ["route.hip", "device_common.h"],
     "permute": ["permute.hip", "device_common.h"],
-    "up_decode": ["gemm_decode.hip", "device_common.h"],
-    "down_decode": ["gemm_decode.hip", "device_common.h"],
-    "up_grouped": ["gemm_grouped.hip", "device_common.h"],
-    "down_grouped": ["gemm_grouped.hip", "device_common.h"],
-    "combine": ["gemm_grouped.hip", "device_common.h"],
+    "logits": ["route.hip", "device_common.h"],
+    "up_decode": ["gemm_decode.hip", "device_common.h", "weight_tiles.h", "routing.h", "topk.h"],
+    "down_decode": ["gemm_decode.hip", "device_common.h", "weight_tiles.h", "routing.h"],
+    "up_stream": ["gemm_stream.hip", "device_common.h", "weight_tiles.h", "routing.h", "lds_dma.h"],
+    "down_stream": ["gemm_stream.hip", "device_common.h", "weight_tiles.h", "routing.h", "lds_dma.h"],
+    "up_grouped": ["gemm_grouped.hip", "device_common.h", "lds_dma.h"],
+    "down_grouped": ["gemm_grouped.hip", "device_common.h", "lds_dma.h"],
+    "combine": ["gemm_grouped.hip", "device_common.h", "lds_dma.h"],
     "combine_decode": ["gemm_decode.hip", "device_common.h"],
 }
-DECODE_STAGES = ["route", "up_decode", "down_decode", "combine_decode"]
+FEW_STAGES = ["logits", "up_decode", "down_decode"]                       # T < 4
+STREAM_STAGES = ["route", "up_stream", "down_stream", "combine_decode"]     # 4 <= T <= 64
 PREFILL_STAGES = ["route", "permute", "up_grouped", "down_grouped", "combine"]
+
+
+def stages_of(T: int):
+    return FEW_STAGES if T < 4 else (STREAM_STAGES if T <= 64 else PREFILL_STAGES)
 
 
 def kernel_source_sha(kernel: str) -> str:
@@ -275,13 +283,16 @@ def kernel_work(wl: Workload, kernel: str, D: float):
     dn_expert = H * (I // 2) + H * (I // 32) + H * 2
     if kernel == "route":
         return T * H * 2 + E * H * 2 + E * 2 + N * 8, 2 * T * E * H
+    if kernel == "logits":
+        return T * H * 2 + E * H * 2 + E * 2 + T * E * 8, 2 * T * E * H
     if kernel == "permute":
         return N * 8 + (E + 1) * 4 + N * 12, 0
-    if kernel == "up_decode":
+    if kernel in ("up_decode", "up_stream"):
         return D * gu_expert + T * H * 2 + N * 8 + N * I * 2, 2 * N * 2 * I * H
-    if kernel == "down_decode":
-        out = T * H * 2 if T <= 16 else N * H * 4          # y directly, or per-slot partials
-        return D * dn_expert + N * I * 2 + N * 8 + out, 2 * N * H * I
+    if kernel == "down_decode":      # y directly
+        return D * dn_expert + N * I * 2 + N * 8 + T * H * 2, 2 * N * H * I
+    if kernel == "down_stream":      # per-slot partial rows
+        return D * dn_expert + N * I * 2 + N * 8 + N * H * 4, 2 * N * H * I
     if kernel == "up_grouped":
         return D * gu_expert + T * H * 2 + N * 4 + N * I * 2, 2 * N * 2 * I * H
     if kernel == "down_grouped":
@@ -336,7 +347,7 @@ def measure(name, steps, warmup, mode, replicas, timed_steps, hip):
     wl = Workload.create(name, replicas)
     ms, wall_ms, steps_run, mode = run_timed(wl, steps, warmup, mode)
     D = distinct_experts(wl)
-    stages = DECODE_STAGES if wl.cfg.T <= 64 else PREFILL_STAGES
+    stages = stages_of(wl.cfg.T)
     kus = run_per_kernel(wl, timed_steps, hip)
     roof, kernels = roofline_for(wl, stages, kus, D)
     layer_bytes = sum(kernel_work(wl, s, D)[0] for s in stages)

@@ -124,9 +124,9 @@ moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape,
  * (timing enabled); launch i records events[2i] and events[2i + 1], so that
  * hipEventElapsedTime(events[2i], events[2i + 1]) is that kernel's duration.
  * *n_launches receives the number of kernels launched. With H <= 4096 and I <= 4096: 3 for
- * T <= 16 (route, up-projection, down-projection with the combine folded in), 4 for
- * 16 < T <= 64 (route, up-projection, down-projection, combine); 5 for T > 64 or a larger H
- * or I (route, permute, up-projection, down-projection, combine). MOE_EINVAL if events, an
+ * T <= 3 (router logits, up-projection with the top-k, down-projection with the combine
+ * folded in), 4 for 4 <= T <= 64 (route, up-projection, down-projection, combine); 5 for
+ * T > 64 or a larger H or I (route, permute, up-projection, down-projection, combine). MOE_EINVAL if events, an
  * events[i] or n_launches is NULL, or n_events is too small.
  */
 moe_status_t moe_mxfp4_forward_timed(const moe_mxfp4_shape_t *shape,

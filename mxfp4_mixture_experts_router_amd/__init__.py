@@ -37,7 +37,8 @@ DECODE_MAX_K = 4096
 
 
 def uses_decode_path(T, H, I):
-    """Whether moe_forward takes the few-token path (3 or 4 launches, no permutation)."""
+    """Whether moe_forward takes the few-token path (3 launches below 4 tokens, 4 from 4 to 64
+    tokens; no permutation)."""
     return T <= DECODE_MAX_T and H <= DECODE_MAX_K and I <= DECODE_MAX_K
 
 MAX_LAUNCHES = 5

@@ -1,6 +1,6 @@
 // C ABI of the MXFP4 mixture-of-experts layer: host-side validation, workspace layout
 // and the launch sequence. No allocation, no synchronisation, no state between calls.
-#include "../../include/moe_mxfp4.h"
+#include "moe_mxfp4.h"
 
 #include <hip/hip_runtime.h>
 
@@ -85,7 +85,7 @@ Layout layout_of(const moe_mxfp4_shape_t *s) {
         L.x8 = p;       p += round_up(moe::mx8_bytes(s->T, s->H));
         L.h8 = p;       p += round_up(moe::mx8_bytes(2 * static_cast<int64_t>(N), s->I));
         L.part = p;
-        if (s->T > moe::kDownTokensMaxT) p += round_up(N * static_cast<size_t>(s->H) * 4);
+        if (s->T >= moe::kStreamMinT) p += round_up(N * static_cast<size_t>(s->H) * 4);
         L.logits = p;   p += round_up(static_cast<size_t>(s->T) * s->E * 8);
         L.offsets = L.sorted_token = L.sorted_w = L.slot_row = L.o = 0;
     } else {
@@ -215,17 +215,18 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
     if (moe::use_decode_path(shape->T, shape->H, shape->I)) {
         float *part = reinterpret_cast<float *>(ws + L.part);
         uint8_t *x8 = ws + L.x8, *h8 = ws + L.h8;
-        // few tokens: logits in a multi-block kernel, top-k + softmax inside the up-projection
-        const bool split_route = shape->T <= moe::kDownTokensMaxT && shape->H <= 6144;
-        double *logits = split_route ? reinterpret_cast<double *>(ws + L.logits) : nullptr;
-        if (split_route)
-            STEP(moe::launch_logits(d, x, router_w, router_b, logits, x8, s), "router logits");
-        else
+        if (shape->T >= moe::kStreamMinT) {
             STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, x8, s), "route");
+            STEP(moe::launch_up_stream(d, x8, gu_blocks, gu_scales, gu_bias, idx, h8, s), "up (stream)");
+            STEP(moe::launch_down_stream(d, h8, dn_blocks, dn_scales, dn_bias, idx, w, part, s), "down (stream)");
+            STEP(moe::launch_combine_decode(d, part, y, s), "combine (decode)");
+            return ok();
+        }
+        // few tokens: logits in a multi-block kernel, top-k + softmax inside the up-projection
+        double *logits = reinterpret_cast<double *>(ws + L.logits);
+        STEP(moe::launch_logits(d, x, router_w, router_b, logits, x8, s), "router logits");
         STEP(moe::launch_up_decode(d, x8, gu_blocks, gu_scales, gu_bias, logits, idx, w, h8, s), "up (decode)");
-        STEP(moe::launch_down_decode(d, h8, dn_blocks, dn_scales, dn_bias, idx, w, part, y, s),
-             "down (decode)");
-        if (shape->T > moe::kDownTokensMaxT) STEP(moe::launch_combine_decode(d, part, y, s), "combine (decode)");
+        STEP(moe::launch_down_decode(d, h8, dn_blocks, dn_scales, dn_bias, idx, w, y, s), "down (decode)");
         return ok();
     }
     uint8_t *x8 = ws + L.x8, *h8 = ws + L.h8;

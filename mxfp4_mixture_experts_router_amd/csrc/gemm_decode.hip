@@ -17,12 +17,13 @@
 #include "device_common.h"
 #include "kernels.h"
 #include "mx_mfma.h"
+#include "routing.h"
+#include "weight_tiles.h"
 #include "topk.h"
 
 namespace moe {
 namespace {
 
-constexpr int kMaxRows = 64;          // = kDecodeMaxT: an expert is chosen at most once per token
 constexpr int kDownScaleLds = 16384;  // LDS bytes for the routed experts' scale rows (few tokens)
 constexpr int kStageLds = 24 * 1024;  // LDS bytes for staged E4M3 activation rows
 
@@ -97,38 +98,6 @@ __device__ __forceinline__ void load_routing(const double *logits, int32_t *topk
     __syncthreads();
 }
 
-// The slot-th routed expert in increasing index order (-1 if fewer), computed by every
-// thread from the bitmap.
-__device__ int expert_of_slot(const uint32_t *bitmap, int slot) {
-    int rem = slot;
-#pragma unroll
-    for (int w = 0; w < kMaxE / 32; ++w) {
-        uint32_t bits = bitmap[w];
-        const int c = __popc(bits);
-        if (rem < c) {
-            for (int q = 0; q < rem; ++q) bits &= bits - 1u;
-            return 32 * w + __ffs(bits) - 1;
-        }
-        rem -= c;
-    }
-    return -1;
-}
-
-// Routed pairs n = t*k + j of expert e in increasing n, by wavefront 0 (caller syncs).
-__device__ void rows_of_expert(const int *s_idx, int N, int e, int *s_rows, int *s_nrows) {
-    const int lane = threadIdx.x % kWave;
-    int cnt = 0;
-    for (int base = 0; base < N; base += kWave) {
-        const int n = base + lane;
-        const bool hit = n < N && s_idx[n] == e;
-        const uint64_t m = __ballot(hit);
-        const int pos = cnt + __popcll(m & lanemask_lt());
-        if (hit && pos < kMaxRows) s_rows[pos] = n;
-        cnt += __popcll(m);
-    }
-    if (lane == 0) *s_nrows = cnt < kMaxRows ? cnt : kMaxRows;
-}
-
 // Copy `bytes` contiguous bytes (a multiple of 16) into LDS; each thread issues up to 4
 // loads before its first LDS store (clamped slots reload and rewrite the last piece).
 __device__ __forceinline__ void stage_bytes(uint8_t *dst, const uint8_t *src, int bytes) {
@@ -145,38 +114,6 @@ __device__ __forceinline__ void stage_bytes(uint8_t *dst, const uint8_t *src, in
         st(q2, v2);
         st(q3, v3);
     }
-}
-
-// ---------------------------------------------------------------------------------------
-// Packed-weight tiles. A 16-row tile of a weight matrix (rows of K/2 bytes, one 16-byte
-// block per 32 contraction entries) is read in chunks of 256 contraction entries (8
-// blocks). Each of the two 16-byte loads per lane covers 8 rows x 128 contiguous bytes, so
-// every load instruction touches whole cache lines: lane l loads block 8c + l/8 of row l%8
-// (first) and of row 8 + l%8 (second).
-__device__ __forceinline__ void load_tile_chunk(const uint8_t *rows, int64_t row_bytes, int c, int nblocks,
-                                                int lane, uint4 &first, uint4 &second) {
-    const int kb = min(8 * c + (lane >> 3), nblocks - 1);   // clamped: the tail re-reads a real block
-    const uint8_t *p = rows + (lane & 7) * row_bytes + kb * 16;
-    first = *reinterpret_cast<const uint4 *>(p);
-    second = *reinterpret_cast<const uint4 *>(p + 8 * row_bytes);
-}
-
-__device__ __forceinline__ uint32_t ror8_in_row(uint32_t v) {   // DPP row_ror:8 (lane n <-> n ^ 8)
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xf, 0xf, false));
-}
-
-// Afterwards lane (n = l%16, g = l/16) holds blocks 8c + 2g (lo) and 8c + 2g + 1 (hi) of
-// row n. Lanes n < 8 loaded (row n, block 8c + 2g) and lanes n >= 8 (row n, block 8c + 2g +
-// 1) themselves; the other halves are exchanged between lanes n and n ^ 8 by one rotation
-// within each 16-lane row.
-__device__ __forceinline__ void tile_chunk_to_mfma(const uint4 &first, const uint4 &second, int lane, uint4 &lo,
-                                                   uint4 &hi) {
-    const bool low = (lane & 15) < 8;
-    const uint4 send = low ? second : first;
-    const uint4 recv = make_uint4(ror8_in_row(send.x), ror8_in_row(send.y), ror8_in_row(send.z),
-                                  ror8_in_row(send.w));
-    lo = low ? first : recv;
-    hi = low ? recv : second;
 }
 
 // One block-scaled MFMA over the blocks 8c + 2v + h (v = 0..3) of chunk c, h = 0 or 1: B is
@@ -555,112 +492,6 @@ __global__ __launch_bounds__(NW * 64) void k_down_mx_tokens(
     }
 }
 
-// ---------------------------------------------------------------------------------------
-// Down-projection for more tokens: block = (routing slot, one 16-row tile of output
-// features); 4 wavefronts split the contraction in 256-wide chunks.
-// part[n, d] = h[n] . Wdn[e, d] + w[n] * bdn[e, d] for the pairs n routed to e (A rows
-// 4s .. 4s + 3 = h8 rows 4n .. 4n + 3 of the expert's s-th pair; block y takes pairs
-// 4 NMT y ..); a separate combine sums part over the k slots of each token.
-template <int NMT, int UB>
-__global__ __launch_bounds__(256) void k_down_mx_slots(
-    const uint8_t *__restrict__ h8, const uint8_t *__restrict__ hs8, const uint8_t *__restrict__ dn_blocks,
-    const uint8_t *__restrict__ dn_scales, const uint16_t *__restrict__ dn_bias,
-    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int T, int H, int I,
-    int E, int k, float *__restrict__ part) {
-    __shared__ uint32_t bitmap[kMaxE / 32];
-    __shared__ int s_idx[kMaxRows * 8];
-    __shared__ float s_w[kMaxRows * 8];
-    __shared__ int s_rows[kMaxRows];
-    __shared__ int s_nrows;
-    __shared__ float red[4][NMT * 4][kWave];
-    __shared__ __attribute__((aligned(16))) uint8_t s_sc[16 * kMaxScaleCols];   // 16 rows x I/32
-
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int col = lane & 15, g = lane >> 4;
-    const int tiles_d = H / 16;
-    const int N = T * k;
-    const int shs = mx8_scale_stride(I);
-    load_routing<false>(nullptr, topk_idx, topk_w, T, E, k, s_idx, s_w, bitmap, [] {});
-    const int e = expert_of_slot(bitmap, blockIdx.x / tiles_d);
-    if (e < 0) return;
-    const int64_t row0 = static_cast<int64_t>(e) * H + (blockIdx.x % tiles_d) * 16;
-    const int d = (blockIdx.x % tiles_d) * 16 + col;
-    const int is = I / 32;
-    const int nblocks = I / 32;
-    const int nchunks = (nblocks + 7) / 8;
-    // the tile's 16 rows of scales: I/2 contiguous bytes, loaded before the weight stream
-    const uint4 scv = tid < I / 32 ? *reinterpret_cast<const uint4 *>(dn_scales + row0 * is + 16 * tid) : zero4();
-    const uint8_t *wrows = dn_blocks + row0 * (I / 2);
-    uint4 wf[UB], ws[UB];
-    auto load_batch = [&](int c0) {
-#pragma unroll
-        for (int u = 0; u < UB; ++u)
-            load_tile_chunk(wrows, I / 2, min(c0 + 4 * u, nchunks - 1), nblocks, lane, wf[u], ws[u]);
-    };
-    load_batch(wave);
-    if (tid < I / 32) *reinterpret_cast<uint4 *>(s_sc + 16 * tid) = scv;
-    const float bd = bf16_to_f32(dn_bias[static_cast<int64_t>(e) * H + d]);
-    if (wave == 0) rows_of_expert(s_idx, N, e, s_rows, &s_nrows);
-    __syncthreads();
-    const int s0 = 4 * NMT * blockIdx.y;
-    const int nrows = s_nrows - s0;
-    if (nrows <= 0) return;                    // uniform
-    // A row r = 16 mt + col: the expert's pair s0 + r / 4, h8 row 4n + r % 4
-    const uint8_t *arow[NMT];
-    const uint8_t *asc[NMT];
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-        const int r = 16 * mt + col;
-        arow[mt] = nullptr;
-        asc[mt] = nullptr;
-        if ((r >> 2) < nrows) {
-            const int64_t hr = 4 * static_cast<int64_t>(s_rows[s0 + (r >> 2)]) + (r & 3);
-            arow[mt] = h8 + hr * I;
-            asc[mt] = hs8 + hr * shs;
-        }
-    }
-    f32x4 acc[NMT];
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c0 = wave; c0 < nchunks; c0 += 4 * UB) {
-        if (c0 != wave) load_batch(c0);
-#pragma unroll
-        for (int u = 0; u < UB; ++u) {
-            const int c = c0 + 4 * u;
-            if (c >= nchunks) break;   // uniform
-            uint4 lo, hi;
-            tile_chunk_to_mfma(wf[u], ws[u], lane, lo, hi);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint32_t sb = s_sc[col * is + min(8 * c + 2 * g + h, nblocks - 1)];
-                const i32x8 bop = mx_b_operand(h ? hi : lo);
-#pragma unroll
-                for (int mt = 0; mt < NMT; ++mt)
-                    if (16 * mt < 4 * nrows) acc[mt] = mx_step(acc[mt], arow[mt], asc[mt], bop, sb, c, h, g, nblocks);
-            }
-        }
-    }
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][mt * 4 + r][lane] = acc[mt][r];
-    __syncthreads();
-    if (wave != 0) return;
-    // D rows 16mt + 4g + r: pair 4mt + g, its four A rows r
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-        const int s = 4 * mt + g;
-        if (s < nrows) {
-            float v = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                v += (red[w][mt * 4][lane] + red[w][mt * 4 + 1][lane]) + (red[w][mt * 4 + 2][lane] + red[w][mt * 4 + 3][lane]);
-            const int n = s_rows[s0 + s];
-            part[static_cast<int64_t>(n) * H + d] = v + s_w[n] * bd;
-        }
-    }
-}
-
 // y[t, d] = bf16(sum_{j < k} part[t*k + j, d]) in slot order. Thread = 4 features.
 __global__ __launch_bounds__(256) void k_combine_slots(const float *__restrict__ part, int T, int H,
                                                        int k, uint16_t *__restrict__ y) {
@@ -693,16 +524,6 @@ hipError_t up_n(const Dims &d, const uint8_t *x8, const uint8_t *xs8, const uint
     return hipGetLastError();
 }
 
-template <int NMT, int UB>
-hipError_t down_slots_n(const Dims &d, const uint8_t *h8, const uint8_t *hs8, const uint8_t *db, const uint8_t *ds,
-                        const uint16_t *dbias, int32_t *idx, float *w, float *part, hipStream_t s) {
-    const unsigned blocks = static_cast<unsigned>(slots_of(d) * (d.H / 16));
-    const unsigned groups = static_cast<unsigned>((d.T + 4 * NMT - 1) / (4 * NMT));
-    MOE_LAUNCH((k_down_mx_slots<NMT, UB>), dim3(blocks, groups), dim3(256), 0, s, h8, hs8, db, ds, dbias, idx, w,
-                       static_cast<int>(d.T), d.H, d.I, d.E, d.k, part);
-    return hipGetLastError();
-}
-
 template <int NMT, int NW, int UB, bool LDS_A, bool SC_LDS>
 hipError_t down_tokens_n(const Dims &d, const uint8_t *h8, const uint8_t *hs8, const uint8_t *db, const uint8_t *ds,
                          const uint16_t *dbias, int32_t *idx, float *w, uint16_t *y, hipStream_t s) {
@@ -727,46 +548,29 @@ hipError_t launch_combine_decode(const Dims &d, const float *part, uint16_t *y, 
 hipError_t launch_up_decode(const Dims &d, const uint8_t *x8, const uint8_t *gu_blocks,
                             const uint8_t *gu_scales, const uint16_t *gu_bias, const double *logits,
                             int32_t *topk_idx, float *topk_w, uint8_t *h8, hipStream_t s) {
+    if (d.T >= kStreamMinT || logits == nullptr) return hipErrorInvalidValue;
     const uint8_t *xs8 = x8 + static_cast<size_t>(2 * d.T) * d.H;
     uint8_t *hs8 = h8 + static_cast<size_t>(4 * d.T * d.k) * d.I;   // h8: mx8 matrix of 2 T k rows
-    const bool lds_a = mx8_bytes(d.T, d.H) <= static_cast<size_t>(kStageLds);
-    // A rows: 2 per routed pair of the expert, at most 2T
-    const int nmt = static_cast<int>((2 * d.T + 15) / 16);
-    if (logits != nullptr) {   // T <= kDownTokensMaxT: top-k in the prologue
-        if (nmt == 1)
-            return lds_a ? up_n<1, 6, true, true>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, h8, hs8, s)
-                         : up_n<1, 6, false, true>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, h8, hs8, s);
-        return up_n<2, 6, false, true>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, h8, hs8, s);
-    }
-    switch (nmt) {
-        case 1: return up_n<1, 6, false, false>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, nullptr, topk_idx, topk_w, h8, hs8, s);
-        case 2: return up_n<2, 6, false, false>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, nullptr, topk_idx, topk_w, h8, hs8, s);
-        default: return up_n<4, 4, false, false>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, nullptr, topk_idx, topk_w, h8, hs8, s);
-    }
+    // the token rows (2T of H bytes) are staged in LDS when they fit
+    if (mx8_bytes(d.T, d.H) <= static_cast<size_t>(kStageLds))
+        return up_n<1, 6, true, true>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, h8, hs8, s);
+    return up_n<1, 6, false, true>(d, x8, xs8, gu_blocks, gu_scales, gu_bias, logits, topk_idx, topk_w, h8, hs8, s);
 }
 
 hipError_t launch_down_decode(const Dims &d, const uint8_t *h8, const uint8_t *dn_blocks,
                               const uint8_t *dn_scales, const uint16_t *dn_bias, int32_t *topk_idx,
-                              float *topk_w, float *part, uint16_t *y, hipStream_t s) {
+                              float *topk_w, uint16_t *y, hipStream_t s) {
+    if (d.T >= kStreamMinT) return hipErrorInvalidValue;
     const int64_t N = d.T * d.k;
     const uint8_t *hs8 = h8 + static_cast<size_t>(4 * N) * d.I;   // h8: mx8 matrix of 2N rows
-    if (d.T <= kDownTokensMaxT) {
-        // weight scale rows of every routed expert: at most min(T*k, E) experts x 16 rows x I/32 bytes
-        const bool sc_lds = static_cast<int64_t>(slots_of(d)) * (d.I / 2) <= kDownScaleLds;
-        const bool lds_a = mx8_bytes(2 * N, d.I) <= static_cast<size_t>(kStageLds);
-        if (d.T <= 4) {
-            if (lds_a && sc_lds)
-                return down_tokens_n<1, 16, 3, true, true>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
-            if (sc_lds)
-                return down_tokens_n<1, 16, 3, false, true>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
-            return down_tokens_n<1, 16, 3, false, false>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
-        }
-        if (d.T <= 8)
-            return down_tokens_n<2, 8, 6, false, false>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
-        return down_tokens_n<4, 8, 4, false, false>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
-    }
-    // pairs of one expert: at most T; blocks of 16 pairs (4 m-tiles of 4 A rows each) along y
-    return down_slots_n<4, 3>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, part, s);
+    // weight scale rows of every routed expert: at most min(T*k, E) experts x 16 rows x I/32 bytes
+    const bool sc_lds = static_cast<int64_t>(slots_of(d)) * (d.I / 2) <= kDownScaleLds;
+    const bool lds_a = mx8_bytes(2 * N, d.I) <= static_cast<size_t>(kStageLds);
+    if (lds_a && sc_lds)
+        return down_tokens_n<1, 16, 3, true, true>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
+    if (sc_lds)
+        return down_tokens_n<1, 16, 3, false, true>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
+    return down_tokens_n<1, 16, 3, false, false>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
 }
 
 }  // namespace moe

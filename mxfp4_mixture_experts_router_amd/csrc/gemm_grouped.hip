@@ -39,6 +39,7 @@
 //       stage's four scale bytes (weight scale rows are K / 32 bytes long, not 4-aligned).
 #include "device_common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 #include "mx_mfma.h"
 
 
@@ -63,32 +64,6 @@ constexpr int kHS = 67;                        // up epilogue: padded row of 64 
 constexpr int kOS = 132;                       // down epilogue: padded row of 128 fp32 outputs
 
 __shared__ __attribute__((aligned(16))) uint8_t g_stages[3 * kStage];
-
-// global_load_lds (saddr form): lane l's 16 (or 4) bytes at base + voff land at LDS byte
-// address lds + 16 l (4 l). base and lds are wavefront-uniform. M0 is set in the same
-// statement; nothing else in these kernels keeps a value in M0.
-__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const uint8_t *base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
-                 : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N) (N <= 63), other counters untouched; the empty asm statements keep the
-// compiler from moving memory accesses across it.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-    asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void barrier_only() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 template <bool UP>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(

@@ -23,8 +23,8 @@ inline LaunchEvents &launch_events() {
     hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ::moe::launch_events().start,   \
                           ::moe::launch_events().stop, 0, __VA_ARGS__)
 
-// Token count up to which the forward pass takes the decode path (route -> fused
-// up-projection -> fused down-projection + combine, no sorted permutation in memory).
+// Token count up to which the forward pass takes the decode path (per-expert work found
+// inside the expert kernels, no sorted permutation in memory).
 constexpr int64_t kDecodeMaxT = 64;
 // Largest H and I the decode kernels take (their scale rows are staged in LDS, 128 bytes per
 // row); larger shapes take the grouped path at any token count.
@@ -71,27 +71,37 @@ hipError_t launch_down_grouped(const Dims &d, const uint8_t *h8, const uint8_t *
 hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row,
                           uint16_t *y, hipStream_t s);
 
-// Decode path (T <= kDecodeMaxT).
-// Tokens up to which the down-projection keeps all routed experts of a feature tile in one
-// workgroup and writes y directly (beyond: per-slot partial sums + a combine kernel).
-constexpr int64_t kDownTokensMaxT = 16;
+// Decode path (T <= kDecodeMaxT). Below kStreamMinT tokens: router logits (launch_logits),
+// then an up-projection that also takes the top-k, then a down-projection that also adds
+// the k slots; from kStreamMinT tokens: launch_route, the weight-streaming projections and
+// a combine.
+constexpr int64_t kStreamMinT = 4;
 
-// up: h[t*k + j, :] = w[t, j] * swiglu(x[t] . Wgu[e_tj]^T + bgu[e_tj]) as the mx8 matrix h8
-// of 2 T k rows of I (row 2n + half: one 16-value half of every MX block of h[n], zeros in
-// the other), from the mx8 matrix x8 (T rows of H). With `logits` (double [T, E],
-// T <= kDownTokensMaxT) every block computes the top-k + softmax itself and block 0 writes
-// it to topk_idx / topk_w; with logits == nullptr they are inputs.
+// up (T < kStreamMinT): h[t*k + j, :] = w[t, j] * swiglu(x[t] . Wgu[e_tj]^T + bgu[e_tj]) as the
+// mx8 matrix h8 of 2 T k rows of I (row 2n + half: one 16-value half of every MX block of
+// h[n], zeros in the other), from the mx8 matrix x8 (T rows of H). Every block computes the
+// top-k + softmax of `logits` (double [T, E]) itself; block 0 writes it to topk_idx / topk_w.
 hipError_t launch_up_decode(const Dims &d, const uint8_t *x8, const uint8_t *gu_blocks,
                             const uint8_t *gu_scales, const uint16_t *gu_bias, const double *logits,
                             int32_t *topk_idx, float *topk_w, uint8_t *h8, hipStream_t s);
-// down: T <= kDownTokensMaxT: y[t, :] = bf16(sum_j h[t*k + j] . Wdn[e_tj]^T + w[t, j] * bdn[e_tj]);
-// otherwise part[t*k + j, :] = h[t*k + j] . Wdn[e_tj]^T + w[t, j] * bdn[e_tj] (fp32, [T*k, H])
-// and launch_combine_decode forms y.
+// down (T < kStreamMinT): y[t, :] = bf16(sum_j h[t*k + j] . Wdn[e_tj]^T + w[t, j] * bdn[e_tj]).
 hipError_t launch_down_decode(const Dims &d, const uint8_t *h8, const uint8_t *dn_blocks,
                               const uint8_t *dn_scales, const uint16_t *dn_bias, int32_t *topk_idx,
-                              float *topk_w, float *part, uint16_t *y, hipStream_t s);
+                              float *topk_w, uint16_t *y, hipStream_t s);
 // y[t, :] = bf16(sum_{j < k} part[t*k + j, :]), slot order.
 hipError_t launch_combine_decode(const Dims &d, const float *part, uint16_t *y, hipStream_t s);
+
+// Batched decode (kStreamMinT <= T <= kDecodeMaxT): the routed experts' weights streamed
+// once, routing (topk_idx / topk_w) from launch_route.
+// up: h[n, :] = swiglu(x[t] . Wgu[e_n]^T + bgu[e_n]) for every pair n = t*k + j, as the plain
+// mx8 matrix h8 of T k rows of I.
+hipError_t launch_up_stream(const Dims &d, const uint8_t *x8, const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                            const uint16_t *gu_bias, const int32_t *topk_idx, uint8_t *h8, hipStream_t s);
+// down: part[n, :] = w[n] * (h[n] . Wdn[e_n]^T + bdn[e_n]) (fp32 [T k, H]); launch_combine_decode
+// then forms y.
+hipError_t launch_down_stream(const Dims &d, const uint8_t *h8, const uint8_t *dn_blocks, const uint8_t *dn_scales,
+                              const uint16_t *dn_bias, const int32_t *topk_idx, const float *topk_w, float *part,
+                              hipStream_t s);
 
 // bf16 [rows, cols] -> mx8 matrix (mx_mfma.h).
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int cols, uint8_t *q8, hipStream_t s);

@@ -8,6 +8,7 @@
 // of earlier pairs (smaller n) routed to the same expert.
 #include "device_common.h"
 #include "kernels.h"
+#include "routing.h"
 
 namespace moe {
 namespace {
@@ -41,18 +42,6 @@ __device__ void wave_exclusive_scan(const int *cnt, int *out, int E, int lane) {
         run += v[c];
     }
     if (lane == kWave - 1) out[E] = incl;   // total
-}
-
-// Lanes of the wavefront whose expert equals this lane's (E <= 256: eight bit ballots).
-__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool valid) {
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t m = __ballot(bit);
-        peers &= bit ? m : ~m;
-    }
-    return peers;
 }
 
 // Wavefront w owns the contiguous pairs [w * per, (w + 1) * per) and walks them 64 at a

@@ -233,8 +233,10 @@ FORWARD_CASES = [
     ("tiny", 65, 96, 64, 5, 2, 65),         # non-square, smallest prefill batch
     ("tiny", 300, 64, 128, 3, 2, 300),      # few experts: several ragged m-tiles each
     ("tiny", 17, 64, 64, 256, 8, 17),       # maximal E and k, decode path
+    ("tiny", 5, 96, 64, 5, 2, 5),           # non-square, batched decode: a partly filled 64-row tile
     ("tiny", 140, 64, 64, 256, 8, 140),     # maximal E and k, prefill path
     ("decode_20b", None, None, None, None, None, 1),
+    ("decode_20b", 2, None, None, None, None, 2),
     ("batched_decode_20b", None, None, None, None, None, 64),
     ("prefill_20b", None, None, None, None, None, 24),
     ("prefill_120b", None, None, None, None, None, 24),
@@ -326,7 +328,7 @@ class _HipEvents:
             self.lib.hipEventDestroy(self.c.c_void_p(ev))
 
 
-@pytest.mark.parametrize("T,launches", [(1, 3), (17, 4), (65, 5)])
+@pytest.mark.parametrize("T,launches", [(1, 3), (3, 3), (4, 4), (17, 4), (65, 5)])
 def test_forward_timed_matches_forward(T, launches):
     import ctypes
     cfg = CONFIGS["tiny"]

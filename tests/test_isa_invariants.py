@@ -1,0 +1,57 @@
+"""Properties of the compiled gfx950 code that the kernels' correctness rests on (CPU only:
+hipcc cross-compiles the device code to assembly here).
+
+The weight-streaming kernels copy the activation rows into LDS with global_load_lds and
+then wait for those copies with s_waitcnt vmcnt(9 + 2 * 12): the copies are older than exactly
+that many vector-memory loads (8 weight-scale dwords, the bias, 24 weight loads). If the
+compiler merged, dropped or moved one of those loads, the wait would end before the copies
+had landed. This test reads the generated assembly and counts.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mxfp4_mixture_experts_router_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def _device_asm(src: str, tmp_path) -> str:
+    if not (os.path.exists(HIPCC) or shutil.which("hipcc")):
+        pytest.skip("hipcc not available")
+    out = tmp_path / "dev.s"
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+def _kernels(asm: str, name: str):
+    """(symbol, body lines) of every kernel whose mangled name contains `name`."""
+    res = []
+    for m in re.finditer(r"^(_Z\S*" + name + r"\S*):", asm, re.M):
+        body = asm[m.end():]
+        end = body.find("s_endpgm")
+        res.append((m.group(1), body[:end].split("\n")))
+    return res
+
+
+def test_stream_copies_wait_counts_the_younger_loads(tmp_path):
+    asm = _device_asm("gemm_stream.hip", tmp_path)
+    kernels = _kernels(asm, "k_stream")
+    assert len(kernels) == 2   # up and down
+    load = re.compile(r"^\s*(global_load|buffer_load|flat_load)\w*\s")
+    for sym, lines in kernels:
+        waits = [i for i, l in enumerate(lines) if re.search(r"s_waitcnt\s+vmcnt\(33\)", l)]
+        assert len(waits) == 1, sym
+        w = waits[0]
+        copies = [i for i in range(w) if "global_load_lds" in lines[i]]
+        assert copies, sym
+        younger = [lines[i] for i in range(copies[-1] + 1, w)
+                   if load.match(lines[i]) and "global_load_lds" not in lines[i]]
+        assert len(younger) == 33, (sym, len(younger))
