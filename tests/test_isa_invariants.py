@@ -2,8 +2,8 @@
 hipcc cross-compiles the device code to assembly here).
 
 The weight-streaming kernels copy the activation rows into LDS with global_load_lds and
-then wait for those copies with s_waitcnt vmcnt(9 + 2 * 12): the copies are older than exactly
-that many vector-memory loads (8 weight-scale dwords, the bias, 24 weight loads). If the
+then wait for those copies with s_waitcnt vmcnt(9 + 2 * kUB): the copies are older than exactly
+that many vector-memory loads (8 weight-scale dwords, the bias, 2 kUB weight loads). If the
 compiler merged, dropped or moved one of those loads, the wait would end before the copies
 had landed. This test reads the generated assembly and counts.
 """
@@ -42,16 +42,19 @@ def _kernels(asm: str, name: str):
 
 
 def test_stream_copies_wait_counts_the_younger_loads(tmp_path):
+    src = open(os.path.join(CSRC, "gemm_stream.hip")).read()
+    ub = int(re.search(r"constexpr int kUB = (\d+);", src).group(1))
+    younger_expected = 9 + 2 * ub
     asm = _device_asm("gemm_stream.hip", tmp_path)
     kernels = _kernels(asm, "k_stream")
     assert len(kernels) == 2   # up and down
     load = re.compile(r"^\s*(global_load|buffer_load|flat_load)\w*\s")
     for sym, lines in kernels:
-        waits = [i for i, l in enumerate(lines) if re.search(r"s_waitcnt\s+vmcnt\(33\)", l)]
+        waits = [i for i, l in enumerate(lines) if re.search(r"s_waitcnt\s+vmcnt\(%d\)" % younger_expected, l)]
         assert len(waits) == 1, sym
         w = waits[0]
         copies = [i for i in range(w) if "global_load_lds" in lines[i]]
         assert copies, sym
         younger = [lines[i] for i in range(copies[-1] + 1, w)
                    if load.match(lines[i]) and "global_load_lds" not in lines[i]]
-        assert len(younger) == 33, (sym, len(younger))
+        assert len(younger) == younger_expected, (sym, len(younger))
