@@ -2,8 +2,9 @@
 hipcc cross-compiles the device code to assembly here).
 
 The weight-streaming kernels copy the activation rows into LDS with global_load_lds and
-then wait for those copies with s_waitcnt vmcnt(9 + 2 * kUB): the copies are older than exactly
-that many vector-memory loads (8 weight-scale dwords, the bias, 2 kUB weight loads). If the
+then wait for those copies with s_waitcnt vmcnt(9 + 2 * kUB (+ the next item's copies, issued
+first)): the copies are older than exactly that many vector-memory loads (8 weight-scale
+dwords, the bias, 2 kUB weight loads). If the
 compiler merged, dropped or moved one of those loads, the wait would end before the copies
 had landed. This test reads the generated assembly and counts.
 """
@@ -50,11 +51,16 @@ def test_stream_copies_wait_counts_the_younger_loads(tmp_path):
     assert len(kernels) == 2   # up and down
     load = re.compile(r"^\s*(global_load|buffer_load|flat_load)\w*\s")
     for sym, lines in kernels:
-        waits = [i for i, l in enumerate(lines) if re.search(r"s_waitcnt\s+vmcnt\(%d\)" % younger_expected, l)]
-        assert len(waits) == 1, sym
-        w = waits[0]
-        copies = [i for i in range(w) if "global_load_lds" in lines[i]]
-        assert copies, sym
-        younger = [lines[i] for i in range(copies[-1] + 1, w)
-                   if load.match(lines[i]) and "global_load_lds" not in lines[i]]
-        assert len(younger) == younger_expected, (sym, len(younger))
+        # the wait may also allow for the next item's copies (issued before the loads): any
+        # vmcnt(n) with n in [younger, younger + 9] must follow the copies by exactly
+        # `younger` loads
+        pat = re.compile(r"s_waitcnt\s+vmcnt\((\d+)\)")
+        waits = [i for i, l in enumerate(lines)
+                 if pat.search(l) and younger_expected <= int(pat.search(l).group(1)) <= younger_expected + 9]
+        assert waits, sym
+        for w in waits:
+            copies = [i for i in range(w) if "global_load_lds" in lines[i]]
+            assert copies, sym
+            younger = [lines[i] for i in range(copies[-1] + 1, w)
+                       if load.match(lines[i]) and "global_load_lds" not in lines[i]]
+            assert len(younger) == younger_expected, (sym, w, len(younger))
