@@ -69,6 +69,11 @@ def _load():
     lib.oracle_expert.argtypes = [_u16, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   _u8, _u8, _u16, _u8, _u8, _u16,
                                   ctypes.c_double, ctypes.c_double, _f64_or_null, _f64]
+    lib.oracle_bf16_round.restype = ctypes.c_uint16
+    lib.oracle_bf16_round.argtypes = [ctypes.c_double]
+    lib.oracle_rmsnorm.restype = None
+    lib.oracle_rmsnorm.argtypes = [_u16, _u16, ctypes.c_int64, ctypes.c_int, ctypes.c_double, _u16,
+                                   _f64_or_null]
     lib.oracle_forward_tokens.restype = None
     lib.oracle_forward_tokens.argtypes = [
         _i64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -113,6 +118,23 @@ def dequant(blocks: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return out
 
 
+def bf16_round(v: float) -> int:
+    """The bf16 bit pattern nearest to ``v`` (ties to even)."""
+    return int(_load().oracle_bf16_round(float(v)))
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float = 1e-5, with_exact: bool = False):
+    """Pre-LN RMSNorm of bf16 rows ``x [T, H]`` with bf16 weights ``gamma [H]``: bf16 bit
+    patterns ``[T, H]`` (and the values before rounding, when ``with_exact``)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+    T, H = x.shape
+    xn = np.empty((T, H), dtype=np.uint16)
+    exact = np.empty((T, H), dtype=np.float64) if with_exact else None
+    _load().oracle_rmsnorm(x, gamma, T, H, float(eps), xn, _ptr(exact))
+    return (xn, exact) if with_exact else xn
+
+
 def router(x, router_w, router_b, with_abs_sum: bool = False):
     T, H = x.shape
     E = router_w.shape[0]
@@ -142,6 +164,21 @@ def expert(x_row, e: int, inp: Dict[str, np.ndarray], alpha=1.702, limit=7.0):
                           inp["gu_scales"], inp["gu_bias"], inp["dn_blocks"], inp["dn_scales"],
                           inp["dn_bias"], float(alpha), float(limit), _ptr(h), o)
     return h, o
+
+
+def forward_prenorm(inp: Dict[str, np.ndarray], k: int, tokens: Optional[Sequence[int]] = None,
+                    alpha: float = 1.702, limit: float = 7.0, eps: float = 1e-5,
+                    intermediates: bool = False):
+    """The Pre-LN block around the layer: ``y = x + layer(rmsnorm(x))`` (MLX README,
+    "Architecture Details"; ZM "API" norm_eps). Same outputs as ``forward``, plus ``xn``
+    (the normalized rows, bf16 bits, of the listed tokens); ``y`` includes the residual."""
+    xn = rmsnorm(inp["x"], inp["norm_w"], eps)
+    out = forward(dict(inp, x=xn), k, tokens=tokens, alpha=alpha, limit=limit,
+                  intermediates=intermediates)
+    x_tok = np.ascontiguousarray(inp["x"][out["tokens"]], dtype=np.uint16)
+    out["y"] = out["y"] + (x_tok.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    out["xn"] = xn[out["tokens"]]
+    return out
 
 
 def forward(inp: Dict[str, np.ndarray], k: int, tokens: Optional[Sequence[int]] = None,

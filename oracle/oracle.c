@@ -27,6 +27,10 @@
  *        maybe_modify_loaded_hf_weight (MXFP4-dequantized down_proj is
  *        [E, hidden, intermediate]; gate_up is [E, 2*intermediate, hidden])
  *        and GPTOSSMLPGateUpProjMapping (alternating row interleaving).
+ *  [MLX] "GPT-OSS MLX Implementation" README, "Architecture Details":
+ *        RMSNorm with Pre-LN placement (the layer's input is normalized, the
+ *        block adds the layer's output to its un-normalized input); [ZM] "API"
+ *        table: norm_eps 1e-5.
  *  [OCP] OCP Microscaling Formats (MX) v1.0 specification, the FP4 E2M1
  *        element type and the E8M0 shared scale (outside the pages; the pages
  *        name the format only).
@@ -120,6 +124,59 @@ ORACLE_API double oracle_swiglu(double gate, double up, double alpha, double lim
     double u = up < -limit ? -limit : (up > limit ? limit : up);
     double sigmoid = 1.0 / (1.0 + exp(-alpha * g));
     return (u + 1.0) * g * sigmoid;
+}
+
+/*
+ * Round a double to the nearest bf16 value, ties to even (finite, normal-range
+ * inputs): with q the power of two of v's leading bit, bf16 keeps 8 significant
+ * bits, so the value is rint(v / (q / 128)) * (q / 128); rint rounds ties to
+ * even in the default rounding mode. Returns the bf16 bit pattern.
+ */
+static uint16_t bf16_round(double v)
+{
+    if (v == 0.0)
+        return signbit(v) ? 0x8000u : 0u;
+    int e;
+    frexp(v, &e);                          /* |v| = f 2^e, 0.5 <= f < 1: leading bit 2^(e-1) */
+    const double ulp = ldexp(1.0, e - 8);   /* 8 significant bits */
+    const double r = rint(v / ulp) * ulp;
+    const float f = (float)r;               /* exact: r has 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+ORACLE_API uint16_t oracle_bf16_round(double v)
+{
+    return bf16_round(v);
+}
+
+/*
+ * [MLX] Pre-LN RMSNorm of the layer input, [ZM] epsilon: per token,
+ *   ms = (sum_h x[t, h]^2) / H,  r = 1 / sqrt(ms + eps),
+ *   xn[t, h] = bf16(x[t, h] * r * gamma[h])   (products left to right, one rounding to
+ *                                               bf16 at the end, ties to even).
+ * The normalized rows are bf16 like every activation the layer takes. `exact`
+ * (optional) receives x * r * gamma before that rounding.
+ */
+ORACLE_API void oracle_rmsnorm(const uint16_t *x, const uint16_t *gamma, int64_t T, int H, double eps,
+                               uint16_t *xn, double *exact)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double ss = 0.0;
+        for (int h = 0; h < H; ++h) {
+            const double v = bf16_value(x[t * H + h]);
+            ss += v * v;
+        }
+        const double r = 1.0 / sqrt(ss / H + eps);
+        for (int h = 0; h < H; ++h) {
+            const double v = bf16_value(x[t * H + h]) * r * bf16_value(gamma[h]);
+            xn[t * H + h] = bf16_round(v);
+            if (exact)
+                exact[t * H + h] = v;
+        }
+    }
 }
 
 /*

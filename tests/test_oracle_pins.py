@@ -329,3 +329,89 @@ def test_token_subset_is_independent():
     part = oracle.forward(inp, cfg.k, tokens=[5, 2])
     assert np.array_equal(part["y"], full["y"][[5, 2]])
     assert np.array_equal(part["idx"], full["idx"][[5, 2]])
+
+
+# --------------------------------------------------------------------------- Pre-LN RMSNorm
+# MLX README "Architecture Details" (RMSNorm, Pre-LN placement) and ZM "API" (norm_eps 1e-5):
+# xn = bf16(x / sqrt(mean(x^2) + eps) * gamma), block output y = x + layer(xn).
+
+def _bf16_nearest_exact(v: float) -> int:
+    """Round a double to bf16 by exact rational arithmetic (ties to even): the bit pattern."""
+    from fractions import Fraction
+    if v == 0.0:
+        return 0x8000 if math.copysign(1.0, v) < 0 else 0
+    fv = Fraction(v)
+    m, e = math.frexp(abs(v))          # |v| = m 2^e, 0.5 <= m < 1
+    ulp = Fraction(2) ** (e - 8)
+    lo = (abs(fv) // ulp) * ulp
+    hi = lo + ulp
+    dlo, dhi = abs(fv) - lo, hi - abs(fv)
+    if dlo < dhi:
+        r = lo
+    elif dhi < dlo:
+        r = hi
+    else:                               # tie: the one with an even last kept bit
+        r = lo if (lo / ulp) % 2 == 0 else hi
+    f = np.float32(float(r) if v > 0 else -float(r))
+    return int(f.view(np.uint32) >> 16)
+
+
+def test_bf16_rounding_ties_to_even():
+    cases = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 1.0 + 2.0 ** -8 + 2.0 ** -30,
+             3.0, -0.0, 0.0, 1e-3, 123.456, -7.0 + 2.0 ** -6]
+    for v in cases:
+        assert oracle.bf16_round(v) == _bf16_nearest_exact(v), v
+    assert oracle.bf16_round(1.0 + 2.0 ** -8) == 0x3F80          # tie -> even (down)
+    assert oracle.bf16_round(1.0 + 3 * 2.0 ** -8) == 0x3F82      # tie -> even (up)
+    rng = np.random.default_rng(7)
+    for v in rng.standard_normal(300) * 10.0 ** rng.integers(-3, 4, 300):
+        assert oracle.bf16_round(float(v)) == _bf16_nearest_exact(float(v))
+
+
+def test_rmsnorm_closed_form_constant_rows():
+    H = 96
+    gamma = np.full(H, 0x3F80, dtype=np.uint16)                   # 1.0
+    for c in (0.5, 1.0, 3.0, -2.25):
+        x = np.full((1, H), bf16_bits_from_f32(np.float32(c)), dtype=np.uint16)
+        for eps in (0.0, 1e-5, 0.25):
+            xn, ex = oracle.rmsnorm(x, gamma, eps, with_exact=True)
+            ref = c / math.sqrt(c * c + eps)
+            np.testing.assert_allclose(ex, ref, rtol=2e-16, atol=0)
+            assert (xn == _bf16_nearest_exact(ref)).all()
+            if eps == 0.0:
+                assert (xn == (0x3F80 if c > 0 else 0xBF80)).all()   # exactly +-1
+
+
+def test_rmsnorm_matches_numpy_and_exact_rounding():
+    cfg = CONFIGS["tiny"].with_(H=96)
+    inp = make_inputs(cfg, seed=11, T=5, parts=("x", "norm_w"))
+    x = f32_from_bf16_bits(inp["x"]).astype(np.float64)
+    g = f32_from_bf16_bits(inp["norm_w"]).astype(np.float64)
+    xn, ex = oracle.rmsnorm(inp["x"], inp["norm_w"], 1e-5, with_exact=True)
+    ref = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-5) * g
+    np.testing.assert_allclose(ex, ref, rtol=1e-14, atol=0)
+    for t in range(5):
+        for h in range(0, 96, 7):
+            assert xn[t, h] == _bf16_nearest_exact(float(ex[t, h]))
+
+
+def test_rmsnorm_scale_invariance_without_eps():
+    cfg = CONFIGS["tiny"]
+    inp = make_inputs(cfg, seed=12, T=4, parts=("x", "norm_w"))
+    xf = f32_from_bf16_bits(inp["x"])
+    for j in (-3, 2, 5):
+        xs = bf16_bits_from_f32(xf * np.float32(2.0 ** j))        # exact: a power of two
+        assert (oracle.rmsnorm(xs, inp["norm_w"], 0.0) == oracle.rmsnorm(inp["x"], inp["norm_w"], 0.0)).all()
+
+
+def test_prenorm_block_is_residual_plus_layer_of_normalized_rows():
+    cfg = CONFIGS["tiny"]
+    inp = make_inputs(cfg, seed=13)
+    out = oracle.forward_prenorm(inp, cfg.k, eps=1e-5)
+    xn = oracle.rmsnorm(inp["x"], inp["norm_w"], 1e-5)
+    plain = oracle.forward(dict(inp, x=xn), cfg.k)
+    np.testing.assert_array_equal(out["idx"], plain["idx"])
+    np.testing.assert_allclose(out["y"] - f32_from_bf16_bits(inp["x"]), plain["y"], rtol=0, atol=1e-12)
+    # gamma = 0 normalizes every row to zero: the layer then sees only its biases
+    zero = oracle.forward_prenorm(dict(inp, norm_w=np.zeros_like(inp["norm_w"])), cfg.k)
+    assert (f32_from_bf16_bits(zero["xn"]) == 0.0).all()          # (+-0: the sign of x survives)

@@ -32,6 +32,7 @@ __all__ = ["MoeConfig", "CONFIGS", "TENSOR_IDS", "ALL_PARTS", "make_inputs", "bf
 TENSOR_IDS = {
     "x": 0, "router_w": 1, "router_b": 2, "gu_blocks": 3, "gu_scales": 4,
     "gu_bias": 5, "dn_blocks": 6, "dn_scales": 7, "dn_bias": 8, "expert_offset": 9,
+    "norm_w": 10,
 }
 
 
@@ -48,6 +49,7 @@ class MoeConfig:
     router_w_std: float = 0.02
     router_b_std: float = 0.02
     expert_offset_std: float = 0.0   # per-expert N(0, std) added to the router bias
+    norm_w_std: float = 0.1          # RMSNorm weights 1 + N(0, std)
     scale_exp_lo: int = -8           # e8m0 exponent range, inclusive
     scale_exp_hi: int = -3
     bias_std: float = 0.02
@@ -109,7 +111,7 @@ def _scales(cfg, tensor, seed, shape) -> np.ndarray:
 
 
 ALL_PARTS = ("x", "router_w", "router_b", "gu_blocks", "gu_scales", "gu_bias", "dn_blocks",
-             "dn_scales", "dn_bias")
+             "dn_scales", "dn_bias", "norm_w")
 
 
 def make_inputs(cfg: MoeConfig, seed: int = 0, T: int | None = None,
@@ -144,6 +146,10 @@ def make_inputs(cfg: MoeConfig, seed: int = 0, T: int | None = None,
         "dn_blocks": lambda: _bytes(cfg, "dn_blocks", seed, (E, H, I // 2)),
         "dn_scales": lambda: _scales(cfg, "dn_scales", seed, (E, H, I // 32)),
         "dn_bias": lambda: _normal_bf16(cfg, "dn_bias", seed, (E, H), cfg.bias_std),
+        # the pre-MoE RMSNorm's weights (used by the Pre-LN block entry point only)
+        "norm_w": lambda: bf16_bits_from_f32(
+            np.float32(1.0) + _rng(cfg, "norm_w", seed).standard_normal(size=(H,), dtype=np.float32)
+            * np.float32(cfg.norm_w_std)),
     }
     unknown = set(parts) - set(makers)
     if unknown:
