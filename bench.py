@@ -55,14 +55,16 @@ KERNEL_SOURCES = {               # kernel -> files whose text defines it
     "down_grouped": ["gemm_grouped.hip", "device_common.h", "lds_dma.h"],
     "combine": ["gemm_grouped.hip", "device_common.h", "lds_dma.h"],
     "combine_decode": ["gemm_decode.hip", "device_common.h"],
+    "rmsnorm": ["norm.hip", "device_common.h"],
 }
 FEW_STAGES = ["logits", "up_decode", "down_decode"]                       # T < 4
 STREAM_STAGES = ["route", "up_stream", "down_stream", "combine_decode"]     # 4 <= T <= 64
 PREFILL_STAGES = ["route", "permute", "up_grouped", "down_grouped", "combine"]
 
 
-def stages_of(T: int):
-    return FEW_STAGES if T < 4 else (STREAM_STAGES if T <= 64 else PREFILL_STAGES)
+def stages_of(T: int, prenorm: bool = False):
+    st = FEW_STAGES if T < 4 else (STREAM_STAGES if T <= 64 else PREFILL_STAGES)
+    return (["rmsnorm"] if prenorm else []) + st
 
 
 def kernel_source_sha(kernel: str) -> str:
@@ -86,6 +88,8 @@ def parse_args():
     ap.add_argument("--timed-steps", type=int, default=200, help="steps of the per-kernel timing run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the CPU sample (0 = auto)")
+    ap.add_argument("--prenorm", action="store_true",
+                    help="time the pre-norm block y = x + layer(rmsnorm(x)) instead of the layer")
     return ap.parse_args()
 
 
@@ -126,8 +130,10 @@ class Workload:
     WEIGHTS = ("router_w", "router_b", "gu_blocks", "gu_scales", "gu_bias", "dn_blocks",
                "dn_scales", "dn_bias")
 
+    NORM_EPS = 1e-5
+
     @classmethod
-    def create(cls, name: str, replicas: int):
+    def create(cls, name: str, replicas: int, prenorm: bool = False):
         import numpy as np
         import torch
         import mxfp4_mixture_experts_router_amd as moe
@@ -143,7 +149,9 @@ class Workload:
                 return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-        host_w = make_inputs(cfg, seed=0, parts=self.WEIGHTS)
+        self.prenorm = prenorm
+        self.label = name + ("+prenorm" if prenorm else "")
+        host_w = make_inputs(cfg, seed=0, parts=self.WEIGHTS + (("norm_w",) if prenorm else ()))
         self.host_weights = host_w
         layer_bytes = sum(v.nbytes for v in host_w.values())
         if replicas <= 0:
@@ -173,13 +181,15 @@ class Workload:
     def args(self, r: int, stream_ptr: int):
         w = self.weights[r]
         P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-        return (ctypes.byref(self.shape), P(self.x[r]), P(w["router_w"]), P(w["router_b"]),
+        norm = (P(w["norm_w"]), ctypes.c_double(self.NORM_EPS)) if self.prenorm else ()
+        return (ctypes.byref(self.shape), P(self.x[r]), *norm, P(w["router_w"]), P(w["router_b"]),
                 P(w["gu_blocks"]), P(w["gu_scales"]), P(w["gu_bias"]), P(w["dn_blocks"]),
                 P(w["dn_scales"]), P(w["dn_bias"]), P(self.y[r]), P(self.idx[r]), P(self.w[r]),
                 P(self.ws), self.ws.numel(), ctypes.c_void_p(stream_ptr))
 
     def step(self, r: int, stream_ptr: int):
-        st = self.lib.moe_mxfp4_forward(*self.args(r, stream_ptr))
+        fn = self.lib.moe_mxfp4_forward_prenorm if self.prenorm else self.lib.moe_mxfp4_forward
+        st = fn(*self.args(r, stream_ptr))
         if st != 0:
             raise RuntimeError(self.lib.moe_mxfp4_last_error().decode())
 
@@ -251,9 +261,9 @@ def run_per_kernel(wl: Workload, steps: int, hip: Hip):
     arrays = [(ctypes.c_void_p * n_ev)(*evs) for evs in events]
     n_launch = ctypes.c_int(0)
     torch.cuda.synchronize()
+    fn = lib.moe_mxfp4_forward_prenorm_timed if wl.prenorm else lib.moe_mxfp4_forward_timed
     for i in range(steps):
-        st = lib.moe_mxfp4_forward_timed(*wl.args(i % wl.R, stream.cuda_stream), arrays[i], n_ev,
-                                         ctypes.byref(n_launch))
+        st = fn(*wl.args(i % wl.R, stream.cuda_stream), arrays[i], n_ev, ctypes.byref(n_launch))
         if st != 0:
             raise RuntimeError(lib.moe_mxfp4_last_error().decode())
     torch.cuda.synchronize()
@@ -281,6 +291,9 @@ def kernel_work(wl: Workload, kernel: str, D: float):
     N = T * k
     gu_expert = 2 * I * (H // 2) + 2 * I * (H // 32) + 2 * I * 2      # packed + scales + bias
     dn_expert = H * (I // 2) + H * (I // 32) + H * 2
+    res = T * H * 2 if wl.prenorm else 0      # the residual the last kernel adds
+    if kernel == "rmsnorm":
+        return 2 * T * H * 2 + H * 2, 0
     if kernel == "route":
         return T * H * 2 + E * H * 2 + E * 2 + N * 8, 2 * T * E * H
     if kernel == "logits":
@@ -290,7 +303,7 @@ def kernel_work(wl: Workload, kernel: str, D: float):
     if kernel in ("up_decode", "up_stream"):
         return D * gu_expert + T * H * 2 + N * 8 + N * I * 2, 2 * N * 2 * I * H
     if kernel == "down_decode":      # y directly
-        return D * dn_expert + N * I * 2 + N * 8 + T * H * 2, 2 * N * H * I
+        return D * dn_expert + N * I * 2 + N * 8 + T * H * 2 + res, 2 * N * H * I
     if kernel == "down_stream":      # per-slot partial rows
         return D * dn_expert + N * I * 2 + N * 8 + N * H * 4, 2 * N * H * I
     if kernel == "up_grouped":
@@ -298,13 +311,15 @@ def kernel_work(wl: Workload, kernel: str, D: float):
     if kernel == "down_grouped":
         return D * dn_expert + N * I * 2 + N * 4 + N * H * 4, 2 * N * H * I
     if kernel == "combine":
-        return N * H * 4 + N * 4 + T * H * 2, 0
+        return N * H * 4 + N * 4 + T * H * 2 + res, 0
     if kernel == "combine_decode":
-        return N * H * 4 + T * H * 2, 0
+        return N * H * 4 + T * H * 2 + res, 0
     raise KeyError(kernel)
 
 
 def load_traffic(workload: str, kernel: str):
+    if workload.endswith("+prenorm"):
+        return None
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -339,15 +354,15 @@ def roofline_for(wl: Workload, stages, kernel_us, D):
     roof["alg_bytes_per_launch"] = e["alg_bytes"]
     roof["alg_flops_per_launch"] = e["alg_flops"]
     roof["avg_us"] = e["avg_us"]
-    roof["traffic"] = load_traffic(wl.name, e["kernel"])
+    roof["traffic"] = load_traffic(wl.label, e["kernel"])
     return roof, entries
 
 
-def measure(name, steps, warmup, mode, replicas, timed_steps, hip):
-    wl = Workload.create(name, replicas)
+def measure(name, steps, warmup, mode, replicas, timed_steps, hip, prenorm=False):
+    wl = Workload.create(name, replicas, prenorm)
     ms, wall_ms, steps_run, mode = run_timed(wl, steps, warmup, mode)
     D = distinct_experts(wl)
-    stages = stages_of(wl.cfg.T)
+    stages = stages_of(wl.cfg.T, prenorm)
     kus = run_per_kernel(wl, timed_steps, hip)
     roof, kernels = roofline_for(wl, stages, kus, D)
     layer_bytes = sum(kernel_work(wl, s, D)[0] for s in stages)
@@ -371,10 +386,13 @@ def cpu_baseline(wl: Workload, sample: int):
     inp = dict(wl.host_weights)
     inp["x"] = make_inputs(wl.cfg, seed=10_000, T=n, parts=("x",))["x"]
     t0 = time.perf_counter()
-    oracle.forward(inp, wl.cfg.k, alpha=wl.cfg.alpha, limit=wl.cfg.limit)
+    if wl.prenorm:
+        oracle.forward_prenorm(inp, wl.cfg.k, alpha=wl.cfg.alpha, limit=wl.cfg.limit, eps=wl.NORM_EPS)
+    else:
+        oracle.forward(inp, wl.cfg.k, alpha=wl.cfg.alpha, limit=wl.cfg.limit)
     dt = time.perf_counter() - t0
     return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} tokens of the {wl.name} layer (same weights), plain fp64 C oracle, "
+            "sample": f"{n} tokens of the {wl.label} layer (same weights), plain fp64 C oracle, "
                       f"{dt:.1f} s"}
 
 
@@ -396,7 +414,7 @@ def main():
         sys.exit(1)
     hip = Hip()
     wl, main_res = measure(args.workload, args.steps, args.warmup, args.mode, args.replicas,
-                           args.timed_steps, hip)
+                           args.timed_steps, hip, args.prenorm)
     cfg = wl.cfg
     out = {
         "metric": METRIC,
@@ -411,7 +429,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k,
+        "config": {"workload": wl.label, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k,
                    "experts": "mxfp4 e2m1 + e8m0 per 32", "replicas": wl.R, "mode": main_res["mode"],
                    "distinct_experts_per_step": main_res["distinct_experts"]},
         "roofline": main_res["roofline"],
@@ -425,9 +443,9 @@ def main():
     torch.cuda.empty_cache()
     if args.secondary:
         wl2, res2 = measure(args.secondary, args.secondary_steps, min(args.warmup, 10), args.mode,
-                            0, min(args.timed_steps, 50), hip)
+                            0, min(args.timed_steps, 50), hip, args.prenorm)
         out["secondary"] = {
-            "workload": wl2.cfg.name, "T": wl2.cfg.T, "E": wl2.cfg.E,
+            "workload": wl2.label, "T": wl2.cfg.T, "E": wl2.cfg.E,
             "value": round(res2["value"], 1), "unit": "tokens/s",
             "ms_per_step": round(res2["ms_per_step"], 6), "steps": res2["steps"],
             "replicas": wl2.R, "roofline": res2["roofline"], "layer_roofline": res2["layer"],

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_MXFP4_ABI_VERSION 2
+#define MOE_MXFP4_ABI_VERSION 3
 
 typedef uint16_t moe_bf16_t;
 
@@ -87,8 +87,8 @@ const char *moe_mxfp4_last_error(void);
 /* Host-only validation of a shape; launches nothing. */
 moe_status_t moe_mxfp4_check_shape(const moe_mxfp4_shape_t *shape);
 
-/* Bytes of device workspace moe_mxfp4_forward needs for `shape` (written to *bytes).
- * Host-only; launches nothing. */
+/* Bytes of device workspace moe_mxfp4_forward and moe_mxfp4_forward_prenorm need for
+ * `shape` (written to *bytes). Host-only; launches nothing. */
 moe_status_t moe_mxfp4_workspace_bytes(const moe_mxfp4_shape_t *shape, size_t *bytes);
 
 /*
@@ -113,8 +113,34 @@ moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape,
                                moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
                                void *workspace, size_t workspace_bytes, void *stream);
 
-/* Most kernels one moe_mxfp4_forward call launches. */
-#define MOE_MXFP4_MAX_LAUNCHES 5
+/*
+ * The pre-norm block around the layer (GPT-OSS MLX Implementation README, "Architecture
+ * Details": RMSNorm in Pre-LN placement; ZeroModels GPT-OSS page, "API" table: norm_eps,
+ * 1e-5 for GPT-OSS):
+ *   xn[t, :] = bf16(x[t, :] * norm_w / sqrt(mean_h x[t, h]^2 + norm_eps))
+ *   y[t, :]  = bf16(x[t, :] + layer(xn)[t, :])
+ * The normalization runs in double and rounds once to bf16 (nearest, ties to even), as
+ * moe_mxfp4_rmsnorm; the layer (steps 1-6) then runs on xn, and its last kernel adds the
+ * residual x before the one bf16 rounding of y. Arguments as moe_mxfp4_forward, plus
+ *  norm_w    [H] bf16, 16-byte aligned (RMSNorm scale; MOE_EINVAL if NULL, MOE_EALIGN if
+ *            misaligned)
+ *  norm_eps  finite and >= 0 (MOE_EINVAL otherwise)
+ * topk_idx / topk_w are the routing of xn. The workspace size is moe_mxfp4_workspace_bytes().
+ * One more kernel than moe_mxfp4_forward.
+ */
+moe_status_t moe_mxfp4_forward_prenorm(const moe_mxfp4_shape_t *shape,
+                                       const moe_bf16_t *x,
+                                       const moe_bf16_t *norm_w, double norm_eps,
+                                       const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                                       const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                                       const moe_bf16_t *gu_bias,
+                                       const uint8_t *dn_blocks, const uint8_t *dn_scales,
+                                       const moe_bf16_t *dn_bias,
+                                       moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Most kernels one moe_mxfp4_forward or moe_mxfp4_forward_prenorm call launches. */
+#define MOE_MXFP4_MAX_LAUNCHES 6
 
 /*
  * moe_mxfp4_forward with timing instrumentation for profilers and benchmarks: the same
@@ -139,6 +165,33 @@ moe_status_t moe_mxfp4_forward_timed(const moe_mxfp4_shape_t *shape,
                                      moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
                                      void *workspace, size_t workspace_bytes, void *stream,
                                      void *const *events, int n_events, int *n_launches);
+
+/* moe_mxfp4_forward_prenorm with the instrumentation of moe_mxfp4_forward_timed; launch 0
+ * is the RMSNorm, the rest follow the counts above. */
+moe_status_t moe_mxfp4_forward_prenorm_timed(const moe_mxfp4_shape_t *shape,
+                                             const moe_bf16_t *x,
+                                             const moe_bf16_t *norm_w, double norm_eps,
+                                             const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                                             const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                                             const moe_bf16_t *gu_bias,
+                                             const uint8_t *dn_blocks, const uint8_t *dn_scales,
+                                             const moe_bf16_t *dn_bias,
+                                             moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
+                                             void *workspace, size_t workspace_bytes, void *stream,
+                                             void *const *events, int n_events, int *n_launches);
+
+/*
+ * The RMSNorm of the pre-norm block alone (GPT-OSS MLX Implementation README, "Architecture
+ * Details"): xn[r, :] = bf16(x[r, :] * r_r * norm_w), r_r = 1 / sqrt(sum_c x[r, c]^2 / cols
+ * + eps), computed in double (the squares of bf16 values are exact; products left to right)
+ * and rounded once to bf16, nearest, ties to even. x, xn [rows, cols] bf16 and norm_w [cols]
+ * bf16, all 16-byte aligned (MOE_EALIGN); cols a positive multiple of 8 (MOE_ESHAPE);
+ * 0 <= rows <= 2^24; eps finite and >= 0 (MOE_EINVAL). The sum of squares is accumulated in
+ * a fixed order (per thread, then across threads); its rounding differs from a sequential
+ * sum only in the last bits of a double.
+ */
+moe_status_t moe_mxfp4_rmsnorm(const moe_bf16_t *x, const moe_bf16_t *norm_w, int64_t rows,
+                               int32_t cols, double eps, moe_bf16_t *xn, void *stream);
 
 /*
  * Steps 1-2 only (router, top-k, softmax). Logits are accumulated in double precision

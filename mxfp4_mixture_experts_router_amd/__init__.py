@@ -25,7 +25,7 @@ __all__ = [
     "MoeError", "MoeLibraryMissing", "library_path", "load_library", "abi_version",
     "workspace_bytes", "moe_forward", "route", "permute", "expert_up", "expert_down",
     "combine", "dequant", "DECODE_MAX_T", "DECODE_MAX_K", "uses_decode_path", "mx8_bytes",
-    "quantize_act",
+    "quantize_act", "rmsnorm",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +41,7 @@ def uses_decode_path(T, H, I):
     tokens; no permutation)."""
     return T <= DECODE_MAX_T and H <= DECODE_MAX_K and I <= DECODE_MAX_K
 
-MAX_LAUNCHES = 5
+MAX_LAUNCHES = 6
 
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ESHAPE", 3: "MOE_EALIGN", 4: "MOE_EWORKSPACE",
           5: "MOE_EHIP"}
@@ -72,6 +72,12 @@ _SIGS = {
     "moe_mxfp4_forward": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 13 + [ctypes.c_size_t, _vp]),
     "moe_mxfp4_forward_timed": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 13
                                 + [ctypes.c_size_t, _vp, _vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
+    "moe_mxfp4_forward_prenorm": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, ctypes.c_double]
+                                  + [_vp] * 12 + [ctypes.c_size_t, _vp]),
+    "moe_mxfp4_forward_prenorm_timed": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, ctypes.c_double]
+                                        + [_vp] * 12 + [ctypes.c_size_t, _vp, _vp, ctypes.c_int,
+                                                        ctypes.POINTER(ctypes.c_int)]),
+    "moe_mxfp4_rmsnorm": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, _vp, _vp]),
     "moe_mxfp4_route": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 7),
     "moe_mxfp4_permute": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 7),
     "moe_mxfp4_expert_up": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 8),
@@ -163,11 +169,17 @@ def _dims(x, router_w, gu_blocks):
 def moe_forward(x, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks, dn_scales,
                 dn_bias, k: int, alpha: float = 1.702, limit: float = 7.0, *,
                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                return_topk: bool = False, stream=None):
-    """The whole layer. Returns y [T, H] bf16 (and (topk_idx, topk_w) if return_topk)."""
+                return_topk: bool = False, norm_weight: Optional[torch.Tensor] = None,
+                norm_eps: float = 1e-5, stream=None):
+    """The whole layer. Returns y [T, H] bf16 (and (topk_idx, topk_w) if return_topk).
+
+    With ``norm_weight`` ([H] bf16), the pre-norm block ``y = x + layer(rmsnorm(x))``
+    (moe_mxfp4_forward_prenorm); the routing returned is that of the normalized rows."""
     T, H, I, E = _dims(x, router_w, gu_blocks)
     dev = x.device
     _need(x, "x", _BF16, (T, H), dev)
+    if norm_weight is not None:
+        _need(norm_weight, "norm_weight", _BF16, (H,), dev)
     _need(router_w, "router_w", _BF16, (E, H), dev)
     _need(router_b, "router_b", _BF16, (E,), dev)
     _need(gu_blocks, "gu_blocks", _U8, (E, 2 * I, H // 2), dev)
@@ -186,10 +198,14 @@ def moe_forward(x, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks,
     _need(y, "out", _BF16, (T, H), dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev) if return_topk else None
     w = torch.empty((T, k), dtype=torch.float32, device=dev) if return_topk else None
-    _check(lib.moe_mxfp4_forward(
-        ctypes.byref(shape), _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(gu_blocks),
-        _ptr(gu_scales), _ptr(gu_bias), _ptr(dn_blocks), _ptr(dn_scales), _ptr(dn_bias), _ptr(y),
-        _ptr(idx), _ptr(w), _ptr(workspace), workspace.numel(), _stream(stream)))
+    tail = (_ptr(router_w), _ptr(router_b), _ptr(gu_blocks), _ptr(gu_scales), _ptr(gu_bias),
+            _ptr(dn_blocks), _ptr(dn_scales), _ptr(dn_bias), _ptr(y), _ptr(idx), _ptr(w),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+    if norm_weight is None:
+        _check(lib.moe_mxfp4_forward(ctypes.byref(shape), _ptr(x), *tail))
+    else:
+        _check(lib.moe_mxfp4_forward_prenorm(ctypes.byref(shape), _ptr(x), _ptr(norm_weight),
+                                             float(norm_eps), *tail))
     return (y, idx, w) if return_topk else y
 
 
@@ -226,6 +242,19 @@ def permute(topk_idx, topk_w, E: int, stream=None):
                                             _ptr(offsets), _ptr(sorted_token), _ptr(sorted_w),
                                             _ptr(slot_row), _stream(stream)))
     return offsets, sorted_token, sorted_w, slot_row
+
+
+def rmsnorm(x, norm_weight, eps: float = 1e-5, stream=None):
+    """Pre-LN RMSNorm of the rows of x [R, C] bf16 with scale norm_weight [C] bf16: returns
+    bf16(x * norm_weight / sqrt(mean(x^2) + eps)) [R, C] (moe_mxfp4_rmsnorm)."""
+    R, C = x.shape
+    dev = x.device
+    _need(x, "x", _BF16, (R, C), dev)
+    _need(norm_weight, "norm_weight", _BF16, (C,), dev)
+    xn = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+    _check(load_library().moe_mxfp4_rmsnorm(_ptr(x), _ptr(norm_weight), R, C, float(eps), _ptr(xn),
+                                            _stream(stream)))
+    return xn
 
 
 def mx8_bytes(rows: int, cols: int) -> int:

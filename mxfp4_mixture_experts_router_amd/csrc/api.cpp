@@ -67,7 +67,7 @@ moe::Dims dims_of(const moe_mxfp4_shape_t *s) {
 
 // Workspace regions (each 256-byte aligned), in order.
 struct Layout {
-    size_t idx, w, logits, offsets, sorted_token, sorted_w, slot_row, o, part, x8, h8, total;
+    size_t idx, w, logits, offsets, sorted_token, sorted_w, slot_row, o, part, x8, h8, xn, total;
 };
 
 size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -78,6 +78,8 @@ Layout layout_of(const moe_mxfp4_shape_t *s) {
     size_t p = 0;
     L.idx = p;          p += round_up(N * 4);
     L.w = p;            p += round_up(N * 4);
+    // the normalized input of the pre-norm entry points (bf16 [T, H])
+    L.xn = p;           p += round_up(static_cast<size_t>(s->T) * s->H * 2);
     L.logits = 0;
     if (moe::use_decode_path(s->T, s->H, s->I)) {
         // activations as E4M3 hi/lo (mx8) matrices: x as T rows of H, h as 2 T k half-block
@@ -153,8 +155,10 @@ namespace {
 // Validation + launch sequence shared by moe_mxfp4_forward and moe_mxfp4_forward_timed.
 // With `events`, launch i records events[2i] and events[2i + 1] at the start and the end of
 // its kernel's execution (hipExtLaunchKernel).
+// With norm_w, the pre-norm block y = x + layer(rmsnorm(x)): the normalized rows go to the
+// workspace, the layer runs on them and its last kernel adds x.
 moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
-                         const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                         const moe_bf16_t *norm_w, double norm_eps, const moe_bf16_t *router_w, const moe_bf16_t *router_b,
                          const uint8_t *gu_blocks, const uint8_t *gu_scales,
                          const moe_bf16_t *gu_bias, const uint8_t *dn_blocks,
                          const uint8_t *dn_scales, const moe_bf16_t *dn_bias, moe_bf16_t *y,
@@ -173,6 +177,11 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
     }
     if (shape->T == 0) return ok();
     REQUIRE16(x, "x");
+    if (norm_w) {
+        if (!aligned16(norm_w)) return fail(MOE_EALIGN, "norm_w is not 16-byte aligned");
+        if (!std::isfinite(norm_eps) || norm_eps < 0.0)
+            return fail(MOE_EINVAL, "norm_eps = %g must be finite and >= 0", norm_eps);
+    }
     REQUIRE16(router_w, "router_w");
     REQUIRE(router_b, "router_b");
     REQUIRE16(gu_blocks, "gu_blocks");
@@ -212,6 +221,14 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
         if (n_launches) *n_launches = launched;          \
     } while (0)
 
+    const moe_bf16_t *residual = nullptr;
+    if (norm_w) {
+        moe_bf16_t *xn = reinterpret_cast<moe_bf16_t *>(ws + L.xn);
+        STEP(moe::launch_rmsnorm(d, x, norm_w, norm_eps, xn, s), "rmsnorm");
+        residual = x;
+        x = xn;
+    }
+
     if (moe::use_decode_path(shape->T, shape->H, shape->I)) {
         float *part = reinterpret_cast<float *>(ws + L.part);
         uint8_t *x8 = ws + L.x8, *h8 = ws + L.h8;
@@ -219,14 +236,14 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
             STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, x8, s), "route");
             STEP(moe::launch_up_stream(d, x8, gu_blocks, gu_scales, gu_bias, idx, h8, s), "up (stream)");
             STEP(moe::launch_down_stream(d, h8, dn_blocks, dn_scales, dn_bias, idx, w, part, s), "down (stream)");
-            STEP(moe::launch_combine_decode(d, part, y, s), "combine (decode)");
+            STEP(moe::launch_combine_decode(d, part, residual, y, s), "combine (decode)");
             return ok();
         }
         // few tokens: logits in a multi-block kernel, top-k + softmax inside the up-projection
         double *logits = reinterpret_cast<double *>(ws + L.logits);
         STEP(moe::launch_logits(d, x, router_w, router_b, logits, x8, s), "router logits");
         STEP(moe::launch_up_decode(d, x8, gu_blocks, gu_scales, gu_bias, logits, idx, w, h8, s), "up (decode)");
-        STEP(moe::launch_down_decode(d, h8, dn_blocks, dn_scales, dn_bias, idx, w, y, s), "down (decode)");
+        STEP(moe::launch_down_decode(d, h8, dn_blocks, dn_scales, dn_bias, idx, w, residual, y, s), "down (decode)");
         return ok();
     }
     uint8_t *x8 = ws + L.x8, *h8 = ws + L.h8;
@@ -239,7 +256,7 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
     STEP(moe::launch_permute(d, idx, w, offsets, sorted_token, sorted_w, slot_row, s), "permute");
     STEP(moe::launch_up_grouped(d, x8, gu_blocks, gu_scales, gu_bias, offsets, sorted_token, h8, s), "up");
     STEP(moe::launch_down_grouped(d, h8, dn_blocks, dn_scales, dn_bias, offsets, sorted_w, o, s), "down");
-    STEP(moe::launch_combine(d, o, slot_row, y, s), "combine");
+    STEP(moe::launch_combine(d, o, slot_row, residual, y, s), "combine");
 #undef STEP
     return ok();
 }
@@ -253,9 +270,39 @@ MOE_EXPORT moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape, const 
                                           const uint8_t *dn_scales, const moe_bf16_t *dn_bias,
                                           moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
                                           void *workspace, size_t workspace_bytes, void *stream) {
-    return run_forward(shape, x, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks,
+    return run_forward(shape, x, nullptr, 0.0, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks,
                        dn_scales, dn_bias, y, topk_idx, topk_w, workspace, workspace_bytes, stream,
                        nullptr, 0, nullptr);
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_forward_prenorm(
+    const moe_mxfp4_shape_t *shape, const moe_bf16_t *x, const moe_bf16_t *norm_w, double norm_eps,
+    const moe_bf16_t *router_w, const moe_bf16_t *router_b, const uint8_t *gu_blocks,
+    const uint8_t *gu_scales, const moe_bf16_t *gu_bias, const uint8_t *dn_blocks,
+    const uint8_t *dn_scales, const moe_bf16_t *dn_bias, moe_bf16_t *y, int32_t *topk_idx,
+    float *topk_w, void *workspace, size_t workspace_bytes, void *stream) {
+    moe_status_t st = check_shape(shape, true);
+    if (st != MOE_OK) return st;
+    if (shape->T > 0) REQUIRE(norm_w, "norm_w");
+    return run_forward(shape, x, norm_w, norm_eps, router_w, router_b, gu_blocks, gu_scales, gu_bias,
+                       dn_blocks, dn_scales, dn_bias, y, topk_idx, topk_w, workspace, workspace_bytes,
+                       stream, nullptr, 0, nullptr);
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_forward_prenorm_timed(
+    const moe_mxfp4_shape_t *shape, const moe_bf16_t *x, const moe_bf16_t *norm_w, double norm_eps,
+    const moe_bf16_t *router_w, const moe_bf16_t *router_b, const uint8_t *gu_blocks,
+    const uint8_t *gu_scales, const moe_bf16_t *gu_bias, const uint8_t *dn_blocks,
+    const uint8_t *dn_scales, const moe_bf16_t *dn_bias, moe_bf16_t *y, int32_t *topk_idx,
+    float *topk_w, void *workspace, size_t workspace_bytes, void *stream, void *const *events,
+    int n_events, int *n_launches) {
+    if (!events) return fail(MOE_EINVAL, "events is NULL");
+    moe_status_t st = check_shape(shape, true);
+    if (st != MOE_OK) return st;
+    if (shape->T > 0) REQUIRE(norm_w, "norm_w");
+    return run_forward(shape, x, norm_w, norm_eps, router_w, router_b, gu_blocks, gu_scales, gu_bias,
+                       dn_blocks, dn_scales, dn_bias, y, topk_idx, topk_w, workspace, workspace_bytes,
+                       stream, events, n_events, n_launches);
 }
 
 MOE_EXPORT moe_status_t moe_mxfp4_forward_timed(
@@ -265,7 +312,7 @@ MOE_EXPORT moe_status_t moe_mxfp4_forward_timed(
     const moe_bf16_t *dn_bias, moe_bf16_t *y, int32_t *topk_idx, float *topk_w, void *workspace,
     size_t workspace_bytes, void *stream, void *const *events, int n_events, int *n_launches) {
     if (!events) return fail(MOE_EINVAL, "events is NULL");
-    return run_forward(shape, x, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks,
+    return run_forward(shape, x, nullptr, 0.0, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks,
                        dn_scales, dn_bias, y, topk_idx, topk_w, workspace, workspace_bytes, stream,
                        events, n_events, n_launches);
 }
@@ -302,6 +349,24 @@ MOE_EXPORT moe_status_t moe_mxfp4_permute(const moe_mxfp4_shape_t *shape, const 
     REQUIRE(slot_row, "slot_row");
     LAUNCH(moe::launch_permute(dims_of(shape), topk_idx, topk_w, expert_offsets, sorted_token,
                                sorted_weight, slot_row, static_cast<hipStream_t>(stream)), "permute");
+    return ok();
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_rmsnorm(const moe_bf16_t *x, const moe_bf16_t *norm_w, int64_t rows,
+                                          int32_t cols, double eps, moe_bf16_t *xn, void *stream) {
+    if (rows < 0) return fail(MOE_EINVAL, "rows = %lld is negative", static_cast<long long>(rows));
+    if (cols <= 0 || cols % 8) return fail(MOE_ESHAPE, "cols = %d is not a positive multiple of 8", cols);
+    if (rows > (static_cast<int64_t>(1) << 24))
+        return fail(MOE_ESHAPE, "rows = %lld exceeds 2^24", static_cast<long long>(rows));
+    if (!std::isfinite(eps) || eps < 0.0) return fail(MOE_EINVAL, "eps = %g must be finite and >= 0", eps);
+    if (rows == 0) return ok();
+    REQUIRE16(x, "x");
+    REQUIRE16(norm_w, "norm_w");
+    REQUIRE16(xn, "xn");
+    moe::Dims d{};
+    d.T = rows;
+    d.H = cols;
+    LAUNCH(moe::launch_rmsnorm(d, x, norm_w, eps, xn, static_cast<hipStream_t>(stream)), "rmsnorm");
     return ok();
 }
 
@@ -366,7 +431,7 @@ MOE_EXPORT moe_status_t moe_mxfp4_combine(const moe_mxfp4_shape_t *shape, const 
     REQUIRE16(o, "o");
     REQUIRE(slot_row, "slot_row");
     REQUIRE16(y, "y");
-    LAUNCH(moe::launch_combine(dims_of(shape), o, slot_row, y, static_cast<hipStream_t>(stream)),
+    LAUNCH(moe::launch_combine(dims_of(shape), o, slot_row, nullptr, y, static_cast<hipStream_t>(stream)),
            "combine");
     return ok();
 }

@@ -26,6 +26,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// s += the four bf16 values at r (8-byte aligned): the residual branch of a pre-norm block.
+__device__ __forceinline__ void add_residual4(float4 &s, const uint16_t *r) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(r);
+    s.x += __uint_as_float(u.x << 16);
+    s.y += __uint_as_float(u.x & 0xffff0000u);
+    s.z += __uint_as_float(u.y << 16);
+    s.w += __uint_as_float(u.y & 0xffff0000u);
+}
+
 // E8M0 scale byte -> the fp32 power of two 2^(s - 127) (valid for s in 1..254, which
 // covers the supported 2..252).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) { return __uint_as_float(s << 23); }

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(NW * 64) void k_down_mx_tokens(
     const uint8_t *__restrict__ h8, const uint8_t *__restrict__ hs8, const uint8_t *__restrict__ dn_blocks,
     const uint8_t *__restrict__ dn_scales, const uint16_t *__restrict__ dn_bias,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int T, int H, int I, int E, int k,
-    uint16_t *__restrict__ y) {
+    const uint16_t *__restrict__ res, uint16_t *__restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
     __shared__ uint32_t bitmap[kMaxE / 32];
     __shared__ int s_idx[16 * 8];
@@ -487,14 +487,17 @@ __global__ __launch_bounds__(NW * 64) void k_down_mx_tokens(
                 v += (red[w][mt * 4][lane] + red[w][mt * 4 + 1][lane]) + (red[w][mt * 4 + 2][lane] + red[w][mt * 4 + 3][lane]);
             float bterm = 0.f;
             for (int jj = 0; jj < k; ++jj) bterm += s_bprod[t * k + jj][col];
-            y[static_cast<int64_t>(t) * H + drow] = f32_to_bf16(v + bterm);
+            float out = v + bterm;
+            if (res) out += bf16_to_f32(res[static_cast<int64_t>(t) * H + drow]);
+            y[static_cast<int64_t>(t) * H + drow] = f32_to_bf16(out);
         }
     }
 }
 
-// y[t, d] = bf16(sum_{j < k} part[t*k + j, d]) in slot order. Thread = 4 features.
+// y[t, d] = bf16(sum_{j < k} part[t*k + j, d] (+ res[t, d])) in slot order. Thread = 4 features.
 __global__ __launch_bounds__(256) void k_combine_slots(const float *__restrict__ part, int T, int H,
-                                                       int k, uint16_t *__restrict__ y) {
+                                                       int k, const uint16_t *__restrict__ res,
+                                                       uint16_t *__restrict__ y) {
     const int per_row = H / 4;
     const int q = blockIdx.x * 256 + threadIdx.x;
     if (q >= T * per_row) return;
@@ -504,6 +507,7 @@ __global__ __launch_bounds__(256) void k_combine_slots(const float *__restrict__
         const float4 v = *reinterpret_cast<const float4 *>(part + static_cast<int64_t>(t * k + j) * H + d);
         s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
+    if (res) add_residual4(s, res + static_cast<int64_t>(t) * H + d);
     const uint32_t lo = f32_to_bf16(s.x) | (static_cast<uint32_t>(f32_to_bf16(s.y)) << 16);
     const uint32_t hi = f32_to_bf16(s.z) | (static_cast<uint32_t>(f32_to_bf16(s.w)) << 16);
     *reinterpret_cast<uint2 *>(y + static_cast<int64_t>(t) * H + d) = make_uint2(lo, hi);
@@ -526,22 +530,24 @@ hipError_t up_n(const Dims &d, const uint8_t *x8, const uint8_t *xs8, const uint
 
 template <int NMT, int NW, int UB, bool LDS_A, bool SC_LDS>
 hipError_t down_tokens_n(const Dims &d, const uint8_t *h8, const uint8_t *hs8, const uint8_t *db, const uint8_t *ds,
-                         const uint16_t *dbias, int32_t *idx, float *w, uint16_t *y, hipStream_t s) {
+                         const uint16_t *dbias, int32_t *idx, float *w, const uint16_t *res, uint16_t *y,
+                         hipStream_t s) {
     const int64_t N = d.T * d.k;
     const size_t lds = (LDS_A ? static_cast<size_t>(4 * N) * d.I : 0) +
                        static_cast<size_t>(4 * N) * mx8_scale_stride(d.I);
     MOE_LAUNCH((k_down_mx_tokens<NMT, NW, UB, LDS_A, SC_LDS>), dim3(static_cast<unsigned>(d.H / 16)),
                        dim3(NW * 64), lds, s, h8, hs8, db, ds, dbias, idx, w, static_cast<int>(d.T), d.H, d.I, d.E,
-                       d.k, y);
+                       d.k, res, y);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_combine_decode(const Dims &d, const float *part, uint16_t *y, hipStream_t s) {
+hipError_t launch_combine_decode(const Dims &d, const float *part, const uint16_t *residual, uint16_t *y,
+                                 hipStream_t s) {
     const unsigned blocks = static_cast<unsigned>((d.T * (d.H / 4) + 255) / 256);
     MOE_LAUNCH(k_combine_slots, dim3(blocks), dim3(256), 0, s, part, static_cast<int>(d.T), d.H,
-                       d.k, y);
+                       d.k, residual, y);
     return hipGetLastError();
 }
 
@@ -559,7 +565,7 @@ hipError_t launch_up_decode(const Dims &d, const uint8_t *x8, const uint8_t *gu_
 
 hipError_t launch_down_decode(const Dims &d, const uint8_t *h8, const uint8_t *dn_blocks,
                               const uint8_t *dn_scales, const uint16_t *dn_bias, int32_t *topk_idx,
-                              float *topk_w, uint16_t *y, hipStream_t s) {
+                              float *topk_w, const uint16_t *residual, uint16_t *y, hipStream_t s) {
     if (d.T >= kStreamMinT) return hipErrorInvalidValue;
     const int64_t N = d.T * d.k;
     const uint8_t *hs8 = h8 + static_cast<size_t>(4 * N) * d.I;   // h8: mx8 matrix of 2N rows
@@ -567,10 +573,10 @@ hipError_t launch_down_decode(const Dims &d, const uint8_t *h8, const uint8_t *d
     const bool sc_lds = static_cast<int64_t>(slots_of(d)) * (d.I / 2) <= kDownScaleLds;
     const bool lds_a = mx8_bytes(2 * N, d.I) <= static_cast<size_t>(kStageLds);
     if (lds_a && sc_lds)
-        return down_tokens_n<1, 16, 3, true, true>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
+        return down_tokens_n<1, 16, 3, true, true>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, residual, y, s);
     if (sc_lds)
-        return down_tokens_n<1, 16, 3, false, true>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
-    return down_tokens_n<1, 16, 3, false, false>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, y, s);
+        return down_tokens_n<1, 16, 3, false, true>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, residual, y, s);
+    return down_tokens_n<1, 16, 3, false, false>(d, h8, hs8, dn_blocks, dn_scales, dn_bias, topk_idx, topk_w, residual, y, s);
 }
 
 }  // namespace moe

@@ -388,7 +388,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
 // per grid-stride step.
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ o,
                                                  const int32_t *__restrict__ slot_row, int64_t T,
-                                                 int H, int k, uint16_t *__restrict__ y) {
+                                                 int H, int k, const uint16_t *__restrict__ res,
+                                                 uint16_t *__restrict__ y) {
     const int per_row = H / 4;
     const int64_t total = T * per_row;
     for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < total;
@@ -400,6 +401,7 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ o,
             const float4 v = *reinterpret_cast<const float4 *>(o + static_cast<int64_t>(slot_row[t * k + j]) * H + d);
             s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
         }
+        if (res) add_residual4(s, res + t * H + d);
         const uint32_t lo = f32_to_bf16(s.x) | (static_cast<uint32_t>(f32_to_bf16(s.y)) << 16);
         const uint32_t hi = f32_to_bf16(s.z) | (static_cast<uint32_t>(f32_to_bf16(s.w)) << 16);
         *reinterpret_cast<uint2 *>(y + t * H + d) = make_uint2(lo, hi);
@@ -480,10 +482,10 @@ hipError_t launch_down_grouped(const Dims &d, const uint8_t *h8, const uint8_t *
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row, uint16_t *y,
-                          hipStream_t s) {
+hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row, const uint16_t *residual,
+                          uint16_t *y, hipStream_t s) {
     MOE_LAUNCH(k_combine, dim3(grid_for(d.T * (d.H / 4))), dim3(256), 0, s, o, slot_row,
-                       d.T, d.H, d.k, y);
+                       d.T, d.H, d.k, residual, y);
     return hipGetLastError();
 }
 

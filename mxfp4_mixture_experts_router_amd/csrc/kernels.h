@@ -68,8 +68,9 @@ hipError_t launch_down_grouped(const Dims &d, const uint8_t *h8, const uint8_t *
                                const int32_t *offsets, const float *sorted_w, float *o,
                                hipStream_t s);
 
+// combine (prefill): y[t, :] = bf16(sum_j o[slot_row[t*k + j], :] (+ residual[t, :])), slot order.
 hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row,
-                          uint16_t *y, hipStream_t s);
+                          const uint16_t *residual, uint16_t *y, hipStream_t s);
 
 // Decode path (T <= kDecodeMaxT). Below kStreamMinT tokens: router logits (launch_logits),
 // then an up-projection that also takes the top-k, then a down-projection that also adds
@@ -84,12 +85,14 @@ constexpr int64_t kStreamMinT = 4;
 hipError_t launch_up_decode(const Dims &d, const uint8_t *x8, const uint8_t *gu_blocks,
                             const uint8_t *gu_scales, const uint16_t *gu_bias, const double *logits,
                             int32_t *topk_idx, float *topk_w, uint8_t *h8, hipStream_t s);
-// down (T < kStreamMinT): y[t, :] = bf16(sum_j h[t*k + j] . Wdn[e_tj]^T + w[t, j] * bdn[e_tj]).
+// down (T < kStreamMinT): y[t, :] = bf16(sum_j h[t*k + j] . Wdn[e_tj]^T + w[t, j] * bdn[e_tj]
+// (+ residual[t, :])).
 hipError_t launch_down_decode(const Dims &d, const uint8_t *h8, const uint8_t *dn_blocks,
                               const uint8_t *dn_scales, const uint16_t *dn_bias, int32_t *topk_idx,
-                              float *topk_w, uint16_t *y, hipStream_t s);
-// y[t, :] = bf16(sum_{j < k} part[t*k + j, :]), slot order.
-hipError_t launch_combine_decode(const Dims &d, const float *part, uint16_t *y, hipStream_t s);
+                              float *topk_w, const uint16_t *residual, uint16_t *y, hipStream_t s);
+// y[t, :] = bf16(sum_{j < k} part[t*k + j, :] (+ residual[t, :])), slot order.
+hipError_t launch_combine_decode(const Dims &d, const float *part, const uint16_t *residual, uint16_t *y,
+                                 hipStream_t s);
 
 // Batched decode (kStreamMinT <= T <= kDecodeMaxT): the routed experts' weights streamed
 // once, routing (topk_idx / topk_w) from launch_route.
@@ -102,6 +105,11 @@ hipError_t launch_up_stream(const Dims &d, const uint8_t *x8, const uint8_t *gu_
 hipError_t launch_down_stream(const Dims &d, const uint8_t *h8, const uint8_t *dn_blocks, const uint8_t *dn_scales,
                               const uint16_t *dn_bias, const int32_t *topk_idx, const float *topk_w, float *part,
                               hipStream_t s);
+
+// Pre-LN RMSNorm: xn[t, :] = bf16(x[t, :] * gamma / sqrt(mean_h x[t, h]^2 + eps)), in double,
+// one rounding (nearest, ties to even). One workgroup per token; H a multiple of 8.
+hipError_t launch_rmsnorm(const Dims &d, const uint16_t *x, const uint16_t *gamma, double eps, uint16_t *xn,
+                          hipStream_t s);
 
 // bf16 [rows, cols] -> mx8 matrix (mx_mfma.h).
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int cols, uint8_t *q8, hipStream_t s);

@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert moe.abi_version() == 2
-    assert "#define MOE_MXFP4_ABI_VERSION 2" in open(HEADER).read()
+    assert moe.abi_version() == 3
+    assert "#define MOE_MXFP4_ABI_VERSION 3" in open(HEADER).read()
 
 
 def shape(T=1, H=2880, I=2880, E=32, k=4, alpha=1.702, limit=7.0):
@@ -152,6 +152,54 @@ def test_stage_entry_points_validate(lib):
     assert lib.moe_mxfp4_combine(ctypes.byref(s), A, A, None, None) == EINVAL
     bad = shape(E=300)
     assert lib.moe_mxfp4_permute(ctypes.byref(bad), A, A, A, A, A, A, None) == ESHAPE
+
+
+def fwd_prenorm(lib, s, timed=False, **over):
+    args = dict(x=A, nw=A, eps=1e-5, rw=A, rb=A, gb=A, gs=A, gbias=A, db=A, ds=A, dbias=A, y=A,
+                idx=None, w=None, ws=0x100000, wsb=1 << 40, stream=None)
+    args.update(over)
+    call = [ctypes.byref(s)] + [args[k] for k in ("x", "nw", "eps", "rw", "rb", "gb", "gs", "gbias", "db",
+                                                  "ds", "dbias", "y", "idx", "w", "ws", "wsb", "stream")]
+    if timed:
+        n = ctypes.c_int(-1)
+        return lib.moe_mxfp4_forward_prenorm_timed(*call, None, 0, ctypes.byref(n))
+    return lib.moe_mxfp4_forward_prenorm(*call)
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(nw=None), EINVAL, "norm_w"), (dict(nw=A + 2), EALIGN, "norm_w"),
+    (dict(eps=float("nan")), EINVAL, "norm_eps"), (dict(eps=-1e-6), EINVAL, "norm_eps"),
+    (dict(eps=float("inf")), EINVAL, "norm_eps"), (dict(x=None), EINVAL, "x"),
+    (dict(ws=None), EWORKSPACE, "workspace"),
+])
+def test_forward_prenorm_validates(lib, over, code, msg):
+    s = shape()
+    assert fwd_prenorm(lib, s, **over) == code
+    assert msg in lib.moe_mxfp4_last_error().decode()
+
+
+def test_forward_prenorm_edges(lib):
+    assert fwd_prenorm(lib, shape(k=0), nw=None) == ESHAPE          # shape first
+    assert fwd_prenorm(lib, shape(T=0), nw=None) == 0               # no tokens: no pointer read
+    assert fwd_prenorm(lib, shape(), timed=True) == EINVAL          # events required
+    assert "events" in lib.moe_mxfp4_last_error().decode()
+    # the pre-norm block needs no more workspace than the plain layer
+    s = shape()
+    need = moe.workspace_bytes(1, 2880, 2880, 32, 4)
+    assert fwd_prenorm(lib, s, wsb=need - 1) == EWORKSPACE
+
+
+def test_rmsnorm_validates(lib):
+    assert lib.moe_mxfp4_rmsnorm(A, A, 4, 60, 1e-5, A, None) == ESHAPE
+    assert lib.moe_mxfp4_rmsnorm(A, A, 4, 0, 1e-5, A, None) == ESHAPE
+    assert lib.moe_mxfp4_rmsnorm(A, A, -1, 64, 1e-5, A, None) == EINVAL
+    assert lib.moe_mxfp4_rmsnorm(A, A, (1 << 24) + 1, 64, 1e-5, A, None) == ESHAPE
+    assert lib.moe_mxfp4_rmsnorm(A, A, 4, 64, float("nan"), A, None) == EINVAL
+    assert lib.moe_mxfp4_rmsnorm(A, A, 4, 64, -1.0, A, None) == EINVAL
+    assert lib.moe_mxfp4_rmsnorm(A, None, 4, 64, 1e-5, A, None) == EINVAL
+    assert lib.moe_mxfp4_rmsnorm(A, A + 8, 4, 64, 1e-5, A, None) == EALIGN
+    assert lib.moe_mxfp4_rmsnorm(A, A, 4, 64, 1e-5, A + 2, None) == EALIGN
+    assert lib.moe_mxfp4_rmsnorm(None, None, 0, 64, 1e-5, None, None) == 0   # empty: no launch
 
 
 def test_mx8_format_entry_points(lib):

@@ -328,12 +328,14 @@ class _HipEvents:
             self.lib.hipEventDestroy(self.c.c_void_p(ev))
 
 
-@pytest.mark.parametrize("T,launches", [(1, 3), (3, 3), (4, 4), (17, 4), (65, 5)])
-def test_forward_timed_matches_forward(T, launches):
+@pytest.mark.parametrize("T,launches,prenorm", [(1, 3, False), (3, 3, False), (4, 4, False), (17, 4, False),
+                                                (65, 5, False), (1, 4, True), (17, 5, True), (65, 6, True)])
+def test_forward_timed_matches_forward(T, launches, prenorm):
     import ctypes
     cfg = CONFIGS["tiny"]
     inp = upload(make_inputs(cfg, seed=5, T=T))
-    y_ref = _forward(inp, cfg.k, cfg)
+    norm = dict(norm_weight=inp["norm_w"], norm_eps=1e-5) if prenorm else {}
+    y_ref = _forward(inp, cfg.k, cfg, **norm)
     H, I, E = cfg.H, cfg.I, cfg.E
     shape = moe._shape(T, H, I, E, cfg.k, cfg.alpha, cfg.limit)
     ws = torch.empty(max(moe.workspace_bytes(T, H, I, E, cfg.k), 256), dtype=torch.uint8, device="cuda")
@@ -343,11 +345,14 @@ def test_forward_timed_matches_forward(T, launches):
     arr = (ctypes.c_void_p * len(evs))(*evs)
     n = ctypes.c_int(-1)
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    st = moe.load_library().moe_mxfp4_forward_timed(
-        ctypes.byref(shape), P(inp["x"]), P(inp["router_w"]), P(inp["router_b"]), P(inp["gu_blocks"]),
-        P(inp["gu_scales"]), P(inp["gu_bias"]), P(inp["dn_blocks"]), P(inp["dn_scales"]),
-        P(inp["dn_bias"]), P(y), None, None, P(ws), ws.numel(),
-        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), arr, len(evs), ctypes.byref(n))
+    lib = moe.load_library()
+    tail = (P(inp["router_w"]), P(inp["router_b"]), P(inp["gu_blocks"]), P(inp["gu_scales"]), P(inp["gu_bias"]),
+            P(inp["dn_blocks"]), P(inp["dn_scales"]), P(inp["dn_bias"]), P(y), None, None, P(ws), ws.numel(),
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), arr, len(evs), ctypes.byref(n))
+    if prenorm:
+        st = lib.moe_mxfp4_forward_prenorm_timed(ctypes.byref(shape), P(inp["x"]), P(inp["norm_w"]), 1e-5, *tail)
+    else:
+        st = lib.moe_mxfp4_forward_timed(ctypes.byref(shape), P(inp["x"]), *tail)
     assert st == 0, moe.load_library().moe_mxfp4_last_error()
     torch.cuda.synchronize()
     assert n.value == launches
@@ -365,3 +370,85 @@ def test_forward_zero_tokens():
     inp = upload(make_inputs(cfg, T=0))
     y = _forward(inp, cfg.k, cfg)
     assert y.shape == (0, cfg.H)
+
+
+# ----------------------------------------------------------------------------- pre-norm block
+
+def _rms_rows(R, C, seed):
+    """bf16 rows of mixed scale: N(0, 1) rows, rows scaled by 2^-20 and 2^20, a constant row
+    and a row of zeros (eps keeps it finite: every output is zero)."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((R, C)).astype(np.float32)
+    if R >= 5:
+        v[1] *= 2.0 ** -20
+        v[2] *= 2.0 ** 20
+        v[3] = 0.75
+        v[4] = 0.0
+    g = (1.0 + 0.1 * rng.standard_normal(C)).astype(np.float32)
+    return bf16_bits_from_f32(v), bf16_bits_from_f32(g)
+
+
+def _near_bf16_tie(exact: np.ndarray) -> np.ndarray:
+    """Where a value lies within 2^-40 relative of a midpoint between two bf16 numbers: only
+    there may a different (correct to the last bits of a double) sum of squares change the
+    rounding."""
+    m, e = np.frexp(exact)
+    frac = np.abs(np.ldexp(m, 8)) % 1.0
+    return np.abs(frac - 0.5) < 2.0 ** -40 * 256
+
+
+@pytest.mark.parametrize("R,C,eps", [(1, 2880, 1e-5), (37, 96, 1e-5), (300, 2880, 1e-5), (6, 8, 1e-5),
+                                     (5, 4104, 1e-5), (9, 2880, 0.0), (5, 2880, 1e-2)])
+def test_rmsnorm_matches_oracle(R, C, eps):
+    x, g = _rms_rows(R, C, seed=R + C)
+    if eps == 0.0:
+        x[4] = x[0]                       # no zero row without eps
+    want, exact = oracle.rmsnorm(x, g, eps, with_exact=True)
+    got = bf16_bits(moe.rmsnorm(to_dev(x), to_dev(g), eps))
+    bad = got != want
+    assert not np.any(bad & ~_near_bf16_tie(exact)), np.argwhere(bad)[:8]
+    assert bad.sum() <= 2
+
+
+PRENORM_CASES = [
+    # (config, T override, H, I, E, k, tokens compared); the residual is added by the last
+    # kernel of each launch sequence: the down-projection (T < 4), the slot combine (4..64),
+    # the prefill combine (> 64)
+    ("tiny", None, None, None, None, None, 64),
+    ("tiny", 1, 96, 64, 5, 2, 1),
+    ("tiny", 3, 96, 64, 5, 2, 3),
+    ("tiny", 5, 96, 64, 5, 2, 5),
+    ("tiny", 65, 96, 64, 5, 2, 65),
+    ("decode_20b", None, None, None, None, None, 1),
+    ("batched_decode_20b", None, None, None, None, None, 64),
+    ("prefill_20b", None, None, None, None, None, 24),
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k,n_cmp", PRENORM_CASES)
+def test_forward_prenorm_matches_oracle(name, T, H, I, E, k, n_cmp):
+    cfg = CONFIGS[name]
+    over = {key: v for key, v in dict(H=H, I=I, E=E, k=k).items() if v is not None}
+    cfg = cfg.with_(**over)
+    T = cfg.T if T is None else T
+    inp = make_inputs(cfg, seed=3, T=T)
+    tokens = _sample(T, n_cmp, seed=T + 1)
+    eps = 1e-5
+    ref = oracle.forward_prenorm(inp, cfg.k, tokens=tokens, alpha=cfg.alpha, limit=cfg.limit, eps=eps)
+    d = upload(inp)
+    y, idx, w = _forward(d, cfg.k, cfg, return_topk=True, norm_weight=d["norm_w"], norm_eps=eps)
+    # the normalized rows the layer ran on
+    xn = bf16_bits(moe.rmsnorm(d["x"], d["norm_w"], eps))[tokens]
+    np.testing.assert_array_equal(xn, ref["xn"])
+    idx_np = idx.cpu().numpy()[tokens]
+    ok = check_selection(idx_np, ref, cfg.H, cfg.k)
+    np.testing.assert_allclose(w.cpu().numpy()[tokens][ok], ref["w"][ok], rtol=1e-6, atol=1e-7)
+    assert_close_rows(bf16_to_f64(y)[tokens][ok], ref["y"][ok], f"prenorm y ({name}, T={T})")
+    # the residual: y - x is the layer's output on xn, so it must also match the plain layer
+    # run on the oracle's xn (to the tolerance of one more bf16 rounding of y)
+    d_n = dict(d, x=to_dev(np.ascontiguousarray(oracle.rmsnorm(inp["x"], inp["norm_w"], eps))))
+    y_plain = _forward(d_n, cfg.k, cfg)
+    x_np = bf16_to_f64(d["x"])[tokens]
+    diff = bf16_to_f64(y)[tokens] - x_np - bf16_to_f64(y_plain)[tokens]
+    bound = 2.0 ** -8 * (np.abs(bf16_to_f64(y)[tokens]) + np.abs(bf16_to_f64(y_plain)[tokens]))
+    assert np.all(np.abs(diff) <= bound + 1e-30)
