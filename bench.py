@@ -44,9 +44,9 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 LLC_BYTES = 256 << 20            # MI355X Infinity Cache
 KERNEL_SOURCES = {               # kernel -> files whose text defines it
-    "route": ["route.hip", "device_common.h"],
+    "route": ["route.hip", "device_common.h", "rms.h"],
     "permute": ["permute.hip", "device_common.h"],
-    "logits": ["route.hip", "device_common.h"],
+    "logits": ["route.hip", "device_common.h", "rms.h"],
     "up_decode": ["gemm_decode.hip", "device_common.h", "weight_tiles.h", "routing.h", "topk.h"],
     "down_decode": ["gemm_decode.hip", "device_common.h", "weight_tiles.h", "routing.h"],
     "up_stream": ["gemm_stream.hip", "device_common.h", "weight_tiles.h", "routing.h", "lds_dma.h"],
@@ -55,7 +55,7 @@ KERNEL_SOURCES = {               # kernel -> files whose text defines it
     "down_grouped": ["gemm_grouped.hip", "device_common.h", "lds_dma.h"],
     "combine": ["gemm_grouped.hip", "device_common.h", "lds_dma.h"],
     "combine_decode": ["gemm_decode.hip", "device_common.h"],
-    "rmsnorm": ["norm.hip", "device_common.h"],
+    "rmsnorm": ["norm.hip", "device_common.h", "rms.h"],
 }
 FEW_STAGES = ["logits", "up_decode", "down_decode"]                       # T < 4
 STREAM_STAGES = ["route", "up_stream", "down_stream", "combine_decode"]     # 4 <= T <= 64
@@ -63,8 +63,10 @@ PREFILL_STAGES = ["route", "permute", "up_grouped", "down_grouped", "combine"]
 
 
 def stages_of(T: int, prenorm: bool = False):
+    """Kernels of one layer call (GPT-OSS shapes). In the pre-norm block the decode routers
+    normalize the rows themselves; the prefill sequence starts with an RMSNorm kernel."""
     st = FEW_STAGES if T < 4 else (STREAM_STAGES if T <= 64 else PREFILL_STAGES)
-    return (["rmsnorm"] if prenorm else []) + st
+    return (["rmsnorm"] if prenorm and T > 64 else []) + st
 
 
 def kernel_source_sha(kernel: str) -> str:
@@ -294,10 +296,11 @@ def kernel_work(wl: Workload, kernel: str, D: float):
     res = T * H * 2 if wl.prenorm else 0      # the residual the last kernel adds
     if kernel == "rmsnorm":
         return 2 * T * H * 2 + H * 2, 0
+    gam = H * 2 if wl.prenorm and T <= 64 else 0    # the decode routers also read the norm weights
     if kernel == "route":
-        return T * H * 2 + E * H * 2 + E * 2 + N * 8, 2 * T * E * H
+        return T * H * 2 + E * H * 2 + E * 2 + N * 8 + gam, 2 * T * E * H
     if kernel == "logits":
-        return T * H * 2 + E * H * 2 + E * 2 + T * E * 8, 2 * T * E * H
+        return T * H * 2 + E * H * 2 + E * 2 + T * E * 8 + gam, 2 * T * E * H
     if kernel == "permute":
         return N * 8 + (E + 1) * 4 + N * 12, 0
     if kernel in ("up_decode", "up_stream"):

@@ -121,12 +121,14 @@ moe_status_t moe_mxfp4_forward(const moe_mxfp4_shape_t *shape,
  *   y[t, :]  = bf16(x[t, :] + layer(xn)[t, :])
  * The normalization runs in double and rounds once to bf16 (nearest, ties to even), as
  * moe_mxfp4_rmsnorm; the layer (steps 1-6) then runs on xn, and its last kernel adds the
- * residual x before the one bf16 rounding of y. Arguments as moe_mxfp4_forward, plus
+ * residual x before the one bf16 rounding of y. On the few-token path (T <= 64, H and I <= 4096;
+ * H <= 3584 from 4 tokens) the router kernel normalizes the rows it loads, so the block takes
+ * as many kernels as the plain layer; otherwise one more kernel writes xn to the workspace
+ * first. Arguments as moe_mxfp4_forward, plus
  *  norm_w    [H] bf16, 16-byte aligned (RMSNorm scale; MOE_EINVAL if NULL, MOE_EALIGN if
  *            misaligned)
  *  norm_eps  finite and >= 0 (MOE_EINVAL otherwise)
  * topk_idx / topk_w are the routing of xn. The workspace size is moe_mxfp4_workspace_bytes().
- * One more kernel than moe_mxfp4_forward.
  */
 moe_status_t moe_mxfp4_forward_prenorm(const moe_mxfp4_shape_t *shape,
                                        const moe_bf16_t *x,
@@ -166,8 +168,8 @@ moe_status_t moe_mxfp4_forward_timed(const moe_mxfp4_shape_t *shape,
                                      void *workspace, size_t workspace_bytes, void *stream,
                                      void *const *events, int n_events, int *n_launches);
 
-/* moe_mxfp4_forward_prenorm with the instrumentation of moe_mxfp4_forward_timed; launch 0
- * is the RMSNorm, the rest follow the counts above. */
+/* moe_mxfp4_forward_prenorm with the instrumentation of moe_mxfp4_forward_timed. Launch
+ * counts as there, plus the RMSNorm kernel (launch 0) where the router does not normalize. */
 moe_status_t moe_mxfp4_forward_prenorm_timed(const moe_mxfp4_shape_t *shape,
                                              const moe_bf16_t *x,
                                              const moe_bf16_t *norm_w, double norm_eps,

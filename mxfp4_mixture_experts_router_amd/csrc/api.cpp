@@ -221,19 +221,27 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
         if (n_launches) *n_launches = launched;          \
     } while (0)
 
-    const moe_bf16_t *residual = nullptr;
+    // pre-norm block: the decode routers normalize the token rows they load; otherwise a
+    // kernel of its own writes them to the workspace
+    const moe_bf16_t *residual = norm_w ? x : nullptr;
+    const moe_bf16_t *gamma = nullptr;
     if (norm_w) {
-        moe_bf16_t *xn = reinterpret_cast<moe_bf16_t *>(ws + L.xn);
-        STEP(moe::launch_rmsnorm(d, x, norm_w, norm_eps, xn, s), "rmsnorm");
-        residual = x;
-        x = xn;
+        const bool fused = moe::use_decode_path(shape->T, shape->H, shape->I) &&
+                           (shape->T < moe::kStreamMinT || moe::route_normalizes(d));
+        if (fused) {
+            gamma = norm_w;
+        } else {
+            moe_bf16_t *xn = reinterpret_cast<moe_bf16_t *>(ws + L.xn);
+            STEP(moe::launch_rmsnorm(d, x, norm_w, norm_eps, xn, s), "rmsnorm");
+            x = xn;
+        }
     }
 
     if (moe::use_decode_path(shape->T, shape->H, shape->I)) {
         float *part = reinterpret_cast<float *>(ws + L.part);
         uint8_t *x8 = ws + L.x8, *h8 = ws + L.h8;
         if (shape->T >= moe::kStreamMinT) {
-            STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, x8, s), "route");
+            STEP(moe::launch_route(d, x, gamma, norm_eps, router_w, router_b, idx, w, nullptr, x8, s), "route");
             STEP(moe::launch_up_stream(d, x8, gu_blocks, gu_scales, gu_bias, idx, h8, s), "up (stream)");
             STEP(moe::launch_down_stream(d, h8, dn_blocks, dn_scales, dn_bias, idx, w, part, s), "down (stream)");
             STEP(moe::launch_combine_decode(d, part, residual, y, s), "combine (decode)");
@@ -241,13 +249,13 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
         }
         // few tokens: logits in a multi-block kernel, top-k + softmax inside the up-projection
         double *logits = reinterpret_cast<double *>(ws + L.logits);
-        STEP(moe::launch_logits(d, x, router_w, router_b, logits, x8, s), "router logits");
+        STEP(moe::launch_logits(d, x, gamma, norm_eps, router_w, router_b, logits, x8, s), "router logits");
         STEP(moe::launch_up_decode(d, x8, gu_blocks, gu_scales, gu_bias, logits, idx, w, h8, s), "up (decode)");
         STEP(moe::launch_down_decode(d, h8, dn_blocks, dn_scales, dn_bias, idx, w, residual, y, s), "down (decode)");
         return ok();
     }
     uint8_t *x8 = ws + L.x8, *h8 = ws + L.h8;
-    STEP(moe::launch_route(d, x, router_w, router_b, idx, w, nullptr, x8, s), "route");
+    STEP(moe::launch_route(d, x, nullptr, 0.0, router_w, router_b, idx, w, nullptr, x8, s), "route");
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
     int32_t *sorted_token = reinterpret_cast<int32_t *>(ws + L.sorted_token);
     float *sorted_w = reinterpret_cast<float *>(ws + L.sorted_w);
@@ -329,7 +337,7 @@ MOE_EXPORT moe_status_t moe_mxfp4_route(const moe_mxfp4_shape_t *shape, const mo
     REQUIRE(router_b, "router_b");
     REQUIRE(topk_idx, "topk_idx");
     REQUIRE(topk_w, "topk_w");
-    LAUNCH(moe::launch_route(dims_of(shape), x, router_w, router_b, topk_idx, topk_w, logits, nullptr,
+    LAUNCH(moe::launch_route(dims_of(shape), x, nullptr, 0.0, router_w, router_b, topk_idx, topk_w, logits, nullptr,
                              static_cast<hipStream_t>(stream)), "route");
     return ok();
 }

@@ -42,13 +42,19 @@ struct Dims {
 
 // Router logits only (double [T, E]); for few tokens, where the top-k runs in the
 // up-projection. Needs H <= 6144. Also writes x as an mx8 matrix (T rows of H, mx_mfma.h).
-hipError_t launch_logits(const Dims &d, const uint16_t *x, const uint16_t *router_w,
-                         const uint16_t *router_b, double *logits, uint8_t *x8, hipStream_t s);
+// With gamma != nullptr the router and the mx8 rows take the RMSNorm of x (rms.h) instead.
+hipError_t launch_logits(const Dims &d, const uint16_t *x, const uint16_t *gamma, double eps,
+                         const uint16_t *router_w, const uint16_t *router_b, double *logits, uint8_t *x8,
+                         hipStream_t s);
+
+// Whether launch_route can normalize the token rows itself (gamma != nullptr): the
+// one-workgroup-per-token router (T <= kDecodeMaxT, H <= 3584).
+inline bool route_normalizes(const Dims &d) { return d.T <= kDecodeMaxT && d.H <= 3584; }
 
 // Router, top-k and softmax; with x8 != nullptr (T <= kDecodeMaxT) also writes x as an mx8
-// matrix.
-hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *router_w,
-                        const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
+// matrix. With gamma != nullptr (only where route_normalizes) both take the RMSNorm of x.
+hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *gamma, double eps,
+                        const uint16_t *router_w, const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
                         float *logits, uint8_t *x8, hipStream_t s);
 
 hipError_t launch_permute(const Dims &d, const int32_t *topk_idx, const float *topk_w,

@@ -10,7 +10,9 @@
 // the identical summation sequence here) resolve to the lower expert index.
 #include "device_common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 #include "mx_mfma.h"
+#include "rms.h"
 #include "topk.h"
 
 #include <math.h>
@@ -37,14 +39,19 @@ __device__ __forceinline__ double dot8(uint4 xv, uint4 wv, double acc) {
 // row and the wave's four router rows are loaded with every load in flight at once (lane l
 // covers h = 8l + 512i, i < NI, NI = ceil(H / 512)); wavefront w handles experts
 // 4w .. 4w+3, then 32 + 4w .. and so on.
+// With gamma (the pre-norm block), the token row is first normalized (rms.h): every
+// wavefront holds the whole row, so each sums its squares itself, in the same order; wavefront
+// w normalizes the 512-element chunk w into LDS, and every wavefront reads the normalized row
+// back. The first router rows are requested before all this and stay in flight.
 template <int NI>
 __global__ __launch_bounds__(512) void k_route_token(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma, double eps, const uint16_t *__restrict__ wr,
     const uint16_t *__restrict__ br, int H, int E, int k, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w, float *__restrict__ logits_out, uint8_t *__restrict__ x8, int T) {
     constexpr int kEPW = 4;
     __shared__ double lg[kMaxE];
     __shared__ __attribute__((aligned(16))) uint64_t s_tk[kTopkScratch];
+    __shared__ __attribute__((aligned(16))) uint16_t s_xn[NI * 8 * kWave];   // the normalized row
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t t = blockIdx.x;
     const uint16_t *xr = x + t * H;
@@ -54,8 +61,10 @@ __global__ __launch_bounds__(512) void k_route_token(
         const int h = 8 * lane + 8 * kWave * i;
         xv[i] = h < H ? *reinterpret_cast<const uint4 *>(xr + h) : zero4();
     }
-    for (int e0 = kEPW * wave; e0 < E; e0 += kEPW * 8) {
-        uint4 a[kEPW][NI];
+    const int hw = 8 * lane + 8 * kWave * wave;        // this wavefront's chunk to normalize
+    const uint4 gv = gamma && wave < NI && hw < H ? *reinterpret_cast<const uint4 *>(gamma + hw) : zero4();
+    uint4 a[kEPW][NI];
+    auto load_rows = [&](int e0) {
 #pragma unroll
         for (int q = 0; q < kEPW; ++q) {
             const int e = e0 + q < E ? e0 + q : e0;
@@ -66,6 +75,28 @@ __global__ __launch_bounds__(512) void k_route_token(
                 a[q][i] = h < H ? *reinterpret_cast<const uint4 *>(wrow + h) : zero4();
             }
         }
+    };
+    if (kEPW * wave < E) load_rows(kEPW * wave);
+    if (gamma) {
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) ss = sumsq8(xv[i], ss);
+        const double r = rms_scale(wave_sum(ss), H, eps);
+        uint4 mine = xv[0];
+#pragma unroll
+        for (int i = 1; i < NI; ++i)
+            if (i == wave) mine = xv[i];
+        if (wave < NI && hw < H) *reinterpret_cast<uint4 *>(s_xn + hw) = rms_apply8(mine, gv, r);
+        wait_lgkm0();
+        barrier_only();
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int h = 8 * lane + 8 * kWave * i;
+            xv[i] = h < H ? *reinterpret_cast<const uint4 *>(s_xn + h) : zero4();
+        }
+    }
+    for (int e0 = kEPW * wave; e0 < E; e0 += kEPW * 8) {
+        if (e0 != kEPW * wave) load_rows(e0);
         double acc[kEPW];
 #pragma unroll
         for (int q = 0; q < kEPW; ++q) {
@@ -87,7 +118,7 @@ __global__ __launch_bounds__(512) void k_route_token(
     if (wave == 0)
         topk_softmax_wave(lg, E, k, lane, topk_idx + t * k, topk_w + t * k, nullptr, nullptr,
                           logits_out ? logits_out + t * E : nullptr, s_tk);
-    if (x8 != nullptr) write_mx8_row(xr, H, x8, T, t);
+    if (x8 != nullptr) write_mx8_row(gamma ? s_xn : xr, H, x8, T, t);   // s_xn: written before the barrier
 }
 
 // Logits only, for few tokens (the top-k then runs in the up-projection's prologue): block
@@ -95,32 +126,65 @@ __global__ __launch_bounds__(512) void k_route_token(
 // h = 8l + 512(w + 4i)) and their partial sums are added in wavefront order.
 //   logits[t, e] = sum_h x[t, h] * Wr[e, h] + br[e]     (double)
 // One extra block per token (the last in x) writes the token as an mx8 row of x8 (T rows)
-// for the expert GEMMs.
+// for the expert GEMMs. With gamma (the pre-norm block) every block first normalizes the
+// token row (rms.h); all blocks sum the squares in the same order (per lane, across each
+// wavefront, then the wavefronts in order), so they agree on every normalized value.
 template <int NIQ>
-__global__ __launch_bounds__(256) void k_logits(const uint16_t *__restrict__ x,
-                                                const uint16_t *__restrict__ wr,
+__global__ __launch_bounds__(256) void k_logits(const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma,
+                                                double eps, const uint16_t *__restrict__ wr,
                                                 const uint16_t *__restrict__ br, int H, int E,
                                                 double *__restrict__ logits, uint8_t *__restrict__ x8, int T) {
     __shared__ double part[4][2];
+    __shared__ double s_ss[4];
+    __shared__ __attribute__((aligned(16))) uint16_t s_xn[NIQ * 4 * 8 * kWave];   // the normalized row
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t t = blockIdx.y;
-    if (blockIdx.x == gridDim.x - 1) {   // the extra block: token t as an mx8 row
+    const bool extra = blockIdx.x == gridDim.x - 1;
+    if (extra && gamma == nullptr) {   // the extra block: token t as an mx8 row
         write_mx8_row(x + t * H, H, x8, T, t);
         return;
     }
     const int e0 = 2 * blockIdx.x;
     const bool has2 = e0 + 1 < E;
     const uint16_t *xr = x + t * H;
-    const uint16_t *w0 = wr + static_cast<int64_t>(e0) * H;
-    const uint16_t *w1 = wr + static_cast<int64_t>(has2 ? e0 + 1 : e0) * H;
+    const int ea = extra ? 0 : e0;                      // the extra block loads no router rows
+    const int eb = extra || !has2 ? ea : e0 + 1;
+    const uint16_t *w0 = wr + static_cast<int64_t>(ea) * H;
+    const uint16_t *w1 = wr + static_cast<int64_t>(eb) * H;
     uint4 xv[NIQ], a[NIQ], b[NIQ];
 #pragma unroll
     for (int i = 0; i < NIQ; ++i) {
         const int h = 8 * lane + 8 * kWave * (wave + 4 * i);
         const bool ok = h < H;
         xv[i] = ok ? *reinterpret_cast<const uint4 *>(xr + h) : zero4();
-        a[i] = ok ? *reinterpret_cast<const uint4 *>(w0 + h) : zero4();
-        b[i] = ok ? *reinterpret_cast<const uint4 *>(w1 + h) : zero4();
+        a[i] = ok && !extra ? *reinterpret_cast<const uint4 *>(w0 + h) : zero4();
+        b[i] = ok && !extra ? *reinterpret_cast<const uint4 *>(w1 + h) : zero4();
+    }
+    if (gamma) {
+        uint4 gv[NIQ];
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < NIQ; ++i) {
+            const int h = 8 * lane + 8 * kWave * (wave + 4 * i);
+            gv[i] = h < H ? *reinterpret_cast<const uint4 *>(gamma + h) : zero4();
+            ss = sumsq8(xv[i], ss);
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) s_ss[wave] = ss;
+        __syncthreads();
+        const double r = rms_scale(((s_ss[0] + s_ss[1]) + s_ss[2]) + s_ss[3], H, eps);
+#pragma unroll
+        for (int i = 0; i < NIQ; ++i) xv[i] = rms_apply8(xv[i], gv[i], r);
+        if (extra) {
+#pragma unroll
+            for (int i = 0; i < NIQ; ++i) {
+                const int h = 8 * lane + 8 * kWave * (wave + 4 * i);
+                if (h < H) *reinterpret_cast<uint4 *>(s_xn + h) = xv[i];
+            }
+            __syncthreads();
+            write_mx8_row(s_xn, H, x8, T, t);
+            return;
+        }
     }
     double acc0 = 0.0, acc1 = 0.0;
 #pragma unroll
@@ -280,42 +344,44 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
 }
 
 template <int NI>
-void launch_token(const Dims &d, const uint16_t *x, const uint16_t *w, const uint16_t *b,
-                  int32_t *idx, float *wt, float *logits, uint8_t *x8, hipStream_t s) {
-    MOE_LAUNCH((k_route_token<NI>), dim3(static_cast<unsigned>(d.T)), dim3(512), 0, s, x, w,
+void launch_token(const Dims &d, const uint16_t *x, const uint16_t *gamma, double eps, const uint16_t *w,
+                  const uint16_t *b, int32_t *idx, float *wt, float *logits, uint8_t *x8, hipStream_t s) {
+    MOE_LAUNCH((k_route_token<NI>), dim3(static_cast<unsigned>(d.T)), dim3(512), 0, s, x, gamma, eps, w,
                        b, d.H, d.E, d.k, idx, wt, logits, x8, static_cast<int>(d.T));
 }
 
 }  // namespace
 
-hipError_t launch_logits(const Dims &d, const uint16_t *x, const uint16_t *router_w,
-                         const uint16_t *router_b, double *logits, uint8_t *x8, hipStream_t s) {
+hipError_t launch_logits(const Dims &d, const uint16_t *x, const uint16_t *gamma, double eps,
+                         const uint16_t *router_w, const uint16_t *router_b, double *logits, uint8_t *x8,
+                         hipStream_t s) {
     if (d.T <= 0) return hipSuccess;
     const int niq = (d.H + 2047) / 2048;
     const dim3 grid(static_cast<unsigned>((d.E + 1) / 2 + 1), static_cast<unsigned>(d.T));
     switch (niq) {
-        case 1: MOE_LAUNCH((k_logits<1>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
-        case 2: MOE_LAUNCH((k_logits<2>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
-        case 3: MOE_LAUNCH((k_logits<3>), grid, dim3(256), 0, s, x, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
+        case 1: MOE_LAUNCH((k_logits<1>), grid, dim3(256), 0, s, x, gamma, eps, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
+        case 2: MOE_LAUNCH((k_logits<2>), grid, dim3(256), 0, s, x, gamma, eps, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
+        case 3: MOE_LAUNCH((k_logits<3>), grid, dim3(256), 0, s, x, gamma, eps, router_w, router_b, d.H, d.E, logits, x8, static_cast<int>(d.T)); break;
         default: return hipErrorInvalidValue;   // H > 6144: the caller uses launch_route
     }
     return hipGetLastError();
 }
 
-hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *router_w,
-                        const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
+hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *gamma, double eps,
+                        const uint16_t *router_w, const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
                         float *logits, uint8_t *x8, hipStream_t s) {
     if (d.T <= 0) return hipSuccess;
     const int ni = (d.H + 511) / 512;
+    if (gamma != nullptr && !route_normalizes(d)) return hipErrorInvalidValue;
     if (d.T <= kDecodeMaxT && ni <= 7) {
         switch (ni) {
-            case 1: launch_token<1>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
-            case 2: launch_token<2>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
-            case 3: launch_token<3>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
-            case 4: launch_token<4>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
-            case 5: launch_token<5>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
-            case 6: launch_token<6>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
-            default: launch_token<7>(d, x, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            case 1: launch_token<1>(d, x, gamma, eps, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            case 2: launch_token<2>(d, x, gamma, eps, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            case 3: launch_token<3>(d, x, gamma, eps, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            case 4: launch_token<4>(d, x, gamma, eps, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            case 5: launch_token<5>(d, x, gamma, eps, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            case 6: launch_token<6>(d, x, gamma, eps, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
+            default: launch_token<7>(d, x, gamma, eps, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
         }
     } else {
         const dim3 grid(static_cast<unsigned>((d.T + kRT - 1) / kRT));

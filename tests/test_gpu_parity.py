@@ -329,7 +329,7 @@ class _HipEvents:
 
 
 @pytest.mark.parametrize("T,launches,prenorm", [(1, 3, False), (3, 3, False), (4, 4, False), (17, 4, False),
-                                                (65, 5, False), (1, 4, True), (17, 5, True), (65, 6, True)])
+                                                (65, 5, False), (1, 3, True), (17, 4, True), (65, 6, True)])
 def test_forward_timed_matches_forward(T, launches, prenorm):
     import ctypes
     cfg = CONFIGS["tiny"]
