@@ -56,17 +56,25 @@ KERNEL_SOURCES = {               # kernel -> files whose text defines it
     "combine": ["gemm_grouped.hip", "device_common.h", "lds_dma.h"],
     "combine_decode": ["gemm_decode.hip", "device_common.h"],
     "rmsnorm": ["norm.hip", "device_common.h", "rms.h"],
+    "up_bank": ["gemm_bank.hip", "device_common.h"],
+    "down_bank": ["gemm_bank.hip", "device_common.h"],
 }
 FEW_STAGES = ["logits", "up_decode", "down_decode"]                       # T < 4
 STREAM_STAGES = ["route", "up_stream", "down_stream", "combine_decode"]     # 4 <= T <= 64
 PREFILL_STAGES = ["route", "permute", "up_grouped", "down_grouped", "combine"]
 
 
-def stages_of(T: int, prenorm: bool = False):
-    """Kernels of one layer call (GPT-OSS shapes). In the pre-norm block the decode routers
-    normalize the rows themselves; the prefill sequence starts with an RMSNorm kernel."""
+BANK_STAGES = ["route", "permute", "up_bank", "down_bank", "combine"]
+
+
+def stages_of(T: int, variant: str = "layer"):
+    """Kernels of one call (GPT-OSS shapes). In the pre-norm block the decode routers
+    normalize the rows themselves; the prefill sequence starts with an RMSNorm kernel. The
+    dequantized-bank variant takes the grouped sequence at every T."""
+    if variant == "dequantized":
+        return BANK_STAGES
     st = FEW_STAGES if T < 4 else (STREAM_STAGES if T <= 64 else PREFILL_STAGES)
-    return (["rmsnorm"] if prenorm and T > 64 else []) + st
+    return (["rmsnorm"] if variant == "prenorm" and T > 64 else []) + st
 
 
 def kernel_source_sha(kernel: str) -> str:
@@ -92,6 +100,8 @@ def parse_args():
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the CPU sample (0 = auto)")
     ap.add_argument("--prenorm", action="store_true",
                     help="time the pre-norm block y = x + layer(rmsnorm(x)) instead of the layer")
+    ap.add_argument("--dequantized-bank", action="store_true",
+                    help="time the layer on the bank dequantized once to bf16 (an ablation)")
     return ap.parse_args()
 
 
@@ -135,7 +145,7 @@ class Workload:
     NORM_EPS = 1e-5
 
     @classmethod
-    def create(cls, name: str, replicas: int, prenorm: bool = False):
+    def create(cls, name: str, replicas: int, variant: str = "layer"):
         import numpy as np
         import torch
         import mxfp4_mixture_experts_router_amd as moe
@@ -151,17 +161,39 @@ class Workload:
                 return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-        self.prenorm = prenorm
-        self.label = name + ("+prenorm" if prenorm else "")
-        host_w = make_inputs(cfg, seed=0, parts=self.WEIGHTS + (("norm_w",) if prenorm else ()))
+        self.variant = variant
+        self.prenorm = variant == "prenorm"
+        self.bank = variant == "dequantized"
+        self.label = name + ("" if variant == "layer" else "+" + variant)
+        host_w = make_inputs(cfg, seed=0, parts=self.WEIGHTS + (("norm_w",) if self.prenorm else ()))
         self.host_weights = host_w
         layer_bytes = sum(v.nbytes for v in host_w.values())
+        if self.bank:   # bf16 weights: 4 bytes per packed byte
+            layer_bytes = 4 * (host_w["gu_blocks"].nbytes + host_w["dn_blocks"].nbytes)
         if replicas <= 0:
             touched = self.touched_weight_bytes_estimate(cfg, layer_bytes)
             replicas = max(2, min(16, -(-2 * LLC_BYTES // max(touched, 1)) + 1))
         self.R = replicas
         base = {k: up(v) for k, v in host_w.items()}
         self.weights = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(replicas - 1)]
+        self.bank_dequant_ms = None
+        if self.bank:
+            # the one-off expansion, timed on the first replica
+            for r, wt in enumerate(self.weights):
+                E_, I2_, Hh_ = wt["gu_blocks"].shape
+                outs = (torch.empty((E_, I2_, 2 * Hh_), dtype=torch.bfloat16, device=dev),
+                        torch.empty((E_, Hh_ * 2, I2_ // 2), dtype=torch.bfloat16, device=dev))
+                torch.cuda.synchronize()
+                start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                start.record()
+                wt["gu_w"], wt["dn_w"] = moe.dequantize_bank(wt["gu_blocks"], wt["gu_scales"], wt["dn_blocks"],
+                                                             wt["dn_scales"], out=outs)
+                end.record()
+                torch.cuda.synchronize()
+                if r == 0:
+                    self.bank_dequant_ms = start.elapsed_time(end)
+                for key in ("gu_blocks", "gu_scales", "dn_blocks", "dn_scales"):
+                    del wt[key]
         self.host_x = [make_inputs(cfg, seed=r, parts=("x",))["x"] for r in range(replicas)]
         self.x = [up(x) for x in self.host_x]
         T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
@@ -169,7 +201,7 @@ class Workload:
         self.y = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(replicas)]
         self.idx = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(replicas)]
         self.w = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(replicas)]
-        nbytes = moe.workspace_bytes(T, H, I, E, k)
+        nbytes = (moe.workspace_bytes_dequantized if self.bank else moe.workspace_bytes)(T, H, I, E, k)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         self.lib = moe.load_library()
         self.layer_bytes = layer_bytes
@@ -183,6 +215,10 @@ class Workload:
     def args(self, r: int, stream_ptr: int):
         w = self.weights[r]
         P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        if self.bank:
+            return (ctypes.byref(self.shape), P(self.x[r]), P(w["router_w"]), P(w["router_b"]), P(w["gu_w"]),
+                    P(w["gu_bias"]), P(w["dn_w"]), P(w["dn_bias"]), P(self.y[r]), P(self.idx[r]), P(self.w[r]),
+                    P(self.ws), self.ws.numel(), ctypes.c_void_p(stream_ptr))
         norm = (P(w["norm_w"]), ctypes.c_double(self.NORM_EPS)) if self.prenorm else ()
         return (ctypes.byref(self.shape), P(self.x[r]), *norm, P(w["router_w"]), P(w["router_b"]),
                 P(w["gu_blocks"]), P(w["gu_scales"]), P(w["gu_bias"]), P(w["dn_blocks"]),
@@ -190,7 +226,8 @@ class Workload:
                 P(self.ws), self.ws.numel(), ctypes.c_void_p(stream_ptr))
 
     def step(self, r: int, stream_ptr: int):
-        fn = self.lib.moe_mxfp4_forward_prenorm if self.prenorm else self.lib.moe_mxfp4_forward
+        fn = {"layer": self.lib.moe_mxfp4_forward, "prenorm": self.lib.moe_mxfp4_forward_prenorm,
+              "dequantized": self.lib.moe_mxfp4_forward_dequantized}[self.variant]
         st = fn(*self.args(r, stream_ptr))
         if st != 0:
             raise RuntimeError(self.lib.moe_mxfp4_last_error().decode())
@@ -263,7 +300,8 @@ def run_per_kernel(wl: Workload, steps: int, hip: Hip):
     arrays = [(ctypes.c_void_p * n_ev)(*evs) for evs in events]
     n_launch = ctypes.c_int(0)
     torch.cuda.synchronize()
-    fn = lib.moe_mxfp4_forward_prenorm_timed if wl.prenorm else lib.moe_mxfp4_forward_timed
+    fn = {"layer": lib.moe_mxfp4_forward_timed, "prenorm": lib.moe_mxfp4_forward_prenorm_timed,
+          "dequantized": lib.moe_mxfp4_forward_dequantized_timed}[wl.variant]
     for i in range(steps):
         st = fn(*wl.args(i % wl.R, stream.cuda_stream), arrays[i], n_ev, ctypes.byref(n_launch))
         if st != 0:
@@ -309,6 +347,10 @@ def kernel_work(wl: Workload, kernel: str, D: float):
         return D * dn_expert + N * I * 2 + N * 8 + T * H * 2 + res, 2 * N * H * I
     if kernel == "down_stream":      # per-slot partial rows
         return D * dn_expert + N * I * 2 + N * 8 + N * H * 4, 2 * N * H * I
+    if kernel == "up_bank":          # bf16 weights and bias of the routed experts
+        return D * (2 * I * H * 2 + 2 * I * 2) + T * H * 2 + N * 4 + N * I * 2, 2 * N * 2 * I * H
+    if kernel == "down_bank":
+        return D * (H * I * 2 + H * 2) + N * I * 2 + N * 8 + N * H * 4, 2 * N * H * I
     if kernel == "up_grouped":
         return D * gu_expert + T * H * 2 + N * 4 + N * I * 2, 2 * N * 2 * I * H
     if kernel == "down_grouped":
@@ -321,7 +363,7 @@ def kernel_work(wl: Workload, kernel: str, D: float):
 
 
 def load_traffic(workload: str, kernel: str):
-    if workload.endswith("+prenorm"):
+    if "+" in workload:
         return None
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
@@ -361,11 +403,11 @@ def roofline_for(wl: Workload, stages, kernel_us, D):
     return roof, entries
 
 
-def measure(name, steps, warmup, mode, replicas, timed_steps, hip, prenorm=False):
-    wl = Workload.create(name, replicas, prenorm)
+def measure(name, steps, warmup, mode, replicas, timed_steps, hip, variant="layer"):
+    wl = Workload.create(name, replicas, variant)
     ms, wall_ms, steps_run, mode = run_timed(wl, steps, warmup, mode)
     D = distinct_experts(wl)
-    stages = stages_of(wl.cfg.T, prenorm)
+    stages = stages_of(wl.cfg.T, variant)
     kus = run_per_kernel(wl, timed_steps, hip)
     roof, kernels = roofline_for(wl, stages, kus, D)
     layer_bytes = sum(kernel_work(wl, s, D)[0] for s in stages)
@@ -373,7 +415,7 @@ def measure(name, steps, warmup, mode, replicas, timed_steps, hip, prenorm=False
     return wl, {
         "ms_per_step": ms, "wall_ms_per_step": wall_ms, "steps": steps_run, "mode": mode,
         "value": wl.cfg.T / (ms * 1e-3), "distinct_experts": D, "roofline": roof,
-        "kernels": kernels,
+        "kernels": kernels, "bank_dequant_ms": wl.bank_dequant_ms,
         "layer": {"alg_bytes": int(layer_bytes), "alg_flops": int(layer_flops),
                   "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
@@ -416,8 +458,12 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     hip = Hip()
+    if args.prenorm and args.dequantized_bank:
+        print("--prenorm and --dequantized-bank are separate variants", file=sys.stderr)
+        sys.exit(2)
+    variant = "prenorm" if args.prenorm else ("dequantized" if args.dequantized_bank else "layer")
     wl, main_res = measure(args.workload, args.steps, args.warmup, args.mode, args.replicas,
-                           args.timed_steps, hip, args.prenorm)
+                           args.timed_steps, hip, variant)
     cfg = wl.cfg
     out = {
         "metric": METRIC,
@@ -439,6 +485,7 @@ def main():
         "layer_roofline": main_res["layer"],
         "wall_ms_per_step": round(main_res["wall_ms_per_step"], 6),
         "kernels": main_res["kernels"],
+        **({"bank_dequant_ms": round(main_res["bank_dequant_ms"], 4)} if main_res["bank_dequant_ms"] else {}),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
@@ -446,13 +493,13 @@ def main():
     torch.cuda.empty_cache()
     if args.secondary:
         wl2, res2 = measure(args.secondary, args.secondary_steps, min(args.warmup, 10), args.mode,
-                            0, min(args.timed_steps, 50), hip, args.prenorm)
+                            0, min(args.timed_steps, 50), hip, variant)
         out["secondary"] = {
             "workload": wl2.label, "T": wl2.cfg.T, "E": wl2.cfg.E,
             "value": round(res2["value"], 1), "unit": "tokens/s",
             "ms_per_step": round(res2["ms_per_step"], 6), "steps": res2["steps"],
             "replicas": wl2.R, "roofline": res2["roofline"], "layer_roofline": res2["layer"],
-            "kernels": res2["kernels"]}
+            "kernels": res2["kernels"], "bank_dequant_ms": res2["bank_dequant_ms"]}
     print(json.dumps(out), flush=True)
 
 

@@ -281,6 +281,43 @@ moe_status_t moe_mxfp4_combine(const moe_mxfp4_shape_t *shape,
                                moe_bf16_t *y, void *stream);
 
 /*
+ * The layer on an expert bank dequantized once to bf16 (ZeroModels GPT-OSS page, "MXFP4
+ * experts": longer prefills dequantize the whole bank once instead of on the fly, with results
+ * identical to the routed-only path; "Mixture-of-experts feed-forward" for steps 1-6). The
+ * caller expands the packed bank once with moe_mxfp4_dequant (rows = E * 2I, cols = H for
+ * gate_up; rows = E * H, cols = I for down) and passes the bf16 tensors:
+ *  gu_w [E, 2I, H] bf16 (rows interleaved gate/up as in the packed layout), dn_w [E, H, I] bf16;
+ *  every other argument as moe_mxfp4_forward.
+ * Steps 1-3 and 6 run the same kernels as the packed path at T > 64 (router, permutation,
+ * combine); steps 4-5 run grouped GEMMs on the bf16 MFMA with bf16 activations, h stored as
+ * bf16 [T k, I] in the workspace. 5 launches at any T. The workspace size is
+ * moe_mxfp4_workspace_bytes_dequantized(); gu_w, dn_w 16-byte aligned (MOE_EALIGN).
+ * This is the pages' dequantize-once variant, kept to measure it against the packed path,
+ * which never expands the weights.
+ */
+moe_status_t moe_mxfp4_forward_dequantized(const moe_mxfp4_shape_t *shape,
+                                           const moe_bf16_t *x,
+                                           const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                                           const moe_bf16_t *gu_w, const moe_bf16_t *gu_bias,
+                                           const moe_bf16_t *dn_w, const moe_bf16_t *dn_bias,
+                                           moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
+                                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* moe_mxfp4_forward_dequantized with the instrumentation of moe_mxfp4_forward_timed
+ * (route, permute, up-projection, down-projection, combine). */
+moe_status_t moe_mxfp4_forward_dequantized_timed(const moe_mxfp4_shape_t *shape,
+                                                 const moe_bf16_t *x,
+                                                 const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                                                 const moe_bf16_t *gu_w, const moe_bf16_t *gu_bias,
+                                                 const moe_bf16_t *dn_w, const moe_bf16_t *dn_bias,
+                                                 moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
+                                                 void *workspace, size_t workspace_bytes, void *stream,
+                                                 void *const *events, int n_events, int *n_launches);
+
+/* Bytes of device workspace moe_mxfp4_forward_dequantized needs for `shape`. Host-only. */
+moe_status_t moe_mxfp4_workspace_bytes_dequantized(const moe_mxfp4_shape_t *shape, size_t *bytes);
+
+/*
  * Standalone MXFP4 -> bf16 dequantization of a packed [rows, cols] matrix
  * (ZeroModels GPT-OSS page, "MXFP4 experts"): out[r, c] = e2m1(nibble) * 2^(scale - 127),
  * exact for scale bytes 2..252. blocks [rows, cols/2], scales [rows, cols/32],

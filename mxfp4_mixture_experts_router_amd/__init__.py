@@ -25,7 +25,7 @@ __all__ = [
     "MoeError", "MoeLibraryMissing", "library_path", "load_library", "abi_version",
     "workspace_bytes", "moe_forward", "route", "permute", "expert_up", "expert_down",
     "combine", "dequant", "DECODE_MAX_T", "DECODE_MAX_K", "uses_decode_path", "mx8_bytes",
-    "quantize_act", "rmsnorm",
+    "quantize_act", "rmsnorm", "moe_forward_dequantized", "dequantize_bank", "workspace_bytes_dequantized",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +77,13 @@ _SIGS = {
     "moe_mxfp4_forward_prenorm_timed": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, ctypes.c_double]
                                         + [_vp] * 12 + [ctypes.c_size_t, _vp, _vp, ctypes.c_int,
                                                         ctypes.POINTER(ctypes.c_int)]),
+    "moe_mxfp4_forward_dequantized": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 11
+                                      + [ctypes.c_size_t, _vp]),
+    "moe_mxfp4_forward_dequantized_timed": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 11
+                                            + [ctypes.c_size_t, _vp, _vp, ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_int)]),
+    "moe_mxfp4_workspace_bytes_dequantized": (ctypes.c_int, [ctypes.POINTER(Shape),
+                                                             ctypes.POINTER(ctypes.c_size_t)]),
     "moe_mxfp4_rmsnorm": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, _vp, _vp]),
     "moe_mxfp4_route": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 7),
     "moe_mxfp4_permute": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 7),
@@ -209,6 +216,54 @@ def moe_forward(x, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks,
     return (y, idx, w) if return_topk else y
 
 
+def workspace_bytes_dequantized(T: int, H: int, I: int, E: int, k: int) -> int:
+    out = ctypes.c_size_t(0)
+    s = _shape(T, H, I, E, k)
+    _check(load_library().moe_mxfp4_workspace_bytes_dequantized(ctypes.byref(s), ctypes.byref(out)))
+    return int(out.value)
+
+
+def dequantize_bank(gu_blocks, gu_scales, dn_blocks, dn_scales, stream=None, out=None):
+    """The packed bank expanded once to bf16 (moe_mxfp4_dequant): (gu_w [E, 2I, H], dn_w [E, H, I]),
+    written into the pair ``out`` when given."""
+    gu_out, dn_out = out if out is not None else (None, None)
+    return dequant(gu_blocks, gu_scales, stream, gu_out), dequant(dn_blocks, dn_scales, stream, dn_out)
+
+
+def moe_forward_dequantized(x, router_w, router_b, gu_w, gu_bias, dn_w, dn_bias, k: int,
+                            alpha: float = 1.702, limit: float = 7.0, *,
+                            workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                            return_topk: bool = False, stream=None):
+    """The layer on a bf16 bank from dequantize_bank (moe_mxfp4_forward_dequantized). Returns
+    y [T, H] bf16 (and (topk_idx, topk_w) if return_topk)."""
+    T, H = x.shape
+    E, I2, _ = gu_w.shape
+    I = I2 // 2
+    dev = x.device
+    _need(x, "x", _BF16, (T, H), dev)
+    _need(router_w, "router_w", _BF16, (E, H), dev)
+    _need(router_b, "router_b", _BF16, (E,), dev)
+    _need(gu_w, "gu_w", _BF16, (E, 2 * I, H), dev)
+    _need(gu_bias, "gu_bias", _BF16, (E, 2 * I), dev)
+    _need(dn_w, "dn_w", _BF16, (E, H, I), dev)
+    _need(dn_bias, "dn_bias", _BF16, (E, H), dev)
+    shape = _shape(T, H, I, E, k, alpha, limit)
+    lib = load_library()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.moe_mxfp4_workspace_bytes_dequantized(ctypes.byref(shape), ctypes.byref(nbytes)))
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes.value), 256), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    _need(y, "out", _BF16, (T, H), dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev) if return_topk else None
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if return_topk else None
+    _check(lib.moe_mxfp4_forward_dequantized(
+        ctypes.byref(shape), _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(gu_w), _ptr(gu_bias),
+        _ptr(dn_w), _ptr(dn_bias), _ptr(y), _ptr(idx), _ptr(w), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return (y, idx, w) if return_topk else y
+
+
 def route(x, router_w, router_b, k: int, return_logits: bool = False, stream=None):
     """Router + top-k + softmax. Returns (topk_idx int32 [T,k], topk_w fp32 [T,k][, logits fp32 [T,E]])."""
     T, H = x.shape
@@ -327,14 +382,18 @@ def combine(o, slot_row, k: int, stream=None):
     return y
 
 
-def dequant(blocks, scales, stream=None):
-    """MXFP4 -> bf16 for a packed [..., rows, cols/2] tensor. Returns [..., rows, cols] bf16."""
+def dequant(blocks, scales, stream=None, out: Optional[torch.Tensor] = None):
+    """MXFP4 -> bf16 for a packed [..., rows, cols/2] tensor. Returns [..., rows, cols] bf16
+    (written into ``out`` when given)."""
     cols = blocks.shape[-1] * 2
     rows = blocks.numel() // (cols // 2) if blocks.numel() else 0
     dev = blocks.device
     _need(blocks, "blocks", _U8, None, dev)
     _need(scales, "scales", _U8, tuple(blocks.shape[:-1]) + (cols // 32,), dev)
-    out = torch.empty(tuple(blocks.shape[:-1]) + (cols,), dtype=torch.bfloat16, device=dev)
+    oshape = tuple(blocks.shape[:-1]) + (cols,)
+    if out is None:
+        out = torch.empty(oshape, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", _BF16, oshape, dev)
     _check(load_library().moe_mxfp4_dequant(_ptr(blocks), _ptr(scales), rows, cols, _ptr(out),
                                             _stream(stream)))
     return out

@@ -104,6 +104,27 @@ Layout layout_of(const moe_mxfp4_shape_t *s) {
     return L;
 }
 
+// Workspace of the dequantized-bank forward (256-byte aligned regions, in order).
+struct BankLayout {
+    size_t idx, w, offsets, sorted_token, sorted_w, slot_row, h, o, total;
+};
+
+BankLayout bank_layout_of(const moe_mxfp4_shape_t *s) {
+    const size_t N = static_cast<size_t>(s->T) * s->k;
+    BankLayout L{};
+    size_t p = 0;
+    L.idx = p;          p += round_up(N * 4);
+    L.w = p;            p += round_up(N * 4);
+    L.offsets = p;      p += round_up((static_cast<size_t>(s->E) + 1) * 4);
+    L.sorted_token = p; p += round_up(N * 4);
+    L.sorted_w = p;     p += round_up(N * 4);
+    L.slot_row = p;     p += round_up(N * 4);
+    L.h = p;            p += round_up(N * static_cast<size_t>(s->I) * 2);
+    L.o = p;            p += round_up(N * static_cast<size_t>(s->H) * 4);
+    L.total = p;
+    return L;
+}
+
 moe_status_t hip_status(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
     return MOE_OK;
@@ -323,6 +344,104 @@ MOE_EXPORT moe_status_t moe_mxfp4_forward_timed(
     return run_forward(shape, x, nullptr, 0.0, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks,
                        dn_scales, dn_bias, y, topk_idx, topk_w, workspace, workspace_bytes, stream,
                        events, n_events, n_launches);
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_workspace_bytes_dequantized(const moe_mxfp4_shape_t *shape, size_t *bytes) {
+    moe_status_t st = check_shape(shape, true);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    REQUIRE(bytes, "bytes");
+    *bytes = bank_layout_of(shape).total;
+    return ok();
+}
+
+namespace {
+
+moe_status_t run_forward_bank(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x, const moe_bf16_t *router_w,
+                              const moe_bf16_t *router_b, const moe_bf16_t *gu_w, const moe_bf16_t *gu_bias,
+                              const moe_bf16_t *dn_w, const moe_bf16_t *dn_bias, moe_bf16_t *y, int32_t *topk_idx,
+                              float *topk_w, void *workspace, size_t workspace_bytes, void *stream,
+                              void *const *events, int n_events, int *n_launches) {
+    moe_status_t st = check_shape(shape, true);
+    if (st != MOE_OK) return st;
+    if (events) {
+        if (n_events < 2 * MOE_MXFP4_MAX_LAUNCHES)
+            return fail(MOE_EINVAL, "n_events = %d, at least %d needed", n_events, 2 * MOE_MXFP4_MAX_LAUNCHES);
+        for (int i = 0; i < 2 * MOE_MXFP4_MAX_LAUNCHES; ++i)
+            if (!events[i]) return fail(MOE_EINVAL, "events[%d] is NULL", i);
+        REQUIRE(n_launches, "n_launches");
+        *n_launches = 0;
+    }
+    if (shape->T == 0) return ok();
+    REQUIRE16(x, "x");
+    REQUIRE16(router_w, "router_w");
+    REQUIRE(router_b, "router_b");
+    REQUIRE16(gu_w, "gu_w");
+    REQUIRE(gu_bias, "gu_bias");
+    REQUIRE16(dn_w, "dn_w");
+    REQUIRE(dn_bias, "dn_bias");
+    REQUIRE16(y, "y");
+    const BankLayout L = bank_layout_of(shape);
+    if (!workspace) return fail(MOE_EWORKSPACE, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(MOE_EALIGN, "workspace is not 256-byte aligned");
+    if (workspace_bytes < L.total)
+        return fail(MOE_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+
+    const moe::Dims d = dims_of(shape);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    int32_t *idx = topk_idx ? topk_idx : reinterpret_cast<int32_t *>(ws + L.idx);
+    float *w = topk_w ? topk_w : reinterpret_cast<float *>(ws + L.w);
+    int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+    int32_t *sorted_token = reinterpret_cast<int32_t *>(ws + L.sorted_token);
+    float *sorted_w = reinterpret_cast<float *>(ws + L.sorted_w);
+    int32_t *slot_row = reinterpret_cast<int32_t *>(ws + L.slot_row);
+    moe_bf16_t *h = reinterpret_cast<moe_bf16_t *>(ws + L.h);
+    float *o = reinterpret_cast<float *>(ws + L.o);
+    int launched = 0;
+    struct EventGuard {
+        ~EventGuard() { moe::launch_events() = moe::LaunchEvents{}; }
+    } guard;
+    auto arm = [&]() {
+        if (events)
+            moe::launch_events() = moe::LaunchEvents{static_cast<hipEvent_t>(events[2 * launched]),
+                                                     static_cast<hipEvent_t>(events[2 * launched + 1])};
+    };
+#define STEP(call, what)                                 \
+    do {                                                 \
+        arm();                                           \
+        LAUNCH(call, what);                              \
+        ++launched;                                      \
+        if (n_launches) *n_launches = launched;          \
+    } while (0)
+    STEP(moe::launch_route(d, x, nullptr, 0.0, router_w, router_b, idx, w, nullptr, nullptr, s), "route");
+    STEP(moe::launch_permute(d, idx, w, offsets, sorted_token, sorted_w, slot_row, s), "permute");
+    STEP(moe::launch_up_bank(d, x, gu_w, gu_bias, offsets, sorted_token, h, s), "up (bf16 bank)");
+    STEP(moe::launch_down_bank(d, h, dn_w, dn_bias, offsets, sorted_w, o, s), "down (bf16 bank)");
+    STEP(moe::launch_combine(d, o, slot_row, nullptr, y, s), "combine");
+#undef STEP
+    return ok();
+}
+
+}  // namespace
+
+MOE_EXPORT moe_status_t moe_mxfp4_forward_dequantized(
+    const moe_mxfp4_shape_t *shape, const moe_bf16_t *x, const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+    const moe_bf16_t *gu_w, const moe_bf16_t *gu_bias, const moe_bf16_t *dn_w, const moe_bf16_t *dn_bias,
+    moe_bf16_t *y, int32_t *topk_idx, float *topk_w, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_forward_bank(shape, x, router_w, router_b, gu_w, gu_bias, dn_w, dn_bias, y, topk_idx, topk_w,
+                            workspace, workspace_bytes, stream, nullptr, 0, nullptr);
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_forward_dequantized_timed(
+    const moe_mxfp4_shape_t *shape, const moe_bf16_t *x, const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+    const moe_bf16_t *gu_w, const moe_bf16_t *gu_bias, const moe_bf16_t *dn_w, const moe_bf16_t *dn_bias,
+    moe_bf16_t *y, int32_t *topk_idx, float *topk_w, void *workspace, size_t workspace_bytes, void *stream,
+    void *const *events, int n_events, int *n_launches) {
+    if (!events) return fail(MOE_EINVAL, "events is NULL");
+    return run_forward_bank(shape, x, router_w, router_b, gu_w, gu_bias, dn_w, dn_bias, y, topk_idx, topk_w,
+                            workspace, workspace_bytes, stream, events, n_events, n_launches);
 }
 
 MOE_EXPORT moe_status_t moe_mxfp4_route(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,

@@ -413,15 +413,13 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ o,
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ blocks,
                                                  const uint8_t *__restrict__ scales, int64_t nblk,
                                                  uint16_t *__restrict__ out) {
-    for (int64_t b = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; b < nblk;
-         b += static_cast<int64_t>(gridDim.x) * 256) {
-        const uint4 p = *reinterpret_cast<const uint4 *>(blocks + b * 16);
-        const float sc = e8m0_to_f32(scales[b]);
-        uint4 *dst = reinterpret_cast<uint4 *>(out + b * 32);
-        dst[0] = __builtin_bit_cast(uint4, mxfp4_word_to_bf16x8(p.x, sc));
-        dst[1] = __builtin_bit_cast(uint4, mxfp4_word_to_bf16x8(p.y, sc));
-        dst[2] = __builtin_bit_cast(uint4, mxfp4_word_to_bf16x8(p.z, sc));
-        dst[3] = __builtin_bit_cast(uint4, mxfp4_word_to_bf16x8(p.w, sc));
+    // thread q: packed word q (8 values of MX block q / 4) -> 16 output bytes, so that a
+    // wavefront's loads and stores are each one contiguous run
+    for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < 4 * nblk;
+         q += static_cast<int64_t>(gridDim.x) * 256) {
+        const uint32_t word = reinterpret_cast<const uint32_t *>(blocks)[q];
+        const float sc = e8m0_to_f32(scales[q >> 2]);
+        reinterpret_cast<uint4 *>(out)[q] = __builtin_bit_cast(uint4, mxfp4_word_to_bf16x8(word, sc));
     }
 }
 
@@ -500,7 +498,7 @@ hipError_t launch_dequant(const uint8_t *blocks, const uint8_t *scales, int64_t 
                           uint16_t *out, hipStream_t s) {
     const int64_t nblk = rows * (cols / 32);
     if (nblk == 0) return hipSuccess;
-    MOE_LAUNCH(k_dequant, dim3(grid_for(nblk)), dim3(256), 0, s, blocks, scales,
+    MOE_LAUNCH(k_dequant, dim3(grid_for(4 * nblk)), dim3(256), 0, s, blocks, scales,
                        nblk, out);
     return hipGetLastError();
 }

@@ -112,6 +112,15 @@ hipError_t launch_down_stream(const Dims &d, const uint8_t *h8, const uint8_t *d
                               const uint16_t *dn_bias, const int32_t *topk_idx, const float *topk_w, float *part,
                               hipStream_t s);
 
+// The expert GEMMs on a bf16 bank (launch_dequant of the packed bank), grouped over the
+// sorted rows of launch_permute, on the bf16 MFMA.
+// up: h[r, :] = bf16(swiglu(x[tok(r)] . Wgu[e]^T + bgu[e])) (bf16 [T k, I]); gu_w [E, 2I, H].
+hipError_t launch_up_bank(const Dims &d, const uint16_t *x, const uint16_t *gu_w, const uint16_t *gu_bias,
+                          const int32_t *offsets, const int32_t *sorted_token, uint16_t *h, hipStream_t s);
+// down: o[r, :] = sorted_w[r] * (h[r] . Wdn[e]^T + bdn[e]) (fp32 [T k, H]); dn_w [E, H, I].
+hipError_t launch_down_bank(const Dims &d, const uint16_t *h, const uint16_t *dn_w, const uint16_t *dn_bias,
+                            const int32_t *offsets, const float *sorted_w, float *o, hipStream_t s);
+
 // Pre-LN RMSNorm: xn[t, :] = bf16(x[t, :] * gamma / sqrt(mean_h x[t, h]^2 + eps)), in double,
 // one rounding (nearest, ties to even). One workgroup per token; H a multiple of 8.
 hipError_t launch_rmsnorm(const Dims &d, const uint16_t *x, const uint16_t *gamma, double eps, uint16_t *xn,

@@ -189,6 +189,29 @@ def test_forward_prenorm_edges(lib):
     assert fwd_prenorm(lib, s, wsb=need - 1) == EWORKSPACE
 
 
+def test_forward_dequantized_validates(lib):
+    s = shape()
+    base = dict(x=A, rw=A, rb=A, gw=A, gb=A, dw=A, db=A, y=A, idx=None, w=None, ws=0x100000, wsb=1 << 40)
+    order = ("x", "rw", "rb", "gw", "gb", "dw", "db", "y", "idx", "w", "ws", "wsb")
+
+    def call(**over):
+        args = dict(base, **over)
+        return lib.moe_mxfp4_forward_dequantized(ctypes.byref(s), *[args[k] for k in order], None)
+    for field in ("x", "rw", "rb", "gw", "gb", "dw", "db", "y"):
+        assert call(**{field: None}) == EINVAL, field
+    for field in ("x", "rw", "gw", "dw", "y"):
+        assert call(**{field: A + 2}) == EALIGN, field
+    assert call(ws=None) == EWORKSPACE
+    need = moe.workspace_bytes_dequantized(1, 2880, 2880, 32, 4)
+    assert call(wsb=need - 1) == EWORKSPACE
+    assert need >= 4 * (2880 * 2 + 2880 * 4)       # h bf16 and o fp32 rows of the 4 pairs
+    n = ctypes.c_int(-1)
+    assert lib.moe_mxfp4_forward_dequantized_timed(ctypes.byref(s), *[base[k] for k in order], None,
+                                                   None, 0, ctypes.byref(n)) == EINVAL
+    bad = shape(k=9, E=16)
+    assert lib.moe_mxfp4_forward_dequantized(ctypes.byref(bad), *[base[k] for k in order], None) == ESHAPE
+
+
 def test_rmsnorm_validates(lib):
     assert lib.moe_mxfp4_rmsnorm(A, A, 4, 60, 1e-5, A, None) == ESHAPE
     assert lib.moe_mxfp4_rmsnorm(A, A, 4, 0, 1e-5, A, None) == ESHAPE

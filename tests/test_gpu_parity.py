@@ -452,3 +452,45 @@ def test_forward_prenorm_matches_oracle(name, T, H, I, E, k, n_cmp):
     diff = bf16_to_f64(y)[tokens] - x_np - bf16_to_f64(y_plain)[tokens]
     bound = 2.0 ** -8 * (np.abs(bf16_to_f64(y)[tokens]) + np.abs(bf16_to_f64(y_plain)[tokens]))
     assert np.all(np.abs(diff) <= bound + 1e-30)
+
+
+# ----------------------------------------------------------------------------- dequantized bank
+
+BANK_CASES = [
+    # (config, T override, H, I, E, k, tokens compared)
+    ("tiny", None, None, None, None, None, 64),
+    ("tiny", 1, 96, 64, 5, 2, 1),           # contraction tail (96 = 64 + 32), partial column tile
+    ("tiny", 65, 96, 160, 5, 2, 65),        # both projections with a contraction tail
+    ("tiny", 300, 64, 128, 3, 2, 300),      # several ragged row tiles per expert
+    ("tiny", 140, 64, 64, 256, 8, 140),     # maximal E and k
+    ("batched_decode_20b", None, None, None, None, None, 64),
+    ("prefill_20b", None, None, None, None, None, 24),
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k,n_cmp", BANK_CASES)
+def test_forward_dequantized_matches_oracle(name, T, H, I, E, k, n_cmp):
+    """The dequantize-once variant against the oracle, and the pages' invariant that it agrees
+    with the routed-only packed path: identical routing, outputs within the same bar."""
+    cfg = CONFIGS[name]
+    over = {key: v for key, v in dict(H=H, I=I, E=E, k=k).items() if v is not None}
+    cfg = cfg.with_(**over)
+    T = cfg.T if T is None else T
+    inp = make_inputs(cfg, seed=2, T=T)
+    tokens = _sample(T, n_cmp, seed=T + 2)
+    ref = oracle.forward(inp, cfg.k, tokens=tokens, alpha=cfg.alpha, limit=cfg.limit)
+    d = upload(inp)
+    gu_w, dn_w = moe.dequantize_bank(d["gu_blocks"], d["gu_scales"], d["dn_blocks"], d["dn_scales"])
+    y, idx, w = moe.moe_forward_dequantized(d["x"], d["router_w"], d["router_b"], gu_w, d["gu_bias"], dn_w,
+                                            d["dn_bias"], cfg.k, cfg.alpha, cfg.limit, return_topk=True)
+    idx_np = idx.cpu().numpy()[tokens]
+    ok = check_selection(idx_np, ref, cfg.H, cfg.k)
+    np.testing.assert_allclose(w.cpu().numpy()[tokens][ok], ref["w"][ok], rtol=1e-6, atol=1e-7)
+    y_np = bf16_to_f64(y)[tokens]
+    assert_close_rows(y_np[ok], ref["y"][ok], f"dequantized bank y ({name}, T={T})")
+    y_p, idx_p, _ = _forward(d, cfg.k, cfg, return_topk=True)
+    assert torch.equal(idx, idx_p)
+    assert_close_rows(y_np, bf16_to_f64(y_p)[tokens], f"dequantized vs packed ({name}, T={T})")
+    y2 = moe.moe_forward_dequantized(d["x"], d["router_w"], d["router_b"], gu_w, d["gu_bias"], dn_w,
+                                     d["dn_bias"], cfg.k, cfg.alpha, cfg.limit)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
