@@ -427,7 +427,7 @@ def cpu_baseline(wl: Workload, sample: int):
     import oracle
     from workloads import make_inputs
     cores = oracle.max_threads()
-    n = sample if sample > 0 else max(16, 4 * cores)
+    n = sample if sample > 0 else max(16, 12 * cores)
     inp = dict(wl.host_weights)
     inp["x"] = make_inputs(wl.cfg, seed=10_000, T=n, parts=("x",))["x"]
     t0 = time.perf_counter()
