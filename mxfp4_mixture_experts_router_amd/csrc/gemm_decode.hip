@@ -16,6 +16,7 @@
 // (load_tile_chunk / tile_chunk_to_mfma).
 #include "device_common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 #include "mx_mfma.h"
 #include "routing.h"
 #include "weight_tiles.h"
@@ -118,20 +119,22 @@ __device__ __forceinline__ void stage_bytes(uint8_t *dst, const uint8_t *src, in
 
 // One block-scaled MFMA over the blocks 8c + 2v + h (v = 0..3) of chunk c, h = 0 or 1: B is
 // the lane's block 8c + 2g + h (from tile_chunk_to_mfma) with scale sb. arow: E4M3 row of the
-// lane's A row m (nullptr: a zero row), asc: its scale row. Blocks past nblocks contribute 0.
-__device__ __forceinline__ f32x4 mx_step(f32x4 acc, const uint8_t *arow, const uint8_t *asc, const i32x8 &bop,
-                                         uint32_t sb, int c, int h, int g, int nblocks) {
+// lane's A row m, asc: its scale row; with !valid (a zero row) they point at any real row.
+// Blocks past nblocks contribute 0. The reads are unconditional (indices clamped into the
+// row) and the zeroing is by selects, so a step has no divergent branches.
+__device__ __forceinline__ f32x4 mx_step(f32x4 acc, const uint8_t *arow, const uint8_t *asc, bool valid,
+                                         const i32x8 &bop, uint32_t sb, int c, int h, int g, int nblocks) {
     const int b0 = 8 * c + 2 * (g >> 1) + h;    // A bytes 0-15: virtual block g/2
     const int b1 = b0 + 4;                      // A bytes 16-31: virtual block 2 + g/2
     const int kb = 8 * c + 2 * g + h;           // the lane group's own (virtual g) block
-    uint4 f = zero4(), s = zero4();
-    uint32_t sa = 127u;
-    if (arow != nullptr) {
-        if (b0 < nblocks) f = *reinterpret_cast<const uint4 *>(arow + b0 * 32 + 16 * (g & 1));
-        if (b1 < nblocks) s = *reinterpret_cast<const uint4 *>(arow + b1 * 32 + 16 * (g & 1));
-        if (kb < nblocks) sa = asc[kb];
-    }
-    return mfma_mx(mx_a_operand(f, s), bop, acc, sa, sb);
+    const int last = nblocks - 1;
+    uint4 f = *reinterpret_cast<const uint4 *>(arow + min(b0, last) * 32 + 16 * (g & 1));
+    uint4 s = *reinterpret_cast<const uint4 *>(arow + min(b1, last) * 32 + 16 * (g & 1));
+    const uint32_t sa = asc[min(kb, last)];
+    const uint32_t m0 = valid && b0 <= last ? ~0u : 0u, m1 = valid && b1 <= last ? ~0u : 0u;
+    f = make_uint4(f.x & m0, f.y & m0, f.z & m0, f.w & m0);
+    s = make_uint4(s.x & m1, s.y & m1, s.z & m1, s.w & m1);
+    return mfma_mx(mx_a_operand(f, s), bop, acc, valid && kb <= last ? sa : 127u, sb);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -212,22 +215,28 @@ __global__ __launch_bounds__(256) void k_up_mx(
     const float bias = bf16_to_f32(gu_bias[row0 + 16 * q + col]);
 
     if (wave == 0) rows_of_expert(s_idx, N, e, s_rows, &s_nrows);
-    __syncthreads();
+    // LDS writes done; the weight loads stay in flight across the barrier (a full
+    // __syncthreads would wait for them), so the contraction starts with the first chunk
+    wait_lgkm0();
+    barrier_only();
     const int s0 = 8 * NMT * blockIdx.y;       // first slot (routed pair of e) of this block
     const int nrows = s_nrows - s0;            // slots of this block (may exceed 8 NMT)
     if (nrows <= 0) return;                    // uniform
     // A row r = 16 mt + col: slot s0 + r / 2, part r % 2 (hi, lo) -> x8 row 2 t + part
     const uint8_t *arow[NMT];
     const uint8_t *asc[NMT];
+    bool avalid[NMT];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
         const int r = 16 * mt + col;
-        arow[mt] = nullptr;
-        asc[mt] = nullptr;
+        arow[mt] = LDS_A ? dyn : x8;     // a real row; zeroed by !avalid
+        asc[mt] = xs_lds;
+        avalid[mt] = false;
         if ((r >> 1) < nrows) {
             const int xr = 2 * (s_rows[s0 + (r >> 1)] / k) + (r & 1);
             arow[mt] = (LDS_A ? dyn : x8) + static_cast<int64_t>(xr) * H;
             asc[mt] = xs_lds + xr * sxs;
+            avalid[mt] = true;
         }
     }
 
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(256) void k_up_mx(
                 const i32x8 bop = mx_b_operand(h ? hi : lo);
 #pragma unroll
                 for (int mt = 0; mt < NMT; ++mt)
-                    if (16 * mt < 2 * nrows) acc[mt] = mx_step(acc[mt], arow[mt], asc[mt], bop, sb, c, h, g, nblocks);
+                    if (16 * mt < 2 * nrows) acc[mt] = mx_step(acc[mt], arow[mt], asc[mt], avalid[mt], bop, sb, c, h, g, nblocks);
             }
         }
     }
@@ -438,7 +447,8 @@ __global__ __launch_bounds__(NW * 64) void k_down_mx_tokens(
         const int idx = tid + NW * 64 * qq;
         if (idx < N * 16) s_bprod[idx / 16][idx % 16] = s_w[idx / 16] * bf16_to_f32(bias_v[qq]);
     }
-    __syncthreads();
+    wait_lgkm0();     // LDS writes done; the weight batch stays in flight across the barrier
+    barrier_only();
 
     f32x4 acc[NMT];
 #pragma unroll
@@ -450,12 +460,14 @@ __global__ __launch_bounds__(NW * 64) void k_down_mx_tokens(
             // A row r = 16 mt + col: token 4 mt + col / 4, h8 row 4n + col % 4
             const uint8_t *arow[NMT];
             const uint8_t *asc[NMT];
+            bool avalid[NMT];
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
                 const int n = ua[u] >= 0 ? s_rowof[ua[u]][4 * mt + (col >> 2)] : -1;
                 const int hr = 4 * n + (col & 3);
-                arow[mt] = n >= 0 ? (LDS_A ? dyn : h8) + static_cast<int64_t>(hr) * I : nullptr;
-                asc[mt] = n >= 0 ? hs_lds + hr * shs : nullptr;
+                arow[mt] = (LDS_A ? dyn : h8) + static_cast<int64_t>(n >= 0 ? hr : 0) * I;
+                asc[mt] = hs_lds + (n >= 0 ? hr : 0) * shs;
+                avalid[mt] = n >= 0;
             }
             uint4 lo, hi;
             tile_chunk_to_mfma(wf[u], ws[u], lane, lo, hi);
@@ -466,7 +478,7 @@ __global__ __launch_bounds__(NW * 64) void k_down_mx_tokens(
                 const i32x8 bop = mx_b_operand(h ? hi : lo);
 #pragma unroll
                 for (int mt = 0; mt < NMT; ++mt)
-                    acc[mt] = mx_step(acc[mt], arow[mt], asc[mt], bop, sb, ucc[u], h, g, nblocks);
+                    acc[mt] = mx_step(acc[mt], arow[mt], asc[mt], avalid[mt], bop, sb, ucc[u], h, g, nblocks);
             }
         }
     }
