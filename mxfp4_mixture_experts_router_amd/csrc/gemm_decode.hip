@@ -169,7 +169,6 @@ __global__ __launch_bounds__(256) void k_up_mx(
     // chunk-half partial sums, later the slots' SwiGLU outputs [slot][17]
     constexpr int kRed = 2 * NMT * 4 * kWave > kMaxRows * 17 ? 2 * NMT * 4 * kWave : kMaxRows * 17;
     __shared__ float s_red[kRed];
-    __shared__ __attribute__((aligned(16))) uint8_t s_sc[32 * kMaxScaleCols];   // 32 rows x H/32
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int col = lane & 15, g = lane >> 4;
@@ -191,27 +190,22 @@ __global__ __launch_bounds__(256) void k_up_mx(
     const int nblocks = hs;
     const int nchunks = (nblocks + 7) / 8;
     const int q = wave & 1, p = wave >> 1;
-    // the 32 rows' scales are H contiguous bytes: up to two 16-byte loads per thread, issued
-    // before the weight stream so that waiting for it never waits for the stream
-    uint4 scv[2];
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        const int idx = tid + 256 * qq;
-        scv[qq] = idx < H / 16 ? *reinterpret_cast<const uint4 *>(gu_scales + row0 * hs + 16 * idx) : zero4();
-    }
+    // each chunk's two scale bytes per lane (row 16q + col, blocks 8c + 2g and 8c + 2g + 1)
+    // are requested just ahead of its weights, so a chunk is usable as soon as it arrives
     const uint8_t *wrows = gu_blocks + (row0 + 16 * q) * hb;
+    const uint8_t *srow = gu_scales + (row0 + 16 * q + col) * hs;
     uint4 wf[UB], ws[UB];
+    uint32_t sclo[UB], schi[UB];
     auto load_batch = [&](int c0) {
 #pragma unroll
-        for (int u = 0; u < UB; ++u)
-            load_tile_chunk(wrows, hb, min(c0 + 2 * u, nchunks - 1), nblocks, lane, wf[u], ws[u]);
+        for (int u = 0; u < UB; ++u) {
+            const int cu = min(c0 + 2 * u, nchunks - 1);
+            sclo[u] = srow[min(8 * cu + 2 * g, nblocks - 1)];
+            schi[u] = srow[min(8 * cu + 2 * g + 1, nblocks - 1)];
+            load_tile_chunk(wrows, hb, cu, nblocks, lane, wf[u], ws[u]);
+        }
     };
     load_batch(p);
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        const int idx = tid + 256 * qq;
-        if (idx < H / 16) *reinterpret_cast<uint4 *>(s_sc + 16 * idx) = scv[qq];
-    }
     const float bias = bf16_to_f32(gu_bias[row0 + 16 * q + col]);
 
     if (wave == 0) rows_of_expert(s_idx, N, e, s_rows, &s_nrows);
@@ -253,7 +247,7 @@ __global__ __launch_bounds__(256) void k_up_mx(
             tile_chunk_to_mfma(wf[u], ws[u], lane, lo, hi);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const uint32_t sb = s_sc[(16 * q + col) * hs + min(8 * c + 2 * g + h, nblocks - 1)];
+                const uint32_t sb = h ? schi[u] : sclo[u];
                 const i32x8 bop = mx_b_operand(h ? hi : lo);
 #pragma unroll
                 for (int mt = 0; mt < NMT; ++mt)

@@ -60,15 +60,15 @@ __device__ __forceinline__ void rank_keys(const uint64_t *s_key, const uint64_t 
 // exp(l_j - l_max) / sum_i exp(l_i - l_max) is summed in slot order, one exp per selected
 // candidate. Slot j goes to idx_out[j] / w_out[j] and, when given, idx_out2[j] / w_out2[j].
 // k <= 8. scratch: kTopkScratch eight-byte LDS words private to the wavefront, 16-byte
-// aligned. Called by all 64 lanes of the wavefront.
-__device__ inline void topk_softmax_values(const double (&v)[kTopkC], int E, int k, int lane,
-                                           int32_t *idx_out, float *w_out, int32_t *idx_out2,
-                                           float *w_out2, uint64_t *scratch) {
-    constexpr int C = kTopkC;
-    const int nc = (E + kWave - 1) / kWave;     // candidate slots in use (uniform)
+// aligned. Called by all 64 lanes of the wavefront. C = ceil(E / 64) candidate slots per lane
+// (a compile-time count, so that no work is spent on the unused ones).
+template <int C>
+__device__ inline void topk_softmax_nc(const double (&v)[kTopkC], int E, int k, int lane,
+                                       int32_t *idx_out, float *w_out, int32_t *idx_out2,
+                                       float *w_out2, uint64_t *scratch) {
     const int epad = (E + 7) & ~7;              // the rank loop reads keys up to here
-    uint64_t key[C];
-    int rank[C];
+    uint64_t key[kTopkC];
+    int rank[kTopkC];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int e = lane + kWave * c;
@@ -77,12 +77,7 @@ __device__ inline void topk_softmax_values(const double (&v)[kTopkC], int E, int
         if (e < epad) scratch[e] = key[c];
     }
     __builtin_amdgcn_wave_barrier();
-    switch (nc) {
-        case 1: rank_keys<1>(scratch, key, E, rank); break;
-        case 2: rank_keys<2>(scratch, key, E, rank); break;
-        case 3: rank_keys<3>(scratch, key, E, rank); break;
-        default: rank_keys<4>(scratch, key, E, rank); break;
-    }
+    rank_keys<C>(scratch, key, E, rank);
     // the largest logit: the candidate of rank 0
     double lmax = 0.0;
 #pragma unroll
@@ -91,7 +86,7 @@ __device__ inline void topk_softmax_values(const double (&v)[kTopkC], int E, int
         if (m) lmax = readlane_f64(v[c], __ffsll(static_cast<long long>(m)) - 1);
     }
     double *s_ex = reinterpret_cast<double *>(scratch + kMaxE);
-    double ex[C];
+    double ex[kTopkC];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const bool sel = lane + kWave * c < E && rank[c] < k;
@@ -123,6 +118,17 @@ __device__ inline void topk_softmax_values(const double (&v)[kTopkC], int E, int
         }
     }
     __builtin_amdgcn_wave_barrier();
+}
+
+__device__ inline void topk_softmax_values(const double (&v)[kTopkC], int E, int k, int lane,
+                                           int32_t *idx_out, float *w_out, int32_t *idx_out2,
+                                           float *w_out2, uint64_t *scratch) {
+    switch ((E + kWave - 1) / kWave) {
+        case 1: topk_softmax_nc<1>(v, E, k, lane, idx_out, w_out, idx_out2, w_out2, scratch); break;
+        case 2: topk_softmax_nc<2>(v, E, k, lane, idx_out, w_out, idx_out2, w_out2, scratch); break;
+        case 3: topk_softmax_nc<3>(v, E, k, lane, idx_out, w_out, idx_out2, w_out2, scratch); break;
+        default: topk_softmax_nc<4>(v, E, k, lane, idx_out, w_out, idx_out2, w_out2, scratch); break;
+    }
 }
 
 // The same for logits lg[0..E) in memory (LDS or global); logits_out (optional) receives
