@@ -68,12 +68,22 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // sigmoid-gated clamped SwiGLU of the GPT-OSS experts: (clamp(up) + 1) * g * sigmoid(alpha*g)
-// with g = min(gate, limit) and up clamped to [-limit, limit].
+// with g = min(gate, limit) and up clamped to [-limit, limit]. The sigmoid takes the hardware
+// reciprocal (1 ulp): every caller rounds h to 8 significant bits afterwards.
 __device__ __forceinline__ float swiglu(float gate, float up, float alpha, float limit) {
     float g = fminf(gate, limit);
     float u = fminf(fmaxf(up, -limit), limit);
-    float sig = 1.0f / (1.0f + __expf(-alpha * g));
+    float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-alpha * g));
     return (u + 1.0f) * g * sig;
+}
+
+// v of lane ^ 1 and of lane ^ 2, by DPP quad permutations (no LDS round trip, unlike
+// __shfl_xor).
+__device__ __forceinline__ float lane_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {

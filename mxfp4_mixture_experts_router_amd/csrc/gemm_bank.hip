@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_bf16(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float v = acc[i][j][r] + b;
-                        const float up = __shfl_xor(v, 1);
+                        const float up = lane_xor1(v);
                         if ((m & 1) == 0) {
                             const int lr = 64 * wm + 16 * i + 4 * g + r;
                             s_h[lr * 64 + 32 * wn + 8 * j + (m >> 1)] = f32_to_bf16(swiglu(v, up, alpha, limit));

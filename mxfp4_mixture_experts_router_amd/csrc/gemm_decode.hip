@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void k_up_mx(
             for (int j = 0; j < 2; ++j) {
                 const int s = 8 * mt + 2 * g + j;   // local slot
                 const float v = acc[mt][2 * j] + acc[mt][2 * j + 1] + bias;
-                const float other = __shfl_xor(v, 1);
+                const float other = lane_xor1(v);
                 if ((col & 1) == 0 && s < nrows)
                     s_h[s][8 * q + col / 2] = swiglu(v, other, alpha, limit) * s_w[s_rows[s0 + s]];
             }
@@ -297,8 +297,8 @@ __global__ __launch_bounds__(256) void k_up_mx(
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = s_h[sl][4 * j + i];
         float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-        m = fmaxf(m, __shfl_xor(m, 1));
-        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, lane_xor1(m));
+        m = fmaxf(m, lane_xor2(m));
         m = fmaxf(m, __shfl_xor(m, 4));
         if (live) {
             const int eb = mx8_block_exponent(m);

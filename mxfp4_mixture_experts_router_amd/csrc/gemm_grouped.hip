@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
                     const float v0 = acc[mt][nt][0] + acc[mt][nt][1] + bias;
                     const float v1 = acc[mt][nt][2] + acc[mt][nt][3] + bias;
                     // even lane (gate column) keeps row 8mt + 2g, odd lane (up) row 8mt + 2g + 1
-                    const float other = __shfl_xor((m & 1) ? v0 : v1, 1);
+                    const float other = lane_xor1((m & 1) ? v0 : v1);
                     const float gate = (m & 1) ? other : v0;
                     const float up = (m & 1) ? v1 : other;
                     s_h[(8 * mt + 2 * g + (m & 1)) * kHS + pair] = swiglu(gate, up, alpha, limit);
