@@ -123,21 +123,70 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
     // item c kChunk + j on that XCD's j-th block
     const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3;
 
-    for (int c = xcd; c * kChunk < items; c += 8) {
-        const int item = c * kChunk + lb;
-        if (item >= items) continue;
+    // Global addresses of one item's stage loads: a uniform base plus a 32-bit per-lane offset
+    // (the host keeps every operand below 4 GiB).
+    struct Addr {
+        int e, row0, rows, n0;
+        uint32_t a_off[8], as_off, b_off[4], bs_off[2], last4;
+        const uint8_t *wblk, *wsc;
+    };
+    // the tile rows' token indices: tok (LDS, the tile's rows in order) or, with nullptr, the
+    // global sorted_token
+    auto addr_of = [&](int item, const int *tok) {
+        Addr A;
         int lo = 0, hi = E - 1;                       // last e with s_icum[e] <= item
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (s_icum[mid] <= item) lo = mid; else hi = mid - 1;
         }
-        const int e = lo;
-        const int mt_e = (s_off[e + 1] - s_off[e] + kBM - 1) / kBM;
-        const int local_item = item - s_icum[e];
-        const int nt_tile = local_item / mt_e, mg = local_item % mt_e;
-        const int row0 = s_off[e] + mg * kBM;
-        const int rows = min(kBM, s_off[e + 1] - row0);
-        const int n0 = nt_tile * kBN;
+        A.e = lo;
+        const int mt_e = (s_off[A.e + 1] - s_off[A.e] + kBM - 1) / kBM;
+        const int local_item = item - s_icum[A.e];
+        A.row0 = s_off[A.e] + (local_item % mt_e) * kBM;
+        A.rows = min(kBM, s_off[A.e + 1] - A.row0);
+        A.n0 = (local_item / mt_e) * kBN;
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+        // source byte row of tile A row R (activation row R / 2, part R % 2); rows past the
+        // tile read the tile's first row (finite data, results never stored)
+        auto a_src = [&](int R) -> uint32_t {
+            const int ar = (R >> 1) < A.rows ? (R >> 1) : 0;
+            const int src = UP ? (tok ? tok[ar] : sorted_token[A.row0 + ar]) : A.row0 + ar;
+            return static_cast<uint32_t>(2 * src + (R & 1));
+        };
+        // A: instruction i of wavefront w fills A rows 64 w + 8 i + lane / 8
+#pragma unroll
+        for (int i = 0; i < 8; ++i) A.a_off[i] = a_src(64 * wave + 8 * i + (lane >> 3)) * static_cast<uint32_t>(K);
+        // A scales: wavefront w fills rows 64 w + lane
+        A.as_off = a_src(64 * wave + lane) * static_cast<uint32_t>(ass);
+        // B: instruction i fills weight rows 64 w + 16 i + lane / 4 (clamped to the matrix)
+        A.wblk = wblocks + static_cast<int64_t>(A.e) * Nrows * kbytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A.b_off[i] = min(A.n0 + 64 * wave + 16 * i + (lane >> 2), Nrows - 1) * kbytes;
+        // B scales, read as aligned dwords: the pair at (p & ~3) holds the stage's bytes
+        // p .. p + 3; a second dword past the tensor's end holds no valid byte and reads the
+        // last dword instead. Instruction j of wavefront w fills rows 64 w + 32 j + lane / 2,
+        // dword lane % 2.
+        A.wsc = wscales + static_cast<int64_t>(A.e) * Nrows * nkb;
+        const int64_t sc_len = static_cast<int64_t>(E - A.e) * Nrows * nkb;   // to the tensor's end
+        A.last4 = static_cast<uint32_t>(min<int64_t>(sc_len, 0x7fffffff) - 4);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            A.bs_off[j] = (min(A.n0 + 64 * wave + 32 * j + (lane >> 1), Nrows - 1) * nkb & ~3) + 4 * (lane & 1);
+        return A;
+    };
+
+    // up: the next tile's token indices, loaded into LDS while the current tile runs, so that
+    // its stage addresses need no dependent global load when it starts
+    __shared__ int s_ntok[2][kBM];
+    int ntile = 0;  // tiles this workgroup has started
+    for (int c = xcd; c * kChunk < items; c += 8, ++ntile) {
+        const int item = c * kChunk + lb;
+        if (item >= items) continue;
+        const bool pre = UP && ntile > 0;     // the previous tile loaded this one's tokens
+        const Addr A = addr_of(item, pre ? s_ntok[ntile & 1] : nullptr);
+        const int e = A.e, row0 = A.row0, rows = A.rows, n0 = A.n0;
 
         // Per-lane values are derived from an opaque copy of the thread index in every tile,
         // so that the compiler recomputes them here instead of keeping them live (spilled)
@@ -148,65 +197,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         const int m = lane & 15, g = lane >> 4;
         const int wm = wave & 1, wn = wave >> 1;
 
-        // --- loads. Global addresses are a uniform base plus a 32-bit per-lane offset (the
-        // host keeps every operand below 4 GiB). A chunk or block past K (last stage only)
-        // loads chunk / block 0 instead: finite data whose contribution the multiply zeroes.
+        // A chunk or block past K (last stage only) loads chunk / block 0 instead: finite data
+        // whose contribution the multiply zeroes.
         const int a_c = (lane & 7) ^ ((lane >> 3) & 7);
         const int b_c = (lane & 3) ^ ((lane >> 3) & 3);
         const int a_vc = (K - kBK * kt_last) / 16;   // valid chunks in the last stage (2..8)
         const int b_vb = nkb - 4 * kt_last;          // valid blocks in the last stage (1..4)
         const uint32_t a_ch = 16 * a_c, a_ch_last = a_c < a_vc ? 16 * a_c : 0;
         const uint32_t b_ch = 16 * b_c, b_ch_last = b_c < b_vb ? 16 * b_c : 0;
-        // source byte row of tile A row R (activation row R / 2, part R % 2); rows past the
-        // tile read the tile's first row (finite data, results never stored)
-        auto a_src = [&](int R) -> uint32_t {
-            const int ar = (R >> 1) < rows ? (R >> 1) : 0;
-            const int src = UP ? sorted_token[row0 + ar] : row0 + ar;
-            return static_cast<uint32_t>(2 * src + (R & 1));
-        };
-        // A: instruction i of wavefront w fills A rows 64 w + 8 i + lane / 8
-        uint32_t a_off[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a_off[i] = a_src(64 * wave + 8 * i + (lane >> 3)) * static_cast<uint32_t>(K);
-        // A scales: wavefront w fills rows 64 w + lane
-        const uint32_t as_off = a_src(64 * wave + lane) * static_cast<uint32_t>(ass);
-        // B: instruction i fills weight rows 64 w + 16 i + lane / 4 (clamped to the matrix)
-        const uint8_t *wblk = wblocks + static_cast<int64_t>(e) * Nrows * kbytes;
-        uint32_t b_off[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) b_off[i] = min(n0 + 64 * wave + 16 * i + (lane >> 2), Nrows - 1) * kbytes;
-        // B scales, read as aligned dwords: the pair at (p & ~3) holds the stage's bytes
-        // p .. p + 3; a second dword past the tensor's end holds no valid byte and reads the
-        // last dword instead. Instruction j of wavefront w fills rows 64 w + 32 j + lane / 2,
-        // dword lane % 2.
-        const uint8_t *wsc = wscales + static_cast<int64_t>(e) * Nrows * nkb;
-        const int64_t sc_len = static_cast<int64_t>(E - e) * Nrows * nkb;   // to the tensor's end
-        const uint32_t last4 = static_cast<uint32_t>(min<int64_t>(sc_len, 0x7fffffff) - 4);
-        uint32_t bs_off[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            bs_off[j] = (min(n0 + 64 * wave + 32 * j + (lane >> 1), Nrows - 1) * nkb & ~3) + 4 * (lane & 1);
 
         const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)g_stages;
         // the loads of stage kt into buffer buf, in parts issued between the row tiles'
         // MFMAs of the current stage, so that no wavefront stalls on a burst of them
-        auto issue_part = [&](int part, int buf, int kt) {
+        auto issue_part_of = [&](const Addr &S, int part, int buf, int kt) {
             const uint32_t lbuf = lds0 + buf * kStage;
             const uint32_t ach = kt == kt_last ? a_ch_last : a_ch;
             const uint32_t bch = kt == kt_last ? b_ch_last : b_ch;
             const uint8_t *a_k = a8 + kBK * kt;          // uniform bases
-            const uint8_t *b_k = wblk + 64 * kt;
+            const uint8_t *b_k = S.wblk + 64 * kt;
             if (part < 4) {
 #pragma unroll
-                for (int i = 2 * part; i < 2 * part + 2; ++i) dma16(a_k, a_off[i] + ach, lbuf + (8 * wave + i) * 1024);
-                if (part == 0) dma4(a_sc + 4 * kt, as_off, lbuf + kOffAS + 256 * wave);
+                for (int i = 2 * part; i < 2 * part + 2; ++i) dma16(a_k, S.a_off[i] + ach, lbuf + (8 * wave + i) * 1024);
+                if (part == 0) dma4(a_sc + 4 * kt, S.as_off, lbuf + kOffAS + 256 * wave);
             } else if (part < 6) {
                 const int j = part - 4;
 #pragma unroll
-                for (int i = 2 * j; i < 2 * j + 2; ++i) dma16(b_k, b_off[i] + bch, lbuf + kOffB + (4 * wave + i) * 1024);
-                dma4(wsc, min(bs_off[j] + 4 * kt, last4), lbuf + kOffBS + (2 * wave + j) * 256);
+                for (int i = 2 * j; i < 2 * j + 2; ++i) dma16(b_k, S.b_off[i] + bch, lbuf + kOffB + (4 * wave + i) * 1024);
+                dma4(S.wsc, min(S.bs_off[j] + 4 * kt, S.last4), lbuf + kOffBS + (2 * wave + j) * 256);
             }
         };
+        auto issue_part = [&](int part, int buf, int kt) { issue_part_of(A, part, buf, kt); };
         auto issue = [&](int buf, int kt) {
 #pragma unroll
             for (int part = 0; part < 6; ++part) issue_part(part, buf, kt);
@@ -280,7 +300,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         const int bcol = min(n0 + tid, Nrows - 1);
         const uint16_t bias_v = tid < kBN ? wbias[static_cast<int64_t>(e) * Nrows + bcol] : 0;
         const float rw_v = !UP && tid < kBM ? sorted_w[row0 + min(tid, rows - 1)] : 0.f;
-        __syncthreads();   // the previous tile's epilogue is done with LDS
+        wait_lgkm0();      // the previous tile's epilogue is done with LDS (loads may stay in flight)
+        barrier_only();
+        const int cn = c + 8, nitem = cn * kChunk + lb;
+        const bool has_next = UP && cn * kChunk < items && nitem < items;
+        if (has_next && wave < 2) {
+            // the next tile's 128 token indices (rows past its end repeat its last row)
+            int lo2 = 0, hi2 = E - 1;
+            while (lo2 < hi2) {
+                const int mid = (lo2 + hi2 + 1) >> 1;
+                if (s_icum[mid] <= nitem) lo2 = mid; else hi2 = mid - 1;
+            }
+            const int mt2 = (s_off[lo2 + 1] - s_off[lo2] + kBM - 1) / kBM;
+            const int r0 = __builtin_amdgcn_readfirstlane(s_off[lo2] + ((nitem - s_icum[lo2]) % mt2) * kBM);
+            const int nr = min(kBM, s_off[lo2 + 1] - r0);
+            const uint32_t ldst = __builtin_amdgcn_readfirstlane(
+                (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int *)&s_ntok[(ntile + 1) & 1][64 * wave]);
+            dma4(reinterpret_cast<const uint8_t *>(sorted_token + r0),
+                 4u * static_cast<uint32_t>(min(64 * wave + lane, nr - 1)), ldst);
+        }
         issue(0, 0);
         if (kt_total > 1) issue(1, 1);
         int buf = 0;
