@@ -39,6 +39,9 @@ __device__ __forceinline__ void load_routing(const double *logits, int32_t *topk
                                              int k, int *s_idx, float *s_w, uint32_t *bitmap, Stage &&stage) {
     constexpr int kPre = 2;                 // routing entries per thread loaded up front
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    // the wavefront's routing role: tokens wr, wr + 4, ..; rotated with the workgroup so that
+    // the workgroups sharing a CU run their top-k on different SIMDs
+    const int wr = (wave + static_cast<int>(blockIdx.x)) & 3;
     const int N = T * k;
     if (tid < kMaxE / 32) bitmap[tid] = 0u;
     double lg0[kMaxE / kWave];
@@ -48,7 +51,7 @@ __device__ __forceinline__ void load_routing(const double *logits, int32_t *topk
 #pragma unroll
         for (int c = 0; c < kMaxE / kWave; ++c) {
             const int e = lane + kWave * c;
-            lg0[c] = (wave < 4 && wave < T && e < E) ? logits[static_cast<int64_t>(wave) * E + e] : 0.0;
+            lg0[c] = (wave < 4 && wr < T && e < E) ? logits[static_cast<int64_t>(wr) * E + e] : 0.0;
         }
     } else {
 #pragma unroll
@@ -63,8 +66,8 @@ __device__ __forceinline__ void load_routing(const double *logits, int32_t *topk
         __shared__ __attribute__((aligned(16))) uint64_t s_tk[4][kTopkScratch];
         if (logits && wave < 4) {
             const bool writer = blockIdx.x == 0;
-            for (int t = wave; t < T; t += 4) {
-                if (t != wave) {
+            for (int t = wr; t < T; t += 4) {
+                if (t != wr) {
 #pragma unroll
                     for (int c = 0; c < kMaxE / kWave; ++c) {
                         const int e = lane + kWave * c;
