@@ -120,10 +120,13 @@ __device__ __forceinline__ void store_mx8_block(const float (&v)[32], uint8_t *q
 }
 
 // The mx8 rows of bf16 activation row `xrow` (K elements) as row r of the mx8 matrix q8
-// holding R rows; the calling block's threads share the K / 32 blocks.
-__device__ __forceinline__ void write_mx8_row(const uint16_t *xrow, int K, uint8_t *q8, int64_t R, int64_t r) {
+// holding R rows; the calling block's threads from `first` on share the K / 32 blocks
+// (threads below `first` do nothing).
+__device__ __forceinline__ void write_mx8_row(const uint16_t *xrow, int K, uint8_t *q8, int64_t R, int64_t r,
+                                              int first = 0) {
     uint8_t *qs = q8 + static_cast<size_t>(2 * R) * K;
-    for (int b = threadIdx.x; b < K / 32; b += blockDim.x) {
+    if (static_cast<int>(threadIdx.x) < first) return;
+    for (int b = static_cast<int>(threadIdx.x) - first; b < K / 32; b += static_cast<int>(blockDim.x) - first) {
         float v[32];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

@@ -118,7 +118,9 @@ __global__ __launch_bounds__(512) void k_route_token(
     if (wave == 0)
         topk_softmax_wave(lg, E, k, lane, topk_idx + t * k, topk_w + t * k, nullptr, nullptr,
                           logits_out ? logits_out + t * E : nullptr, s_tk);
-    if (x8 != nullptr) write_mx8_row(gamma ? s_xn : xr, H, x8, T, t);   // s_xn: written before the barrier
+    // wavefront 0 runs the top-k; the others write the mx8 row meanwhile (s_xn: written before
+    // the barrier)
+    if (x8 != nullptr && wave > 0) write_mx8_row(gamma ? s_xn : xr, H, x8, T, t, kWave);
 }
 
 // Logits only, for few tokens (the top-k then runs in the up-projection's prologue): block

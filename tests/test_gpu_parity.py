@@ -419,6 +419,7 @@ PRENORM_CASES = [
     ("tiny", 3, 96, 64, 5, 2, 3),
     ("tiny", 5, 96, 64, 5, 2, 5),
     ("tiny", 65, 96, 64, 5, 2, 65),
+    ("tiny", 5, 3616, 64, 4, 2, 5),         # H > 3584 from 4 tokens: the RMSNorm kernel of its own
     ("decode_20b", None, None, None, None, None, 1),
     ("batched_decode_20b", None, None, None, None, None, 64),
     ("prefill_20b", None, None, None, None, None, 24),
