@@ -86,6 +86,31 @@ __device__ __forceinline__ float lane_xor2(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));
 }
 
+// v + (the double from another lane by DPP control CTRL; 0 where ROW_MASK disables the row)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double add_dpp_f64(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b & 0xffffffffll), CTRL, ROW_MASK, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, ROW_MASK, 0xf, false);
+    return v + __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+// Sum of v over the 64 lanes of a wavefront, the same bits in every lane: pairs, quads,
+// 8- and 16-lane groups by DPP within each row, then the rows by broadcasts into lane 63,
+// whose value every lane reads. A fixed order, no LDS round trips.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v = add_dpp_f64<0xB1, 0xf>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+    v = add_dpp_f64<0x4E, 0xf>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+    v = add_dpp_f64<0x141, 0xf>(v);   // row_half_mirror: the other quad of the 8
+    v = add_dpp_f64<0x140, 0xf>(v);   // row_mirror: the other 8 of the row
+    v = add_dpp_f64<0x142, 0xa>(v);   // row_bcast15 into rows 1 and 3
+    v = add_dpp_f64<0x143, 0xc>(v);   // row_bcast31 into rows 2 and 3
+    const long long b = __double_as_longlong(v);
+    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(b & 0xffffffffll), 63));
+    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), 63));
+    return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     return (1ull << __lane_id()) - 1ull;
 }

@@ -33,13 +33,8 @@ __device__ __forceinline__ double sumsq8(const uint4 &u, double ss) {
     return ss;
 }
 
-// Sum over the 64 lanes of a wavefront; every lane receives the same bits (each butterfly
-// step adds the same two values in either lane).
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
+// Sum over the 64 lanes of a wavefront; every lane receives the same bits.
+__device__ __forceinline__ double wave_sum(double v) { return wave_sum_f64(v); }
 
 __device__ __forceinline__ double rms_scale(double ss, int H, double eps) { return 1.0 / sqrt(ss / H + eps); }
 

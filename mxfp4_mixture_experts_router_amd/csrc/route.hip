@@ -105,9 +105,7 @@ __global__ __launch_bounds__(512) void k_route_token(
             for (int i = 0; i < NI; ++i) acc[q] = dot8(xv[i], a[q][i], acc[q]);
         }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1)
-#pragma unroll
-            for (int q = 0; q < kEPW; ++q) acc[q] += __shfl_xor(acc[q], off);
+        for (int q = 0; q < kEPW; ++q) acc[q] = wave_sum_f64(acc[q]);
         if (lane == 0) {
 #pragma unroll
             for (int q = 0; q < kEPW; ++q)
@@ -194,11 +192,8 @@ __global__ __launch_bounds__(256) void k_logits(const uint16_t *__restrict__ x, 
         acc0 = dot8(xv[i], a[i], acc0);
         acc1 = dot8(xv[i], b[i], acc1);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        acc0 += __shfl_xor(acc0, off);
-        acc1 += __shfl_xor(acc1, off);
-    }
+    acc0 = wave_sum_f64(acc0);
+    acc1 = wave_sum_f64(acc1);
     if (lane == 0) {
         part[wave][0] = acc0;
         part[wave][1] = acc1;
