@@ -53,13 +53,14 @@ constexpr int kBM = 128;                       // activation rows per tile
 constexpr int kAR = 2 * kBM;                   // A rows per tile (hi, lo)
 constexpr int kBN = 256;                       // output columns (weight rows) per tile
 constexpr int kBK = 128;                       // contraction per stage
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;                  // 8 wavefronts: 4 row groups x 2 column halves
 constexpr int kChunk = 32;                     // items per XCD chunk (= blocks per XCD)
 constexpr int kOffB = kAR * kBK;               // 32768
 constexpr int kOffAS = kOffB + kBN * kBK / 2;  // 49152
 constexpr int kOffBS = kOffAS + kAR * 4;       // 50176
 constexpr int kStage = kOffBS + kBN * 8;       // 52224
-constexpr int kOps = 15;                       // global_load_lds per wavefront per stage
+// global_load_lds per wavefront per stage: 4 A, 2 B, 1 B-scale, and 1 A-scale for wavefronts 0-3
+constexpr int kOpsLo = 8, kOpsHi = 7;
 constexpr int kHS = 67;                        // up epilogue: padded row of 64 fp32 pairs
 constexpr int kOS = 132;                       // down epilogue: padded row of 128 fp32 outputs
 
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
     // (the host keeps every operand below 4 GiB).
     struct Addr {
         int e, row0, rows, n0;
-        uint32_t a_off[8], as_off, b_off[4], bs_off[2], last4;
+        uint32_t a_off[4], as_off, b_off[2], bs_off[1], last4;
         const uint8_t *wblk, *wsc;
     };
     // the tile rows' token indices: tok (LDS, the tile's rows in order) or, with nullptr, the
@@ -155,25 +156,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             const int src = UP ? (tok ? tok[ar] : sorted_token[A.row0 + ar]) : A.row0 + ar;
             return static_cast<uint32_t>(2 * src + (R & 1));
         };
-        // A: instruction i of wavefront w fills A rows 64 w + 8 i + lane / 8
+        // A: instruction i of wavefront w fills A rows 32 w + 8 i + lane / 8
 #pragma unroll
-        for (int i = 0; i < 8; ++i) A.a_off[i] = a_src(64 * wave + 8 * i + (lane >> 3)) * static_cast<uint32_t>(K);
-        // A scales: wavefront w fills rows 64 w + lane
-        A.as_off = a_src(64 * wave + lane) * static_cast<uint32_t>(ass);
-        // B: instruction i fills weight rows 64 w + 16 i + lane / 4 (clamped to the matrix)
+        for (int i = 0; i < 4; ++i) A.a_off[i] = a_src(32 * wave + 8 * i + (lane >> 3)) * static_cast<uint32_t>(K);
+        // A scales: wavefront w < 4 fills rows 64 w + lane
+        A.as_off = a_src(64 * (wave & 3) + lane) * static_cast<uint32_t>(ass);
+        // B: instruction i fills weight rows 32 w + 16 i + lane / 4 (clamped to the matrix)
         A.wblk = wblocks + static_cast<int64_t>(A.e) * Nrows * kbytes;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) A.b_off[i] = min(A.n0 + 64 * wave + 16 * i + (lane >> 2), Nrows - 1) * kbytes;
+        for (int i = 0; i < 2; ++i) A.b_off[i] = min(A.n0 + 32 * wave + 16 * i + (lane >> 2), Nrows - 1) * kbytes;
         // B scales, read as aligned dwords: the pair at (p & ~3) holds the stage's bytes
         // p .. p + 3; a second dword past the tensor's end holds no valid byte and reads the
-        // last dword instead. Instruction j of wavefront w fills rows 64 w + 32 j + lane / 2,
-        // dword lane % 2.
+        // last dword instead. Wavefront w fills rows 32 w + lane / 2, dword lane % 2.
         A.wsc = wscales + static_cast<int64_t>(A.e) * Nrows * nkb;
         const int64_t sc_len = static_cast<int64_t>(E - A.e) * Nrows * nkb;   // to the tensor's end
         A.last4 = static_cast<uint32_t>(min<int64_t>(sc_len, 0x7fffffff) - 4);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            A.bs_off[j] = (min(A.n0 + 64 * wave + 32 * j + (lane >> 1), Nrows - 1) * nkb & ~3) + 4 * (lane & 1);
+        A.bs_off[0] = (min(A.n0 + 32 * wave + (lane >> 1), Nrows - 1) * nkb & ~3) + 4 * (lane & 1);
         return A;
     };
 
@@ -195,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         asm volatile("" : "+v"(tid));
         const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
         const int m = lane & 15, g = lane >> 4;
-        const int wm = wave & 1, wn = wave >> 1;
+        const int wm = wave & 3, wn = wave >> 2;
 
         // A chunk or block past K (last stage only) loads chunk / block 0 instead: finite data
         // whose contribution the multiply zeroes.
@@ -215,29 +213,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             const uint32_t bch = kt == kt_last ? b_ch_last : b_ch;
             const uint8_t *a_k = a8 + kBK * kt;          // uniform bases
             const uint8_t *b_k = S.wblk + 64 * kt;
-            if (part < 4) {
+            if (part < 2) {
 #pragma unroll
-                for (int i = 2 * part; i < 2 * part + 2; ++i) dma16(a_k, S.a_off[i] + ach, lbuf + (8 * wave + i) * 1024);
-                if (part == 0) dma4(a_sc + 4 * kt, S.as_off, lbuf + kOffAS + 256 * wave);
-            } else if (part < 6) {
-                const int j = part - 4;
+                for (int i = 2 * part; i < 2 * part + 2; ++i) dma16(a_k, S.a_off[i] + ach, lbuf + (4 * wave + i) * 1024);
+                if (part == 0 && wave < 4) dma4(a_sc + 4 * kt, S.as_off, lbuf + kOffAS + 256 * wave);
+            } else if (part == 2) {
 #pragma unroll
-                for (int i = 2 * j; i < 2 * j + 2; ++i) dma16(b_k, S.b_off[i] + bch, lbuf + kOffB + (4 * wave + i) * 1024);
-                dma4(S.wsc, min(S.bs_off[j] + 4 * kt, S.last4), lbuf + kOffBS + (2 * wave + j) * 256);
+                for (int i = 0; i < 2; ++i) dma16(b_k, S.b_off[i] + bch, lbuf + kOffB + (2 * wave + i) * 1024);
+                dma4(S.wsc, min(S.bs_off[0] + 4 * kt, S.last4), lbuf + kOffBS + wave * 256);
             }
         };
         auto issue_part = [&](int part, int buf, int kt) { issue_part_of(A, part, buf, kt); };
         auto issue = [&](int buf, int kt) {
 #pragma unroll
-            for (int part = 0; part < 6; ++part) issue_part(part, buf, kt);
+            for (int part = 0; part < 3; ++part) issue_part(part, buf, kt);
         };
 
-        // The tile body, for NL = the wavefront's row tiles that hold valid rows (rounded up
-        // to 2, 4, 6 or 8; a compile-time constant, so that skipped tiles cost no branches
-        // and the accumulators stay in their registers).
+        // The tile body, for NL = the wavefront's row tiles that hold valid rows (1 to 4; a
+        // compile-time constant, so that skipped tiles cost no branches and the accumulators
+        // stay in their registers).
         auto tile_body = [&](auto nl_tag) {
         constexpr int NL = decltype(nl_tag)::value;
-        f32x4 acc[8][8];
+        f32x4 acc[4][8];
 #pragma unroll
         for (int a = 0; a < NL; ++a)
 #pragma unroll
@@ -253,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         const uint32_t lb_bs = kOffBS + 1024 * wn + 8 * m + (((n0 + 128 * wn + m) * nkb) & 3) + g;
         const uint32_t lb_a = 2048 * wm + 128 * m + 16 * (g ^ (m & 7));
         const uint32_t lb_as = kOffAS + 64 * wm + 4 * m + g;
-        // the wavefront's row tiles are the tile's 16-row tiles 2 mt + wm (interleaved, so
+        // the wavefront's row tiles are the tile's 16-row tiles 4 mt + wm (interleaved, so
         // that a partly filled tile splits its rows evenly); only the first NL are multiplied
         // In the last stage of a contraction whose block count is not a multiple of 4
         // (vb < 4, a uniform branch), blocks past K get zero A data and unit scales, so they
@@ -273,11 +270,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
                 for (int nt = 0; nt < 8; ++nt) sb[nt] = g < vb ? sb[nt] : 127u;
             }
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
+            for (int mt = 0; mt < 4; ++mt) {
                 if (mt < NL) {
-                    uint4 lo16 = *reinterpret_cast<const uint4 *>(base + lb_a + 4096 * mt);
-                    uint4 hi16 = *reinterpret_cast<const uint4 *>(base + (lb_a ^ 64u) + 4096 * mt);   // chunk g + 4
-                    uint32_t sa = base[lb_as + 128 * mt];
+                    uint4 lo16 = *reinterpret_cast<const uint4 *>(base + lb_a + 8192 * mt);
+                    uint4 hi16 = *reinterpret_cast<const uint4 *>(base + (lb_a ^ 64u) + 8192 * mt);   // chunk g + 4
+                    uint32_t sa = base[lb_as + 256 * mt];
                     if (vb < 4) {
                         // lane group g carries blocks g / 2 (low half) and 2 + g / 2 (high half)
                         if ((g >> 1) >= vb) lo16 = zero4();
@@ -288,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
 #pragma unroll
                     for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = mfma_mx(af, bop[nt], acc[mt][nt], sa, sb[nt]);
                 }
-                if (refill && mt < 6) issue_part(mt, buf2, kt + 2);
+                if (refill && mt < 3) issue_part(mt, buf2, kt + 2);
             }
         };
 
@@ -323,7 +320,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         if (kt_total > 1) issue(1, 1);
         int buf = 0;
         for (int kt = 0; kt < kt_total; ++kt) {
-            if (kt + 1 < kt_total) wait_vm<kOps>(); else wait_vm<0>();
+            if (kt + 1 < kt_total) {
+                if (wave < 4) wait_vm<kOpsLo>(); else wait_vm<kOpsHi>();
+            } else {
+                wait_vm<0>();
+            }
             barrier_only();
             const int buf2 = buf == 0 ? 2 : buf - 1;     // (kt + 2) % 3
             compute(buf, kt, kt + 2 < kt_total, buf2);
@@ -336,11 +337,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         // --- epilogue. Lane (m, g) of MFMA tile (mt, nt) holds column 16 nt + m of the
         // wavefront's A rows 16 mt + 4g + r: its activation row 8 mt + 2g (r = 0, 1: hi, lo)
         // and 8 mt + 2g + 1 (r = 2, 3); value = D[hi] + D[lo]. The wavefront's activation row
-        // r is the tile's row 16 (r / 8) + 8 wm + r % 8.
+        // r is the tile's row 32 (r / 8) + 8 wm + r % 8.
         if (UP) {
-            // h of the wavefront's 64 rows x 64 pairs (fp32) into LDS (region 2 wn + wm of 64 kHS
-            // floats), then each lane quantizes two (row, MX block) items
-            float *s_h = reinterpret_cast<float *>(g_stages) + (2 * wn + wm) * (64 * kHS);
+            // h of the wavefront's 32 rows x 64 pairs (fp32) into LDS (region `wave` of 32 kHS
+            // floats), then each lane quantizes one (row, MX block) item
+            float *s_h = reinterpret_cast<float *>(g_stages) + wave * (32 * kHS);
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
                 const int wr = n0 + 128 * wn + 16 * nt + m;
@@ -361,11 +362,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             const int Iw = Nrows / 2;
             const int is8 = mx8_scale_stride(Iw);
             uint8_t *h_sc = h8 + static_cast<size_t>(2 * h_rows) * Iw;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int item = lane + 64 * q;
-                const int r = item >> 1, blk = item & 1;
-                const int R = 16 * (r >> 3) + 8 * wm + (r & 7);   // tile activation row
+            {
+                const int r = lane >> 1, blk = lane & 1;
+                const int R = 32 * (r >> 3) + 8 * wm + (r & 7);   // tile activation row
                 const int ib = (n0 + 128 * wn) / 64 + blk;        // MX block of h
                 if (R < rows && 64 * ib < Nrows) {
                     float v[32];
@@ -375,16 +374,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
                 }
             }
         } else {
-            // o of the wavefront's 64 rows x 128 columns (bias added, weighted) through LDS
+            // o of the wavefront's 32 rows x 128 columns (bias added, weighted) through LDS
             // (region `wave`, rows of kOS floats), so that each store writes 16 contiguous
             // bytes per lane
-            float *s_o = reinterpret_cast<float *>(g_stages) + wave * (64 * kOS);
-            float wrow[8][2];
+            float *s_o = reinterpret_cast<float *>(g_stages) + wave * (32 * kOS);
+            float wrow[4][2];
 #pragma unroll
             for (int mt = 0; mt < NL; ++mt)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const int lr = 16 * mt + 8 * wm + 2 * g + j;
+                    const int lr = 32 * mt + 8 * wm + 2 * g + j;
                     wrow[mt][j] = lr < rows ? s_rw[lr] : 0.f;
                 }
 #pragma unroll
@@ -402,10 +401,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             }
             __syncthreads();
 #pragma unroll 4
-            for (int it = 0; it < 32; ++it) {
+            for (int it = 0; it < 16; ++it) {
                 const int lrow = 2 * it + (lane >> 5);       // wavefront row
                 const int c4 = 4 * (lane & 31);              // first of 4 columns
-                const int lr = 16 * (lrow >> 3) + 8 * wm + (lrow & 7);   // tile row
+                const int lr = 32 * (lrow >> 3) + 8 * wm + (lrow & 7);   // tile row
                 const int d = n0 + 128 * wn + c4;
                 if (lr < rows && d < Nrows)
                     *reinterpret_cast<float4 *>(o_out + static_cast<int64_t>(row0 + lr) * Nrows + d) =
@@ -414,11 +413,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         }
         };
         // the wavefront's row tiles holding valid rows (of the (rows + 7) / 8 that do)
-        const int nloc = ((rows + 7) / 8 - wm + 1) / 2;
-        if (nloc > 6) tile_body(IntC<8>{});
-        else if (nloc > 4) tile_body(IntC<6>{});
-        else if (nloc > 2) tile_body(IntC<4>{});
-        else tile_body(IntC<2>{});
+        const int nloc = ((rows + 7) / 8 - wm + 3) / 4;
+        if (nloc > 3) tile_body(IntC<4>{});
+        else if (nloc > 2) tile_body(IntC<3>{});
+        else if (nloc > 1) tile_body(IntC<2>{});
+        else tile_body(IntC<1>{});
     }
 }
 
