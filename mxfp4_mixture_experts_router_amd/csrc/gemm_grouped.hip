@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             for (int part = 0; part < 3; ++part) issue_part(part, buf, kt);
         };
 
-        // The tile body, for NL = the wavefront's row tiles that hold valid rows (1 to 4; a
+        // The tile body, for NL = the wavefront's row tiles that hold valid rows (0 to 4; a
         // compile-time constant, so that skipped tiles cost no branches and the accumulators
         // stay in their registers).
         auto tile_body = [&](auto nl_tag) {
@@ -412,12 +412,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             }
         }
         };
-        // the wavefront's row tiles holding valid rows (of the (rows + 7) / 8 that do)
-        const int nloc = ((rows + 7) / 8 - wm + 3) / 4;
+        // the wavefront's row tiles holding valid rows (of the (rows + 7) / 8 that do); none
+        // when all its 128 columns lie past the matrix (the last column tile of a matrix whose
+        // row count is not a multiple of 256), so that the SIMD's other wavefront runs alone
+        const int nloc = n0 + 128 * wn >= Nrows ? 0 : ((rows + 7) / 8 - wm + 3) / 4;
         if (nloc > 3) tile_body(IntC<4>{});
         else if (nloc > 2) tile_body(IntC<3>{});
         else if (nloc > 1) tile_body(IntC<2>{});
-        else tile_body(IntC<1>{});
+        else if (nloc > 0) tile_body(IntC<1>{});
+        else tile_body(IntC<0>{});
     }
 }
 
