@@ -47,8 +47,9 @@ __device__ void wave_exclusive_scan(const int *cnt, int *out, int E, int lane) {
 // Wavefront w owns the contiguous pairs [w * per, (w + 1) * per) and walks them 64 at a
 // time twice: first counting its pairs per expert, then, after the block has turned the
 // counts into each wavefront's starting position per expert, scattering them. Within a
-// round the pairs of one expert are ranked by lane (ballot match), so the order is by pair
-// index throughout.
+// round the pairs of one expert are ranked by lane (ballot match over the BITS bits an
+// expert index can have), so the order is by pair index throughout.
+template <int BITS>
 __global__ __launch_bounds__(kThreads) void k_permute(
     const int32_t *__restrict__ topk_idx, const float *__restrict__ topk_w, int32_t N, int E,
     int k, int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_token,
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(
         for (int r = 0; r < kBatch; ++r) {
             const int e = eb[r];
             const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
-            const uint64_t peers = same_expert_lanes(e, valid);
+            const uint64_t peers = same_expert_lanes<BITS>(e, valid);
             if (valid && (peers & lanemask_lt()) == 0) wcnt[wave][e] += __popcll(peers);
             __builtin_amdgcn_wave_barrier();
         }
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void k_permute(
             const int n = nb + r * kWave + lane;
             const int e = eb[r];
             const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
-            const uint64_t peers = same_expert_lanes(e, valid);
+            const uint64_t peers = same_expert_lanes<BITS>(e, valid);
             const int base = valid ? wcnt[wave][e] : 0;
             __builtin_amdgcn_wave_barrier();
             if (valid) {
@@ -151,8 +152,13 @@ hipError_t launch_permute(const Dims &d, const int32_t *topk_idx, const float *t
                           int32_t *offsets, int32_t *sorted_token, float *sorted_w,
                           int32_t *slot_row, hipStream_t s) {
     const int32_t N = static_cast<int32_t>(d.T * d.k);
-    MOE_LAUNCH(k_permute, dim3(1), dim3(kThreads), 0, s, topk_idx, topk_w, N, d.E, d.k,
-                       offsets, sorted_token, sorted_w, slot_row);
+#define MOE_PERMUTE(B) MOE_LAUNCH(k_permute<B>, dim3(1), dim3(kThreads), 0, s, topk_idx, topk_w, N, d.E, d.k, \
+                                   offsets, sorted_token, sorted_w, slot_row)
+    if (d.E <= 32) MOE_PERMUTE(5);
+    else if (d.E <= 64) MOE_PERMUTE(6);
+    else if (d.E <= 128) MOE_PERMUTE(7);
+    else MOE_PERMUTE(8);
+#undef MOE_PERMUTE
     return hipGetLastError();
 }
 

@@ -41,11 +41,13 @@ __device__ inline int rows_of_expert(const int *s_idx, int N, int e, int *s_rows
     return cnt < kMaxRows ? cnt : kMaxRows;
 }
 
-// Lanes of the wavefront whose expert equals this lane's (E <= 256: eight bit ballots).
+// Lanes of the wavefront whose expert equals this lane's, for experts below 2^BITS (one
+// ballot per bit; E <= 256 needs at most eight).
+template <int BITS = 8>
 __device__ __forceinline__ uint64_t same_expert_lanes(int e, bool valid) {
     uint64_t peers = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < BITS; ++b) {
         const bool bit = (e >> b) & 1;
         const uint64_t m = __ballot(bit);
         peers &= bit ? m : ~m;
