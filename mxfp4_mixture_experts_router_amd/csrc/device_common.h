@@ -12,7 +12,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kMaxE = 256;       // most experts the kernels handle (one bit each in a 256-bit mask)
-constexpr int kMaxScaleCols = 128;   // scale bytes per row the decode kernels stage in LDS
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -17,11 +17,12 @@
 // once, then from that XCD's L2) and its activation tiles.
 //
 // Block tile: BM = 128 activation rows (256 A rows: hi, lo) x BN = 256 output columns; the
-// contraction advances BK = 128 (one MFMA step = four scale blocks) per stage. Four
-// wavefronts, one per SIMD, in a 2 x 2 arrangement: wavefront (wm, wn) owns the 16-row A
-// tiles 2 i + wm (i < 8; interleaved so that the rows of a partly filled tile are shared
-// evenly, and tiles past the expert's rows are skipped) and columns 128 wn .. 128 wn + 127,
-// i.e. 8 x 8 MFMA tiles (256 accumulators, in the accumulation registers). Operands go from global memory straight into LDS (global_load_lds: each
+// contraction advances BK = 128 (one MFMA step = four scale blocks) per stage. Eight
+// wavefronts, two per SIMD (so that one's LDS waits overlap the other's MFMAs), in a 4 x 2
+// arrangement: wavefront (wm, wn) owns the 16-row A tiles 4 i + wm (i < 4; interleaved so that
+// the rows of a partly filled tile are shared evenly, and tiles past the expert's rows are
+// skipped) and columns 128 wn .. 128 wn + 127, i.e. 4 x 8 MFMA tiles (128 accumulators).
+// Operands go from global memory straight into LDS (global_load_lds: each
 // lane's 16 or 4 bytes land at the instruction's LDS base + lane * size) into a ring of
 // three stage buffers; a stage's loads are issued two stages before it is multiplied, and
 // one barrier per stage both publishes the stage and retires the buffer the next issue
