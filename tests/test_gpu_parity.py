@@ -423,6 +423,7 @@ PRENORM_CASES = [
     ("decode_20b", None, None, None, None, None, 1),
     ("batched_decode_20b", None, None, None, None, None, 64),
     ("prefill_20b", None, None, None, None, None, 24),
+    ("prefill_120b", None, None, None, None, None, 16),
 ]
 
 
@@ -466,6 +467,7 @@ BANK_CASES = [
     ("tiny", 140, 64, 64, 256, 8, 140),     # maximal E and k
     ("batched_decode_20b", None, None, None, None, None, 64),
     ("prefill_20b", None, None, None, None, None, 24),
+    ("prefill_120b", None, None, None, None, None, 16),
 ]
 
 
