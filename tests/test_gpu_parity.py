@@ -235,6 +235,11 @@ FORWARD_CASES = [
     ("tiny", 17, 64, 64, 256, 8, 17),       # maximal E and k, decode path
     ("tiny", 5, 96, 64, 5, 2, 5),           # non-square, batched decode: a partly filled 64-row tile
     ("tiny", 140, 64, 64, 256, 8, 140),     # maximal E and k, prefill path
+    ("tiny", 2, 64, 64, 1, 1, 2),           # one expert, k = 1 (weight 1), few-token path
+    ("tiny", 9, 64, 64, 1, 1, 9),           # one expert, batched decode path
+    ("tiny", 70, 64, 64, 1, 1, 70),         # one expert, prefill path
+    ("tiny", 9, 64, 64, 3, 3, 9),           # k = E: every expert routed
+    ("tiny", 70, 96, 64, 3, 3, 70),         # k = E, prefill path
     ("decode_20b", None, None, None, None, None, 1),
     ("decode_20b", 2, None, None, None, None, 2),
     ("batched_decode_20b", None, None, None, None, None, 64),
