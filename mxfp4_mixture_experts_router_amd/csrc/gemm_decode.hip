@@ -503,18 +503,23 @@ __global__ __launch_bounds__(NW * 64) void k_down_mx_tokens(
     }
 }
 
-// y[t, d] = bf16(sum_{j < k} part[t*k + j, d] (+ res[t, d])) in slot order. Thread = 4 features.
+// y[t, d] = bf16(sum_{j < K} part[t*K + j, d] (+ res[t, d])) in slot order. Thread = 4
+// features; its K row reads are issued together.
+template <int K>
 __global__ __launch_bounds__(256) void k_combine_slots(const float *__restrict__ part, int T, int H,
-                                                       int k, const uint16_t *__restrict__ res,
+                                                       const uint16_t *__restrict__ res,
                                                        uint16_t *__restrict__ y) {
     const int per_row = H / 4;
     const int q = blockIdx.x * 256 + threadIdx.x;
     if (q >= T * per_row) return;
     const int t = q / per_row, d = (q % per_row) * 4;
+    float4 v[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[j] = *reinterpret_cast<const float4 *>(part + static_cast<int64_t>(t * K + j) * H + d);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const float4 v = *reinterpret_cast<const float4 *>(part + static_cast<int64_t>(t * k + j) * H + d);
-        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
     }
     if (res) add_residual4(s, res + static_cast<int64_t>(t) * H + d);
     const uint32_t lo = f32_to_bf16(s.x) | (static_cast<uint32_t>(f32_to_bf16(s.y)) << 16);
@@ -555,8 +560,19 @@ hipError_t down_tokens_n(const Dims &d, const uint8_t *h8, const uint8_t *hs8, c
 hipError_t launch_combine_decode(const Dims &d, const float *part, const uint16_t *residual, uint16_t *y,
                                  hipStream_t s) {
     const unsigned blocks = static_cast<unsigned>((d.T * (d.H / 4) + 255) / 256);
-    MOE_LAUNCH(k_combine_slots, dim3(blocks), dim3(256), 0, s, part, static_cast<int>(d.T), d.H,
-                       d.k, residual, y);
+#define MOE_COMBINE(K) MOE_LAUNCH((k_combine_slots<K>), dim3(blocks), dim3(256), 0, s, part, \
+                                   static_cast<int>(d.T), d.H, residual, y)
+    switch (d.k) {
+        case 1: MOE_COMBINE(1); break;
+        case 2: MOE_COMBINE(2); break;
+        case 3: MOE_COMBINE(3); break;
+        case 4: MOE_COMBINE(4); break;
+        case 5: MOE_COMBINE(5); break;
+        case 6: MOE_COMBINE(6); break;
+        case 7: MOE_COMBINE(7); break;
+        default: MOE_COMBINE(8); break;
+    }
+#undef MOE_COMBINE
     return hipGetLastError();
 }
 

@@ -425,11 +425,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
     }
 }
 
-// y[t, d] = sum_j o[slot_row[t*k + j], d] in slot order, rounded to bf16. Thread = 4 columns
-// per grid-stride step.
+// y[t, d] = sum_j o[slot_row[t*K + j], d] in slot order, rounded to bf16. Thread = 4 columns
+// per grid-stride step; its K slot indices, then its K rows, are loaded together so that the
+// K row reads are in flight at once.
+template <int K>
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ o,
                                                  const int32_t *__restrict__ slot_row, int64_t T,
-                                                 int H, int k, const uint16_t *__restrict__ res,
+                                                 int H, const uint16_t *__restrict__ res,
                                                  uint16_t *__restrict__ y) {
     const int per_row = H / 4;
     const int64_t total = T * per_row;
@@ -437,10 +439,16 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ o,
          q += static_cast<int64_t>(gridDim.x) * 256) {
         const int64_t t = q / per_row;
         const int d = static_cast<int>(q % per_row) * 4;
+        int32_t sr[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) sr[j] = slot_row[t * K + j];
+        float4 v[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = *reinterpret_cast<const float4 *>(o + static_cast<int64_t>(sr[j]) * H + d);
         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < k; ++j) {
-            const float4 v = *reinterpret_cast<const float4 *>(o + static_cast<int64_t>(slot_row[t * k + j]) * H + d);
-            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
         }
         if (res) add_residual4(s, res + t * H + d);
         const uint32_t lo = f32_to_bf16(s.x) | (static_cast<uint32_t>(f32_to_bf16(s.y)) << 16);
@@ -523,8 +531,19 @@ hipError_t launch_down_grouped(const Dims &d, const uint8_t *h8, const uint8_t *
 
 hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row, const uint16_t *residual,
                           uint16_t *y, hipStream_t s) {
-    MOE_LAUNCH(k_combine, dim3(grid_for(d.T * (d.H / 4))), dim3(256), 0, s, o, slot_row,
-                       d.T, d.H, d.k, residual, y);
+    const dim3 grid(grid_for(d.T * (d.H / 4)));
+#define MOE_COMBINE(K) MOE_LAUNCH((k_combine<K>), grid, dim3(256), 0, s, o, slot_row, d.T, d.H, residual, y)
+    switch (d.k) {
+        case 1: MOE_COMBINE(1); break;
+        case 2: MOE_COMBINE(2); break;
+        case 3: MOE_COMBINE(3); break;
+        case 4: MOE_COMBINE(4); break;
+        case 5: MOE_COMBINE(5); break;
+        case 6: MOE_COMBINE(6); break;
+        case 7: MOE_COMBINE(7); break;
+        default: MOE_COMBINE(8); break;
+    }
+#undef MOE_COMBINE
     return hipGetLastError();
 }
 
