@@ -67,7 +67,7 @@ moe::Dims dims_of(const moe_mxfp4_shape_t *s) {
 
 // Workspace regions (each 256-byte aligned), in order.
 struct Layout {
-    size_t idx, w, logits, offsets, sorted_token, sorted_w, slot_row, o, part, x8, h8, xn, total;
+    size_t idx, w, logits, offsets, sorted_token, sorted_w, slot_row, o, part, x8, h8, xn, hist, total;
 };
 
 size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -89,12 +89,13 @@ Layout layout_of(const moe_mxfp4_shape_t *s) {
         L.part = p;
         if (s->T >= moe::kStreamMinT) p += round_up(N * static_cast<size_t>(s->H) * 4);
         L.logits = p;   p += round_up(static_cast<size_t>(s->T) * s->E * 8);
-        L.offsets = L.sorted_token = L.sorted_w = L.slot_row = L.o = 0;
+        L.offsets = L.sorted_token = L.sorted_w = L.slot_row = L.o = L.hist = 0;
     } else {
         L.offsets = p;      p += round_up((static_cast<size_t>(s->E) + 1) * 4);
         L.sorted_token = p; p += round_up(N * 4);
         L.sorted_w = p;     p += round_up(N * 4);
         L.slot_row = p;     p += round_up(N * 4);
+        L.hist = p;         p += round_up(static_cast<size_t>(moe::permute_hist_ints(N, s->E)) * 4);
         L.x8 = p;           p += round_up(moe::mx8_bytes(s->T, s->H));
         L.h8 = p;           p += round_up(moe::mx8_bytes(static_cast<int64_t>(N), s->I));
         L.o = p;            p += round_up(N * static_cast<size_t>(s->H) * 4);
@@ -106,7 +107,7 @@ Layout layout_of(const moe_mxfp4_shape_t *s) {
 
 // Workspace of the dequantized-bank forward (256-byte aligned regions, in order).
 struct BankLayout {
-    size_t idx, w, offsets, sorted_token, sorted_w, slot_row, h, o, total;
+    size_t idx, w, offsets, sorted_token, sorted_w, slot_row, hist, h, o, total;
 };
 
 BankLayout bank_layout_of(const moe_mxfp4_shape_t *s) {
@@ -119,6 +120,7 @@ BankLayout bank_layout_of(const moe_mxfp4_shape_t *s) {
     L.sorted_token = p; p += round_up(N * 4);
     L.sorted_w = p;     p += round_up(N * 4);
     L.slot_row = p;     p += round_up(N * 4);
+    L.hist = p;         p += round_up(static_cast<size_t>(moe::permute_hist_ints(N, s->E)) * 4);
     L.h = p;            p += round_up(N * static_cast<size_t>(s->I) * 2);
     L.o = p;            p += round_up(N * static_cast<size_t>(s->H) * 4);
     L.total = p;
@@ -282,7 +284,8 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
     float *sorted_w = reinterpret_cast<float *>(ws + L.sorted_w);
     int32_t *slot_row = reinterpret_cast<int32_t *>(ws + L.slot_row);
     float *o = reinterpret_cast<float *>(ws + L.o);
-    STEP(moe::launch_permute(d, idx, w, offsets, sorted_token, sorted_w, slot_row, s), "permute");
+    STEP(moe::launch_permute(d, idx, w, offsets, sorted_token, sorted_w, slot_row, s,
+                             reinterpret_cast<int32_t *>(ws + L.hist)), "permute");
     STEP(moe::launch_up_grouped(d, x8, gu_blocks, gu_scales, gu_bias, offsets, sorted_token, h8, s), "up");
     STEP(moe::launch_down_grouped(d, h8, dn_blocks, dn_scales, dn_bias, offsets, sorted_w, o, s), "down");
     STEP(moe::launch_combine(d, o, slot_row, residual, y, s), "combine");
@@ -416,7 +419,8 @@ moe_status_t run_forward_bank(const moe_mxfp4_shape_t *shape, const moe_bf16_t *
         if (n_launches) *n_launches = launched;          \
     } while (0)
     STEP(moe::launch_route(d, x, nullptr, 0.0, router_w, router_b, idx, w, nullptr, nullptr, s), "route");
-    STEP(moe::launch_permute(d, idx, w, offsets, sorted_token, sorted_w, slot_row, s), "permute");
+    STEP(moe::launch_permute(d, idx, w, offsets, sorted_token, sorted_w, slot_row, s,
+                             reinterpret_cast<int32_t *>(ws + L.hist)), "permute");
     STEP(moe::launch_up_bank(d, x, gu_w, gu_bias, offsets, sorted_token, h, s), "up (bf16 bank)");
     STEP(moe::launch_down_bank(d, h, dn_w, dn_bias, offsets, sorted_w, o, s), "down (bf16 bank)");
     STEP(moe::launch_combine(d, o, slot_row, nullptr, y, s), "combine");

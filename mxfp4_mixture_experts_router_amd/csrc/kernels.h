@@ -57,9 +57,14 @@ hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *gamma,
                         const uint16_t *router_w, const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
                         float *logits, uint8_t *x8, hipStream_t s);
 
+// hist (optional): workspace of permute_hist_ints(T k, E) ints; with it (and that count
+// nonzero) the permutation runs on many workgroups (a histogram pass, then a scatter pass),
+// without it on one. Both give the same result.
+constexpr int64_t kPermuteMaxBlocks = 1024;
+int64_t permute_hist_ints(int64_t N, int E);
 hipError_t launch_permute(const Dims &d, const int32_t *topk_idx, const float *topk_w,
                           int32_t *offsets, int32_t *sorted_token, float *sorted_w,
-                          int32_t *slot_row, hipStream_t s);
+                          int32_t *slot_row, hipStream_t s, int32_t *hist = nullptr);
 
 // up (prefill): h[r] = swiglu(x[sorted_token[r]] . Wgu[e]^T + bgu[e]) for the sorted rows r of
 // every expert e, from the mx8 matrix x8 (T rows of H) into the mx8 matrix h8 (T k rows of I).

@@ -146,12 +146,114 @@ __global__ __launch_bounds__(kThreads) void k_permute(
     }
 }
 
+// The same permutation by many workgroups, for the forward passes (which have workspace for
+// the per-block histograms). Block b owns pairs [b P, (b + 1) P), one per thread.
+// k_permute_count writes hist[b][e], the number of block b's pairs routed to expert e.
+// k_permute_scatter then gives pair n (expert e, block b, wavefront w, lane l) the position
+//   offsets[e] + sum_{b' < b} hist[b'][e] + (pairs of e in wavefronts < w of block b)
+//              + (pairs of e in lanes < l of wavefront w),
+// the count of earlier pairs routed to e: the same stable order as k_permute.
+constexpr int kPT = 256;   // threads (and pairs) per block
+constexpr int kPW = kPT / kWave;
+
+template <int BITS>
+__global__ __launch_bounds__(kPT) void k_permute_count(const int32_t *__restrict__ topk_idx, int32_t N, int E,
+                                                       int32_t *__restrict__ hist) {
+    __shared__ int cnt[kMaxE];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kPT) cnt[e] = 0;
+    __syncthreads();
+    const int n = blockIdx.x * kPT + tid;
+    const int e = n < N ? topk_idx[n] : -1;
+    const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+    const uint64_t peers = same_expert_lanes<BITS>(e, valid);
+    if (valid && (peers & lanemask_lt()) == 0) atomicAdd(&cnt[e], __popcll(peers));
+    __syncthreads();
+    for (int e2 = tid; e2 < E; e2 += kPT) hist[static_cast<int64_t>(blockIdx.x) * E + e2] = cnt[e2];
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kPT) void k_permute_scatter(
+    const int32_t *__restrict__ topk_idx, const float *__restrict__ topk_w, int32_t N, int E, int k,
+    int nblk, const int32_t *__restrict__ hist, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ sorted_token, float *__restrict__ sorted_w, int32_t *__restrict__ slot_row) {
+    __shared__ int tot[kMaxE];        // pairs per expert, all blocks
+    __shared__ int before[kMaxE];     // pairs per expert in blocks < this one
+    __shared__ int start[kMaxE + 1];  // exclusive scan of tot
+    __shared__ int wc[kPW][kMaxE];    // pairs per expert in each wavefront of this block
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int b = blockIdx.x;
+    for (int e = tid; e < E; e += kPT) {
+        tot[e] = 0;
+        before[e] = 0;
+    }
+#pragma unroll
+    for (int w = 0; w < kPW; ++w)
+        for (int e = tid; e < E; e += kPT) wc[w][e] = 0;
+    const int n = b * kPT + tid;
+    const int e = n < N ? topk_idx[n] : -1;
+    const float wt = n < N ? topk_w[n] : 0.f;
+    __syncthreads();
+    // column sums of hist (integers: the order of the LDS atomics does not matter)
+    const int total = nblk * E;
+#pragma unroll 8
+    for (int q = tid; q < total; q += kPT) {
+        const int c = hist[q];
+        const int i = q / E, ee = q - i * E;
+        atomicAdd(&tot[ee], c);
+        if (i < b) atomicAdd(&before[ee], c);
+    }
+    const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+    const uint64_t peers = same_expert_lanes<BITS>(e, valid);
+    if (valid && (peers & lanemask_lt()) == 0) wc[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (wave == 0) wave_exclusive_scan(tot, start, E, lane);
+    __syncthreads();
+    if (b == 0)
+        for (int e2 = tid; e2 <= E; e2 += kPT) offsets[e2] = start[e2];
+    if (valid) {
+        int pos = start[e] + before[e] + __popcll(peers & lanemask_lt());
+        for (int w = 0; w < wave; ++w) pos += wc[w][e];
+        sorted_token[pos] = n / k;
+        sorted_w[pos] = wt;
+        slot_row[n] = pos;
+    }
+}
+
 }  // namespace
+
+int64_t permute_hist_ints(int64_t N, int E) {
+    const int64_t nblk = (N + kPT - 1) / kPT;
+    return nblk <= kPermuteMaxBlocks ? nblk * E : 0;
+}
 
 hipError_t launch_permute(const Dims &d, const int32_t *topk_idx, const float *topk_w,
                           int32_t *offsets, int32_t *sorted_token, float *sorted_w,
-                          int32_t *slot_row, hipStream_t s) {
+                          int32_t *slot_row, hipStream_t s, int32_t *hist) {
     const int32_t N = static_cast<int32_t>(d.T * d.k);
+    const int nblk = static_cast<int>((static_cast<int64_t>(N) + kPT - 1) / kPT);
+    if (hist != nullptr && N > 0 && permute_hist_ints(N, d.E) > 0) {
+        // one stage, two launches: the count kernel records the stage's start event, the
+        // scatter kernel its stop event
+        const LaunchEvents ev = launch_events();
+#define MOE_PERMUTE2(B)                                                                                  \
+    do {                                                                                                 \
+        launch_events() = LaunchEvents{ev.start, nullptr};                                               \
+        MOE_LAUNCH(k_permute_count<B>, dim3(nblk), dim3(kPT), 0, s, topk_idx, N, d.E, hist);             \
+        launch_events() = LaunchEvents{nullptr, ev.stop};                                                \
+        MOE_LAUNCH(k_permute_scatter<B>, dim3(nblk), dim3(kPT), 0, s, topk_idx, topk_w, N, d.E, d.k,     \
+                   nblk, hist, offsets, sorted_token, sorted_w, slot_row);                               \
+        launch_events() = ev;                                                                            \
+    } while (0)
+        if (d.E <= 32) MOE_PERMUTE2(5);
+        else if (d.E <= 64) MOE_PERMUTE2(6);
+        else if (d.E <= 128) MOE_PERMUTE2(7);
+        else MOE_PERMUTE2(8);
+#undef MOE_PERMUTE2
+        return hipGetLastError();
+    }
 #define MOE_PERMUTE(B) MOE_LAUNCH(k_permute<B>, dim3(1), dim3(kThreads), 0, s, topk_idx, topk_w, N, d.E, d.k, \
                                    offsets, sorted_token, sorted_w, slot_row)
     if (d.E <= 32) MOE_PERMUTE(5);
