@@ -149,9 +149,11 @@ moe_status_t moe_mxfp4_forward_prenorm(const moe_mxfp4_shape_t *shape,
  * validation, kernels and results, with every kernel launched through hipExtLaunchKernel so
  * that it records two events at the start and at the end of its own execution. `events`
  * holds at least 2 * MOE_MXFP4_MAX_LAUNCHES hipEvent_t handles created by the caller
- * (timing enabled); launch i records events[2i] and events[2i + 1], so that
- * hipEventElapsedTime(events[2i], events[2i + 1]) is that kernel's duration.
- * *n_launches receives the number of kernels launched. With H <= 4096 and I <= 4096: 3 for
+ * (timing enabled); stage i records events[2i] and events[2i + 1], so that
+ * hipEventElapsedTime(events[2i], events[2i + 1]) is that stage's duration. Every stage is one
+ * kernel except the permute of T > 64, two kernels (a histogram pass, then a scatter pass):
+ * the first records the start event, the second the end event.
+ * *n_launches receives the number of stages. With H <= 4096 and I <= 4096: 3 for
  * T <= 3 (router logits, up-projection with the top-k, down-projection with the combine
  * folded in), 4 for 4 <= T <= 64 (route, up-projection, down-projection, combine); 5 for
  * T > 64 or a larger H or I (route, permute, up-projection, down-projection, combine). MOE_EINVAL if events, an
