@@ -4,24 +4,26 @@
 One step = one call of the whole layer (router, top-k + softmax, permutation,
 gate_up GEMM + SwiGLU, down GEMM, combine) on one batch of synthetic tokens whose
 inputs are already resident in HBM. The headline workload is the GPT-OSS-20B
-shaped single-token decode (T=1, H=I=2880, E=32, top-4); the 4096-token prefill of
-the same layer is measured as a secondary workload in the same run.
+shaped single-token decode (T=1, H=I=2880, E=32, top-4); the skewed 64-token batched
+decode, the 4096-token prefill of the same layer and the 2048-token prefill of the
+120B-shaped layer (E=128) are measured in the same run (``other_workloads``).
 
-Timing: W untimed warmup steps, then K steps bracketed by torch.cuda.synchronize()
-and HIP events on the stream the kernels run on. The weights are replicated R
-times (and x drawn R times) and the steps rotate over the replicas so that the
-256 MB last-level cache cannot serve a step's weights from the previous step.
-By default the K steps are replayed from a HIP graph captured over one rotation
-(--mode eager launches every call from Python instead).
+Timing: W untimed warmup steps, then exactly K steps bracketed by torch.cuda.synchronize()
+and HIP events on the stream the kernels run on; the K steps are timed 5 times and the
+median is reported. The weights are replicated R times (and x drawn R times) and the steps
+rotate over the replicas so that the 256 MB last-level cache cannot serve a step's weights
+from the previous step. By default the steps are replayed from two HIP graphs, one captured
+over a whole rotation and one over the first K mod R replicas (--mode eager launches every
+call from Python instead). One cold call (after a 512 MiB write has evicted the caches) is
+timed on its own.
 
-Also reported, in the same JSON line:
+Also reported, in the same JSON line, per workload:
 * roofline: the dominant kernel's average duration, measured with the start / end HIP
   events each kernel of a moe_mxfp4_forward_timed call records around itself, turned into
-  achieved GB/s (HBM-bound decode) or TFLOP/s (MFMA-bound prefill) from its
-  algorithmic bytes or flops per launch, against MI355X's published peak;
-  `traffic` comes from the committed rocprofv3 counter summary for that kernel
-  when its source has not changed since;
-* cpu_baseline: the CPU oracle timed on this host on a bounded sample of tokens.
+  achieved GB/s and TFLOP/s from its algorithmic bytes and flops per launch, against
+  MI355X's published peaks (the binding one in `frac`); `traffic` comes from the committed
+  rocprofv3 counter summary for that kernel when its source has not changed since;
+* cpu_baseline: the CPU oracle (expert-major mode) timed on this host on the same inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode graph|eager]
 """
@@ -85,19 +87,27 @@ def kernel_source_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
+OTHER_WORKLOADS = "batched_decode_20b,prefill_20b,prefill_120b"
+DEFAULT_STEPS = {"decode_20b": 2000, "batched_decode_20b": 500, "prefill_20b": 100, "prefill_120b": 100}
+REPEATS = 5
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps of the headline workload (default: 2000); the other workloads "
+                         "time min(K, their default) steps")
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode_20b")
-    ap.add_argument("--secondary", default="prefill_20b", help="'' to skip")
-    ap.add_argument("--secondary-steps", type=int, default=100)
+    ap.add_argument("--also", "--secondary", dest="also", default=OTHER_WORKLOADS,
+                    help="comma-separated other workloads measured in the same run ('' to skip)")
+    ap.add_argument("--repeats", type=int, default=REPEATS, help="timed repetitions (median reported)")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to defeat the LLC")
     ap.add_argument("--timed-steps", type=int, default=200, help="steps of the per-kernel timing run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the CPU sample (0 = auto)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold single-call timing")
     ap.add_argument("--prenorm", action="store_true",
                     help="time the pre-norm block y = x + layer(rmsnorm(x)) instead of the layer")
     ap.add_argument("--dequantized-bank", action="store_true",
@@ -233,59 +243,97 @@ class Workload:
             raise RuntimeError(self.lib.moe_mxfp4_last_error().decode())
 
 
-def run_timed(wl: Workload, steps: int, warmup: int, mode: str):
-    """Whole-layer throughput. Returns (ms_per_step, wall_ms_per_step, mode_used)."""
+def _capture(wl: Workload, replicas):
+    """A HIP graph of one call per replica in `replicas`, checked bit for bit against eager
+    launches of the same calls over three replays."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ref = {r: wl.y[r].clone() for r in replicas}
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for r in replicas:
+            wl.step(r, side.cuda_stream)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream()
+        for r in replicas:
+            wl.step(r, cap.cuda_stream)
+    for _ in range(3):
+        for r in replicas:
+            wl.y[r].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for r in replicas:
+            if not torch.equal(wl.y[r].view(torch.int16), ref[r].view(torch.int16)):
+                raise RuntimeError("graph replay differs from eager launches")
+    return graph
+
+
+def run_timed(wl: Workload, steps: int, warmup: int, mode: str, repeats: int):
+    """Whole-layer time per step: exactly `steps` steps (rotating over the replicas), timed
+    `repeats` times. Returns (median ms/step, all ms/step, wall ms/step of the median run)."""
     import torch
     stream = torch.cuda.current_stream()
     for i in range(max(warmup, wl.R)):
         wl.step(i % wl.R, stream.cuda_stream)
     torch.cuda.synchronize()
-    reps = max(1, -(-steps // wl.R))
-    steps = reps * wl.R
-    graph = None
+    full, rest = divmod(steps, wl.R)
+    graphs = []
     if mode == "graph":
-        ref = [y.clone() for y in wl.y]
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for r in range(wl.R):
-                wl.step(r, side.cuda_stream)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            cap = torch.cuda.current_stream()
-            for r in range(wl.R):
-                wl.step(r, cap.cuda_stream)
-        for y in wl.y:
-            y.zero_()
-        torch.cuda.synchronize()
-        for _ in range(3):
-            graph.replay()
-            torch.cuda.synchronize()
-            for y, want in zip(wl.y, ref):
-                if not torch.equal(y.view(torch.int16), want.view(torch.int16)):
-                    raise RuntimeError("graph replay differs from eager launches")
-            for y in wl.y:
-                y.zero_()
-        for _ in range(2):
-            graph.replay()
+        g_all = _capture(wl, list(range(wl.R)))
+        g_rest = _capture(wl, list(range(rest))) if rest else None
+        graphs = [g_all] * full + ([g_rest] if g_rest is not None else [])
+        for g in graphs[:2]:
+            g.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    if graph is not None:
-        for _ in range(reps):
-            graph.replay()
-    else:
-        sp = stream.cuda_stream
-        for i in range(steps):
-            wl.step(i % wl.R, sp)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3
-    gpu_ms = start.elapsed_time(end)
-    return gpu_ms / steps, wall / steps, steps, mode
+    times, walls = [], []
+    for _ in range(repeats):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        if graphs:
+            for g in graphs:
+                g.replay()
+        else:
+            sp = stream.cuda_stream
+            for i in range(steps):
+                wl.step(i % wl.R, sp)
+        end.record(stream)
+        torch.cuda.synchronize()
+        walls.append((time.perf_counter() - t0) * 1e3 / steps)
+        times.append(start.elapsed_time(end) / steps)
+    order = sorted(range(repeats), key=lambda i: times[i])
+    med = order[repeats // 2]
+    return times[med], times, walls[med]
+
+
+def run_cold(wl: Workload):
+    """One call after a 512 MiB write has pushed every weight byte out of the L2s and the
+    last-level cache: GPU time between events recorded around the call on its stream (host
+    launch included), and host wall time until it has finished."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = None
+    for _ in range(3):
+        flush.fill_(1)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        wl.step(0, stream.cuda_stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        gpu = start.elapsed_time(end)
+        if best is None or gpu < best[0]:
+            best = (gpu, wall)
+    del flush
+    return {"gpu_ms": round(best[0], 4), "wall_ms": round(best[1], 4), "runs": 3, "reported": "fastest"}
 
 
 def run_per_kernel(wl: Workload, steps: int, hip: Hip):
@@ -395,6 +443,8 @@ def roofline_for(wl: Workload, stages, kernel_us, D):
     else:
         roof = {"bound": "hbm", "achieved": e["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(e["GB/s"] / HBM_PEAK_GBS, 4)}
+    roof["hbm_frac"] = round(e["GB/s"] / HBM_PEAK_GBS, 4)
+    roof["mfma_frac"] = round(e["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)
     roof["kernel"] = e["kernel"]
     roof["alg_bytes_per_launch"] = e["alg_bytes"]
     roof["alg_flops_per_launch"] = e["alg_flops"]
@@ -403,9 +453,10 @@ def roofline_for(wl: Workload, stages, kernel_us, D):
     return roof, entries
 
 
-def measure(name, steps, warmup, mode, replicas, timed_steps, hip, variant="layer"):
+def measure(name, steps, warmup, mode, replicas, timed_steps, hip, variant="layer", repeats=REPEATS,
+            cold=True):
     wl = Workload.create(name, replicas, variant)
-    ms, wall_ms, steps_run, mode = run_timed(wl, steps, warmup, mode)
+    ms, all_ms, wall_ms = run_timed(wl, steps, warmup, mode, repeats)
     D = distinct_experts(wl)
     stages = stages_of(wl.cfg.T, variant)
     kus = run_per_kernel(wl, timed_steps, hip)
@@ -413,32 +464,126 @@ def measure(name, steps, warmup, mode, replicas, timed_steps, hip, variant="laye
     layer_bytes = sum(kernel_work(wl, s, D)[0] for s in stages)
     layer_flops = sum(kernel_work(wl, s, D)[1] for s in stages)
     return wl, {
-        "ms_per_step": ms, "wall_ms_per_step": wall_ms, "steps": steps_run, "mode": mode,
+        "ms_per_step": ms, "ms_per_step_repeats": [round(t, 6) for t in all_ms],
+        "wall_ms_per_step": wall_ms, "steps": steps, "mode": mode,
         "value": wl.cfg.T / (ms * 1e-3), "distinct_experts": D, "roofline": roof,
         "kernels": kernels, "bank_dequant_ms": wl.bank_dequant_ms,
+        "cold_call": run_cold(wl) if cold else None,
         "layer": {"alg_bytes": int(layer_bytes), "alg_flops": int(layer_flops),
                   "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
 
 
-def cpu_baseline(wl: Workload, sample: int):
+def cpu_threads():
+    """Threads the oracle uses: OpenMP's (its C loops) and the BLAS library's (its matrix
+    products)."""
+    import oracle
+    omp = oracle.max_threads()
+    blas = None
+    try:
+        import threadpoolctl
+        blas = max((p["num_threads"] for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"),
+                   default=None)
+    except Exception:   # threadpoolctl missing or unreadable: report OpenMP's count only
+        blas = None
+    return omp, blas
+
+
+def cpu_baseline(wl: Workload):
+    """The oracle's expert-major mode on the same inputs as replica 0 (all T tokens): the median
+    of 3 runs up to 64 tokens, one run above."""
     import numpy as np
     import oracle
-    from workloads import make_inputs
-    cores = oracle.max_threads()
-    n = sample if sample > 0 else max(16, 12 * cores)
     inp = dict(wl.host_weights)
-    inp["x"] = make_inputs(wl.cfg, seed=10_000, T=n, parts=("x",))["x"]
-    t0 = time.perf_counter()
-    if wl.prenorm:
-        oracle.forward_prenorm(inp, wl.cfg.k, alpha=wl.cfg.alpha, limit=wl.cfg.limit, eps=wl.NORM_EPS)
-    else:
-        oracle.forward(inp, wl.cfg.k, alpha=wl.cfg.alpha, limit=wl.cfg.limit)
-    dt = time.perf_counter() - t0
-    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} tokens of the {wl.label} layer (same weights), plain fp64 C oracle, "
-                      f"{dt:.1f} s"}
+    inp["x"] = wl.host_x[0]
+    runs = 3 if wl.cfg.T <= 64 else 1
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        if wl.prenorm:
+            oracle.forward_prenorm_expert_major(inp, wl.cfg.k, alpha=wl.cfg.alpha, limit=wl.cfg.limit,
+                                                eps=wl.NORM_EPS)
+        else:
+            oracle.forward_expert_major(inp, wl.cfg.k, alpha=wl.cfg.alpha, limit=wl.cfg.limit)
+        ts.append(time.perf_counter() - t0)
+    dt = float(np.median(ts))
+    omp, blas = cpu_threads()
+    return {"value": round(wl.cfg.T / dt, 4), "unit": "tokens/s", "cores": max(omp, blas or 0),
+            "kind": "oracle",
+            "sample": f"the whole {wl.label} workload ({wl.cfg.T} tokens, same weights and x as the GPU's "
+                      f"replica 0), oracle expert-major mode (fp64: C dequantization and SwiGLU with OpenMP, "
+                      f"float64 BLAS matrix products), {'median of 3 runs' if runs > 1 else 'one run'}, "
+                      f"{dt:.2f} s per run",
+            "omp_threads": omp, "blas_threads": blas}
+
+
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    git = None
+    try:
+        import subprocess
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=5)
+        git = r.stdout.strip() or None if r.returncode == 0 else None
+    except Exception:   # no git, or not a checkout (the source hash below still identifies the code)
+        git = None
+    h = hashlib.sha256()
+    for sub in ("include", os.path.join("mxfp4_mixture_experts_router_amd", "csrc")):
+        d = os.path.join(ROOT, sub)
+        for f in sorted(os.listdir(d)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    with open(os.path.abspath(__file__), "rb") as fh:
+        h.update(fh.read())
+    return {"cpu_model": model, "host_cores": len(os.sched_getaffinity(0)), "git_sha": git,
+            "source_sha16": h.hexdigest()[:16]}
+
+
+def hbm_probe():
+    """Streaming-read bandwidth of this GPU with a plain library reduction (torch.sum over
+    2 GiB of fp32, best of 5), as context for the roofline's published 8 TB/s."""
+    import torch
+    a = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    a.sum()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(5):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        a.sum()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end)
+        best = ms if best is None else min(best, ms)
+    del a
+    return {"read_GBps": round(4 * (1 << 29) / (best * 1e-3) / 1e9, 1),
+            "method": "torch.sum over 2 GiB fp32, best of 5"}
+
+
+def record(wl, res, cpu):
+    cfg = wl.cfg
+    out = {
+        "workload": wl.label, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k,
+        "value": round(res["value"], 2), "unit": "tokens/s",
+        "ms_per_step": round(res["ms_per_step"], 6), "ms_per_step_repeats": res["ms_per_step_repeats"],
+        "steps": res["steps"], "replicas": wl.R, "mode": res["mode"],
+        "distinct_experts_per_step": res["distinct_experts"],
+        "roofline": res["roofline"], "layer_roofline": res["layer"], "kernels": res["kernels"],
+        "wall_ms_per_step": round(res["wall_ms_per_step"], 6), "cold_call": res["cold_call"],
+    }
+    if res["bank_dequant_ms"]:
+        out["bank_dequant_ms"] = round(res["bank_dequant_ms"], 4)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    return out
 
 
 def main():
@@ -462,8 +607,9 @@ def main():
         print("--prenorm and --dequantized-bank are separate variants", file=sys.stderr)
         sys.exit(2)
     variant = "prenorm" if args.prenorm else ("dequantized" if args.dequantized_bank else "layer")
-    wl, main_res = measure(args.workload, args.steps, args.warmup, args.mode, args.replicas,
-                           args.timed_steps, hip, variant)
+    steps = args.steps if args.steps is not None else DEFAULT_STEPS.get(args.workload, 100)
+    wl, main_res = measure(args.workload, steps, args.warmup, args.mode, args.replicas,
+                           args.timed_steps, hip, variant, args.repeats, not args.no_cold)
     cfg = wl.cfg
     out = {
         "metric": METRIC,
@@ -483,23 +629,30 @@ def main():
                    "distinct_experts_per_step": main_res["distinct_experts"]},
         "roofline": main_res["roofline"],
         "layer_roofline": main_res["layer"],
+        "timing": {"repeats": args.repeats, "reported": "median", "ms_per_step_repeats":
+                   main_res["ms_per_step_repeats"]},
+        "cold_call": main_res["cold_call"],
         "wall_ms_per_step": round(main_res["wall_ms_per_step"], 6),
         "kernels": main_res["kernels"],
         **({"bank_dequant_ms": round(main_res["bank_dequant_ms"], 4)} if main_res["bank_dequant_ms"] else {}),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(wl)
     del wl
     torch.cuda.empty_cache()
-    if args.secondary:
-        wl2, res2 = measure(args.secondary, args.secondary_steps, min(args.warmup, 10), args.mode,
-                            0, min(args.timed_steps, 50), hip, variant)
-        out["secondary"] = {
-            "workload": wl2.label, "T": wl2.cfg.T, "E": wl2.cfg.E,
-            "value": round(res2["value"], 1), "unit": "tokens/s",
-            "ms_per_step": round(res2["ms_per_step"], 6), "steps": res2["steps"],
-            "replicas": wl2.R, "roofline": res2["roofline"], "layer_roofline": res2["layer"],
-            "kernels": res2["kernels"], "bank_dequant_ms": res2["bank_dequant_ms"]}
+    others = []
+    for name in [n for n in args.also.split(",") if n and n != args.workload]:
+        st = min(steps, DEFAULT_STEPS.get(name, 100)) if args.steps is not None else DEFAULT_STEPS.get(name, 100)
+        wl2, res2 = measure(name, st, min(args.warmup, 10), args.mode, 0, min(args.timed_steps, 50), hip,
+                            variant, args.repeats, not args.no_cold)
+        cpu2 = None if args.no_cpu_baseline else cpu_baseline(wl2)
+        others.append(record(wl2, res2, cpu2))
+        del wl2
+        torch.cuda.empty_cache()
+    if others:
+        out["other_workloads"] = others
+    out["host"] = host_info()
+    out["hbm_probe"] = hbm_probe()
     print(json.dumps(out), flush=True)
 
 

@@ -24,7 +24,7 @@ import torch
 __all__ = [
     "MoeError", "MoeLibraryMissing", "library_path", "load_library", "abi_version",
     "workspace_bytes", "moe_forward", "route", "permute", "expert_up", "expert_down",
-    "combine", "dequant", "DECODE_MAX_T", "DECODE_MAX_K", "uses_decode_path", "mx8_bytes",
+    "combine", "dequant", "permute_workspace_bytes", "DECODE_MAX_T", "DECODE_MAX_K", "uses_decode_path", "mx8_bytes",
     "quantize_act", "rmsnorm", "moe_forward_dequantized", "dequantize_bank", "workspace_bytes_dequantized",
 ]
 
@@ -87,6 +87,9 @@ _SIGS = {
     "moe_mxfp4_rmsnorm": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, _vp, _vp]),
     "moe_mxfp4_route": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 7),
     "moe_mxfp4_permute": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 7),
+    "moe_mxfp4_permute_ws": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 7 + [ctypes.c_size_t, _vp]),
+    "moe_mxfp4_permute_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(Shape),
+                                                         ctypes.POINTER(ctypes.c_size_t)]),
     "moe_mxfp4_expert_up": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 8),
     "moe_mxfp4_expert_down": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 8),
     "moe_mxfp4_combine": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 4),
@@ -282,8 +285,19 @@ def route(x, router_w, router_b, k: int, return_logits: bool = False, stream=Non
     return (idx, w, logits) if return_logits else (idx, w)
 
 
-def permute(topk_idx, topk_w, E: int, stream=None):
-    """Expert-sorted permutation. Returns (offsets [E+1], sorted_token, sorted_weight, slot_row)."""
+def permute_workspace_bytes(T: int, E: int, k: int) -> int:
+    """Workspace bytes of the many-workgroup permutation (0: it runs on one workgroup)."""
+    out = ctypes.c_size_t(0)
+    s = _shape(T, 32, 32, E, k)
+    _check(load_library().moe_mxfp4_permute_workspace_bytes(ctypes.byref(s), ctypes.byref(out)))
+    return int(out.value)
+
+
+def permute(topk_idx, topk_w, E: int, stream=None, multi_block: bool = False):
+    """Expert-sorted permutation. Returns (offsets [E+1], sorted_token, sorted_weight, slot_row).
+
+    ``multi_block``: the histogram + scatter passes the forward calls run (moe_mxfp4_permute_ws),
+    instead of the one-workgroup kernel (moe_mxfp4_permute)."""
     T, k = topk_idx.shape
     dev = topk_idx.device
     _need(topk_idx, "topk_idx", (torch.int32,), (T, k), dev)
@@ -293,9 +307,16 @@ def permute(topk_idx, topk_w, E: int, stream=None):
     sorted_w = torch.empty(T * k, dtype=torch.float32, device=dev)
     slot_row = torch.empty(T * k, dtype=torch.int32, device=dev)
     shape = _shape(T, 32, 32, E, k)
-    _check(load_library().moe_mxfp4_permute(ctypes.byref(shape), _ptr(topk_idx), _ptr(topk_w),
-                                            _ptr(offsets), _ptr(sorted_token), _ptr(sorted_w),
-                                            _ptr(slot_row), _stream(stream)))
+    if multi_block:
+        nbytes = permute_workspace_bytes(T, E, k)
+        ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
+        _check(load_library().moe_mxfp4_permute_ws(ctypes.byref(shape), _ptr(topk_idx), _ptr(topk_w),
+                                                   _ptr(offsets), _ptr(sorted_token), _ptr(sorted_w),
+                                                   _ptr(slot_row), _ptr(ws), ws.numel(), _stream(stream)))
+    else:
+        _check(load_library().moe_mxfp4_permute(ctypes.byref(shape), _ptr(topk_idx), _ptr(topk_w),
+                                                _ptr(offsets), _ptr(sorted_token), _ptr(sorted_w),
+                                                _ptr(slot_row), _stream(stream)))
     return offsets, sorted_token, sorted_w, slot_row
 
 

@@ -483,6 +483,41 @@ MOE_EXPORT moe_status_t moe_mxfp4_permute(const moe_mxfp4_shape_t *shape, const 
     return ok();
 }
 
+MOE_EXPORT moe_status_t moe_mxfp4_permute_workspace_bytes(const moe_mxfp4_shape_t *shape, size_t *bytes) {
+    moe_status_t st = check_shape(shape, false);
+    if (st != MOE_OK) return st;
+    REQUIRE(bytes, "bytes");
+    *bytes = static_cast<size_t>(moe::permute_hist_ints(shape->T * shape->k, shape->E)) * 4;
+    return ok();
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_permute_ws(const moe_mxfp4_shape_t *shape, const int32_t *topk_idx,
+                                             const float *topk_w, int32_t *expert_offsets,
+                                             int32_t *sorted_token, float *sorted_weight, int32_t *slot_row,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+    moe_status_t st = check_shape(shape, false);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    REQUIRE(topk_idx, "topk_idx");
+    REQUIRE(topk_w, "topk_w");
+    REQUIRE(expert_offsets, "expert_offsets");
+    REQUIRE(sorted_token, "sorted_token");
+    REQUIRE(sorted_weight, "sorted_weight");
+    REQUIRE(slot_row, "slot_row");
+    const size_t need = static_cast<size_t>(moe::permute_hist_ints(shape->T * shape->k, shape->E)) * 4;
+    int32_t *hist = nullptr;
+    if (need > 0) {
+        if (!workspace) return fail(MOE_EWORKSPACE, "workspace is NULL");
+        if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(MOE_EALIGN, "workspace is not 4-byte aligned");
+        if (workspace_bytes < need)
+            return fail(MOE_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+        hist = static_cast<int32_t *>(workspace);
+    }
+    LAUNCH(moe::launch_permute(dims_of(shape), topk_idx, topk_w, expert_offsets, sorted_token, sorted_weight,
+                               slot_row, static_cast<hipStream_t>(stream), hist), "permute");
+    return ok();
+}
+
 MOE_EXPORT moe_status_t moe_mxfp4_rmsnorm(const moe_bf16_t *x, const moe_bf16_t *norm_w, int64_t rows,
                                           int32_t cols, double eps, moe_bf16_t *xn, void *stream) {
     if (rows < 0) return fail(MOE_EINVAL, "rows = %lld is negative", static_cast<long long>(rows));

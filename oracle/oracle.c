@@ -12,7 +12,8 @@
  * decoding), so the only rounding is that of the double operations themselves.
  * Loops follow the definitions in the order the pages state them; no blocking,
  * reordering or fusion beyond what the definitions say. Parallelism (OpenMP)
- * is only across independent tokens and never changes a token's arithmetic.
+ * is only across independent tokens or independent output elements and never
+ * changes the arithmetic of any one result.
  *
  * Sources (web pages, cited by title and section):
  *  [ZM]  ZeroModels "GPT-OSS" documentation page: the intro list items
@@ -104,13 +105,26 @@ static double weight_at(const uint8_t *blocks, const uint8_t *scales,
     return oracle_e2m1(code) * oracle_e8m0(scales[row * (cols / 32) + col / 32]);
 }
 
-/* Dequantize a whole packed [rows, cols] matrix to double. */
+/*
+ * Dequantize a whole packed [rows, cols] matrix to double: out[r, c] is weight_at(r, c),
+ * with the 16 E2M1 codes and the 256 E8M0 bytes decoded once each by the functions above
+ * (rows are independent; OpenMP splits them across threads).
+ */
 ORACLE_API void oracle_dequant(const uint8_t *blocks, const uint8_t *scales,
                                int64_t rows, int64_t cols, double *out)
 {
+    double value[16], scale[256];
+    for (int code = 0; code < 16; ++code)
+        value[code] = oracle_e2m1(code);
+    for (int byte = 0; byte < 256; ++byte)
+        scale[byte] = oracle_e8m0(byte);
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r)
-        for (int64_t c = 0; c < cols; ++c)
-            out[r * cols + c] = weight_at(blocks, scales, r, c, cols);
+        for (int64_t c = 0; c < cols; ++c) {
+            const uint8_t byte = blocks[r * (cols / 2) + c / 2];
+            const int code = (c & 1) ? (byte >> 4) : (byte & 0x0F);
+            out[r * cols + c] = value[code] * scale[scales[r * (cols / 32) + c / 32]];
+        }
 }
 
 /*
@@ -124,6 +138,15 @@ ORACLE_API double oracle_swiglu(double gate, double up, double alpha, double lim
     double u = up < -limit ? -limit : (up > limit ? limit : up);
     double sigmoid = 1.0 / (1.0 + exp(-alpha * g));
     return (u + 1.0) * g * sigmoid;
+}
+
+/* oracle_swiglu applied element by element: h[i] = swiglu(gate[i], up[i]). */
+ORACLE_API void oracle_swiglu_n(const double *gate, const double *up, int64_t n, double alpha, double limit,
+                                double *h)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        h[i] = oracle_swiglu(gate[i], up[i], alpha, limit);
 }
 
 /*

@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert moe.abi_version() == 3
-    assert "#define MOE_MXFP4_ABI_VERSION 3" in open(HEADER).read()
+    assert moe.abi_version() == 4
+    assert "#define MOE_MXFP4_ABI_VERSION 4" in open(HEADER).read()
 
 
 def shape(T=1, H=2880, I=2880, E=32, k=4, alpha=1.702, limit=7.0):
@@ -250,3 +250,30 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(moe.MoeLibraryMissing):
         moe.load_library()
+
+
+@pytest.mark.parametrize("T,E,k,blocks", [(64, 32, 4, 1), (65, 32, 4, 2), (4096, 32, 4, 64), (2048, 128, 4, 32),
+                                          (65536, 32, 4, 1024), (65537, 32, 4, 0), (1, 256, 8, 1)])
+def test_permute_workspace_bytes(lib, T, E, k, blocks):
+    """One histogram row of E ints per 256 pairs, up to 1024 rows; none above (one workgroup)."""
+    s = shape(T=T, E=E, k=k)
+    n = ctypes.c_size_t(12345)
+    assert lib.moe_mxfp4_permute_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == 0
+    assert n.value == blocks * E * 4
+
+
+def test_permute_ws_validation(lib):
+    s = shape(T=100, E=32, k=4)       # 400 pairs: 2 histogram rows of 32 ints
+    need = 2 * 32 * 4
+    args = [A, A, A, A, A, A]
+    assert lib.moe_mxfp4_permute_ws(ctypes.byref(s), *args, None, need, None) == EWORKSPACE
+    assert lib.moe_mxfp4_permute_ws(ctypes.byref(s), *args, A, need - 1, None) == EWORKSPACE
+    assert lib.moe_mxfp4_permute_ws(ctypes.byref(s), *args, A + 2, need, None) == EALIGN
+    for i in range(6):
+        bad = list(args)
+        bad[i] = None
+        assert lib.moe_mxfp4_permute_ws(ctypes.byref(s), *bad, A, need, None) == EINVAL
+    bad_shape = shape(T=100, E=32, k=33)
+    assert lib.moe_mxfp4_permute_ws(ctypes.byref(bad_shape), *args, A, need, None) == ESHAPE
+    zero = shape(T=0, E=32, k=4)
+    assert lib.moe_mxfp4_permute_ws(ctypes.byref(zero), None, None, None, None, None, None, None, 0, None) == 0

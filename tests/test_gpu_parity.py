@@ -7,7 +7,8 @@ GPT-OSS-20B decode / batched decode / 4k prefill shapes and the 120B-shaped pref
 plus fixtures: non-square H != I, duplicated router rows (ties), zero up rows
 (gate/up interleave), maximal E and k, and ragged token counts on both sides of the
 decode/prefill switch. Full-size configs run in the same launch configuration as the
-benchmark and are compared on a sample of tokens (every token is independent).
+benchmark and are compared on every token (the 4096-token and 120B-shaped workloads against
+the oracle's expert-major mode).
 """
 import numpy as np
 import pytest
@@ -33,6 +34,15 @@ def _lib():
     moe.load_library()
     yield
     torch.cuda.synchronize()
+
+
+def _reference(inp, cfg, tokens, **kw):
+    """The oracle's layer for ``tokens``: the brute mode up to the work of 64 tokens of the
+    GPT-OSS shape, the expert-major mode (pinned to it on CPU) beyond, so that the full-size
+    workloads are compared on every token."""
+    big = len(tokens) * cfg.H * cfg.I > 64 * 2880 * 2880
+    fn = oracle.forward_expert_major if big else oracle.forward
+    return fn(inp, cfg.k, tokens=tokens, alpha=cfg.alpha, limit=cfg.limit, **kw)
 
 
 def _sample(T, n, seed=0):
@@ -138,22 +148,33 @@ def test_route_max_experts_and_k():
 # ----------------------------------------------------------------------------- permute
 
 def _random_routing(T, E, k, seed, skew=0.0):
+    """k distinct experts per token, drawn without replacement with skewed probabilities
+    (Gumbel top-k of log p: the same distribution as sequential draws without replacement)."""
     rng = np.random.default_rng(seed)
-    p = np.exp(skew * rng.standard_normal(E))
-    p /= p.sum()
-    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    logp = skew * rng.standard_normal(E)
+    keys = logp[None, :] + rng.gumbel(size=(T, E))
+    idx = np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
     w = rng.random((T, k)).astype(np.float32)
     return idx, w
 
 
-@pytest.mark.parametrize("T,E,k,skew", [(1, 32, 4, 0.0), (64, 32, 4, 2.0), (4096, 32, 4, 0.0),
-                                        (2048, 128, 4, 1.0), (333, 256, 8, 3.0), (1025, 4, 4, 0.0),
-                                        (500, 16, 1, 5.0), (4097, 32, 4, 0.0), (5000, 64, 4, 1.0)])
-def test_permute_is_a_stable_sort(T, E, k, skew):
-    # T k = 16384 pairs and fewer are sorted in LDS; 16388 and 20000 take the direct path
+PERMUTE_CASES = [(1, 32, 4, 0.0), (64, 32, 4, 2.0), (4096, 32, 4, 0.0), (2048, 128, 4, 1.0),
+                 (333, 256, 8, 3.0), (1025, 4, 4, 0.0), (500, 16, 1, 5.0), (4097, 32, 4, 0.0),
+                 (5000, 64, 4, 1.0),
+                 (32, 256, 8, 0.0),        # 256 pairs: one block of the two-pass permute
+                 (20000, 256, 8, 2.0),     # 625 blocks, E = 256, k = 8
+                 (65536, 32, 4, 1.0),      # 1024 blocks: the largest two-pass permute
+                 (65537, 32, 4, 1.0)]      # 262148 pairs: past 1024 blocks, one workgroup
+
+
+@pytest.mark.parametrize("multi_block", [False, True], ids=["one_workgroup", "two_pass"])
+@pytest.mark.parametrize("T,E,k,skew", PERMUTE_CASES)
+def test_permute_is_a_stable_sort(T, E, k, skew, multi_block):
+    # one workgroup: T k = 16384 pairs and fewer are sorted in LDS, more take the direct path;
+    # two-pass: the histogram + scatter kernels every forward of the grouped sequence runs
     idx, w = _random_routing(T, E, k, seed=T + E, skew=skew)
     offsets, sorted_token, order, slot_row = host_permutation(idx, E)
-    g_off, g_tok, g_w, g_slot = moe.permute(to_dev(idx), to_dev(w), E)
+    g_off, g_tok, g_w, g_slot = moe.permute(to_dev(idx), to_dev(w), E, multi_block=multi_block)
     np.testing.assert_array_equal(g_off.cpu().numpy(), offsets)
     np.testing.assert_array_equal(g_tok.cpu().numpy(), sorted_token)
     np.testing.assert_array_equal(g_w.cpu().numpy(), w.reshape(-1)[order])
@@ -162,24 +183,20 @@ def test_permute_is_a_stable_sort(T, E, k, skew):
 
 # ----------------------------------------------------------------------------- grouped experts
 
-def _grouped_case(cfg, T, seed, n_sample):
+def _grouped_case(cfg, T, seed):
     inp = make_inputs(cfg, seed=seed, T=T)
-    tokens = _sample(T, n_sample, seed)
-    ref = oracle.forward(inp, cfg.k, tokens=tokens, alpha=cfg.alpha, limit=cfg.limit,
-                         intermediates=True)
-    # the routing of all tokens (the permutation needs every row): oracle router + top-k
-    logits = oracle.router(inp["x"], inp["router_w"], inp["router_b"])
-    idx, w = oracle.topk_softmax(logits, cfg.k)
-    assert np.array_equal(idx[tokens], ref["idx"])
-    return inp, tokens, ref, idx, w
+    tokens = np.arange(T)
+    ref = _reference(inp, cfg, tokens, intermediates=True)
+    return inp, tokens, ref, ref["idx"], ref["w"]
 
 
 @pytest.mark.parametrize("name,T,H,I,E,k", [
     ("tiny", 8, 64, 64, 4, 2), ("tiny", 200, 96, 64, 5, 2), ("tiny", 333, 64, 128, 3, 2),
     ("prefill_20b", 4096, 2880, 2880, 32, 4), ("prefill_120b", 2048, 2880, 2880, 128, 4)])
 def test_expert_up_and_down_grouped(name, T, H, I, E, k):
+    """Every row of h and o, and every token of y, against the oracle."""
     cfg = CONFIGS[name].with_(H=H, I=I, E=E, k=k)
-    inp, tokens, ref, idx, w = _grouped_case(cfg, T, seed=7, n_sample=24)
+    inp, tokens, ref, idx, w = _grouped_case(cfg, T, seed=7)
     offsets, sorted_token, order, slot_row = host_permutation(idx, E)
     d = upload(inp)
     x8 = moe.quantize_act(d["x"])
@@ -240,11 +257,15 @@ FORWARD_CASES = [
     ("tiny", 70, 64, 64, 1, 1, 70),         # one expert, prefill path
     ("tiny", 9, 64, 64, 3, 3, 9),           # k = E: every expert routed
     ("tiny", 70, 96, 64, 3, 3, 70),         # k = E, prefill path
+    ("tiny", 3, 4128, 64, 4, 2, 3),         # H > 4096 at few tokens: the grouped sequence
+    ("tiny", 17, 4128, 64, 4, 2, 17),
+    ("tiny", 3, 64, 4128, 4, 2, 3),         # I > 4096 at few tokens: the grouped sequence
+    ("tiny", 17, 64, 4128, 4, 2, 17),
     ("decode_20b", None, None, None, None, None, 1),
     ("decode_20b", 2, None, None, None, None, 2),
     ("batched_decode_20b", None, None, None, None, None, 64),
-    ("prefill_20b", None, None, None, None, None, 24),
-    ("prefill_120b", None, None, None, None, None, 24),
+    ("prefill_20b", None, None, None, None, None, 4096),
+    ("prefill_120b", None, None, None, None, None, 2048),
 ]
 
 
@@ -256,7 +277,7 @@ def test_forward_matches_oracle(name, T, H, I, E, k, n_cmp):
     T = cfg.T if T is None else T
     inp = make_inputs(cfg, seed=1, T=T)
     tokens = _sample(T, n_cmp, seed=T)
-    ref = oracle.forward(inp, cfg.k, tokens=tokens, alpha=cfg.alpha, limit=cfg.limit)
+    ref = _reference(inp, cfg, tokens)
     d = upload(inp)
     y, idx, w = _forward(d, cfg.k, cfg, return_topk=True)
     y_np = bf16_to_f64(y)[tokens]
@@ -333,11 +354,14 @@ class _HipEvents:
             self.lib.hipEventDestroy(self.c.c_void_p(ev))
 
 
-@pytest.mark.parametrize("T,launches,prenorm", [(1, 3, False), (3, 3, False), (4, 4, False), (17, 4, False),
-                                                (65, 5, False), (1, 3, True), (17, 4, True), (65, 6, True)])
-def test_forward_timed_matches_forward(T, launches, prenorm):
+@pytest.mark.parametrize("T,launches,prenorm,H,I", [
+    (1, 3, False, 64, 64), (3, 3, False, 64, 64), (4, 4, False, 64, 64), (17, 4, False, 64, 64),
+    (65, 5, False, 64, 64), (1, 3, True, 64, 64), (17, 4, True, 64, 64), (65, 6, True, 64, 64),
+    # H or I above 4096: the grouped sequence at any token count
+    (3, 5, False, 4128, 64), (17, 5, False, 64, 4128), (3, 6, True, 4128, 64), (17, 6, True, 64, 4128)])
+def test_forward_timed_matches_forward(T, launches, prenorm, H, I):
     import ctypes
-    cfg = CONFIGS["tiny"]
+    cfg = CONFIGS["tiny"].with_(H=H, I=I)
     inp = upload(make_inputs(cfg, seed=5, T=T))
     norm = dict(norm_weight=inp["norm_w"], norm_eps=1e-5) if prenorm else {}
     y_ref = _forward(inp, cfg.k, cfg, **norm)
@@ -425,10 +449,12 @@ PRENORM_CASES = [
     ("tiny", 5, 96, 64, 5, 2, 5),
     ("tiny", 65, 96, 64, 5, 2, 65),
     ("tiny", 5, 3616, 64, 4, 2, 5),         # H > 3584 from 4 tokens: the RMSNorm kernel of its own
+    ("tiny", 3, 4128, 64, 4, 2, 3),         # H > 4096 at few tokens: RMSNorm kernel + grouped sequence
+    ("tiny", 17, 64, 4128, 4, 2, 17),       # I > 4096 at few tokens: RMSNorm kernel + grouped sequence
     ("decode_20b", None, None, None, None, None, 1),
     ("batched_decode_20b", None, None, None, None, None, 64),
-    ("prefill_20b", None, None, None, None, None, 24),
-    ("prefill_120b", None, None, None, None, None, 16),
+    ("prefill_20b", None, None, None, None, None, 4096),
+    ("prefill_120b", None, None, None, None, None, 2048),
 ]
 
 
@@ -441,7 +467,9 @@ def test_forward_prenorm_matches_oracle(name, T, H, I, E, k, n_cmp):
     inp = make_inputs(cfg, seed=3, T=T)
     tokens = _sample(T, n_cmp, seed=T + 1)
     eps = 1e-5
-    ref = oracle.forward_prenorm(inp, cfg.k, tokens=tokens, alpha=cfg.alpha, limit=cfg.limit, eps=eps)
+    big = len(tokens) * cfg.H * cfg.I > 64 * 2880 * 2880
+    ref_fn = oracle.forward_prenorm_expert_major if big else oracle.forward_prenorm
+    ref = ref_fn(inp, cfg.k, tokens=tokens, alpha=cfg.alpha, limit=cfg.limit, eps=eps)
     d = upload(inp)
     y, idx, w = _forward(d, cfg.k, cfg, return_topk=True, norm_weight=d["norm_w"], norm_eps=eps)
     # the normalized rows the layer ran on
@@ -471,8 +499,8 @@ BANK_CASES = [
     ("tiny", 300, 64, 128, 3, 2, 300),      # several ragged row tiles per expert
     ("tiny", 140, 64, 64, 256, 8, 140),     # maximal E and k
     ("batched_decode_20b", None, None, None, None, None, 64),
-    ("prefill_20b", None, None, None, None, None, 24),
-    ("prefill_120b", None, None, None, None, None, 16),
+    ("prefill_20b", None, None, None, None, None, 4096),
+    ("prefill_120b", None, None, None, None, None, 2048),
 ]
 
 
@@ -486,7 +514,7 @@ def test_forward_dequantized_matches_oracle(name, T, H, I, E, k, n_cmp):
     T = cfg.T if T is None else T
     inp = make_inputs(cfg, seed=2, T=T)
     tokens = _sample(T, n_cmp, seed=T + 2)
-    ref = oracle.forward(inp, cfg.k, tokens=tokens, alpha=cfg.alpha, limit=cfg.limit)
+    ref = _reference(inp, cfg, tokens)
     d = upload(inp)
     gu_w, dn_w = moe.dequantize_bank(d["gu_blocks"], d["gu_scales"], d["dn_blocks"], d["dn_scales"])
     y, idx, w = moe.moe_forward_dequantized(d["x"], d["router_w"], d["router_b"], gu_w, d["gu_bias"], dn_w,

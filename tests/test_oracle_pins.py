@@ -415,3 +415,61 @@ def test_prenorm_block_is_residual_plus_layer_of_normalized_rows():
     # gamma = 0 normalizes every row to zero: the layer then sees only its biases
     zero = oracle.forward_prenorm(dict(inp, norm_w=np.zeros_like(inp["norm_w"])), cfg.k)
     assert (f32_from_bf16_bits(zero["xn"]) == 0.0).all()          # (+-0: the sign of x survives)
+
+
+# ---------------------------------------------------------------- expert-major mode
+
+def _modes_agree(inp, k, tokens=None, alpha=1.702, limit=7.0, rel=1e-12):
+    a = oracle.forward(inp, k, tokens=tokens, alpha=alpha, limit=limit, intermediates=True)
+    b = oracle.forward_expert_major(inp, k, tokens=tokens, alpha=alpha, limit=limit, intermediates=True)
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+    np.testing.assert_array_equal(a["w"], b["w"])
+    np.testing.assert_array_equal(a["logits"], b["logits"])
+    for key in ("h", "o", "y"):
+        d = np.linalg.norm((a[key] - b[key]).reshape(a[key].shape[0], -1), axis=1)
+        n = np.linalg.norm(a[key].reshape(a[key].shape[0], -1), axis=1)
+        assert np.all(d <= rel * n), (key, float((d / n).max()))
+    return a, b
+
+
+@pytest.mark.parametrize("H,I,E,k,T", [(64, 64, 4, 2, 8), (96, 64, 5, 2, 40), (64, 128, 3, 3, 17),
+                                       (64, 64, 1, 1, 6), (64, 96, 256, 8, 11)])
+def test_expert_major_equals_brute_mode_small(H, I, E, k, T):
+    """The two oracle modes compute the same definitions: identical routing, and h, o, y
+    equal to double rounding (only the order inside the dot products differs); non-square
+    shapes, one expert with k = 1, k = E and the largest E and k."""
+    cfg = CONFIGS["tiny"].with_(H=H, I=I, E=E, k=k)
+    _modes_agree(make_inputs(cfg, seed=11, T=T), k)
+
+
+def test_expert_major_equals_brute_mode_decode_shapes():
+    """The 20B-shaped decode (T = 1) and a token subset of the skewed batched decode, where
+    several tokens share experts and an expert's tokens come from different slots."""
+    cfg = CONFIGS["decode_20b"]
+    _modes_agree(make_inputs(cfg, seed=1), cfg.k, rel=1e-6)
+    cfg = CONFIGS["batched_decode_20b"]
+    a, _ = _modes_agree(make_inputs(cfg, seed=1), cfg.k, tokens=[0, 5, 9, 17, 33, 63], rel=1e-6)
+    assert len(np.unique(a["idx"])) < a["idx"].size     # experts shared between tokens
+
+
+def test_expert_major_interleave_fixture():
+    """Zero up rows with up bias -1: every h is 0, so y = sum_j w_j b_dn[e_j] in this mode too."""
+    cfg = CONFIGS["tiny"].with_(H=64, I=96, E=4, k=2)
+    inp = make_inputs(cfg, seed=9, T=12)
+    inp["gu_blocks"].reshape(4, 2 * 96, 32)[:, 1::2, :] = 0
+    inp["gu_bias"][:, 1::2] = bf16_bits_from_f32(np.array([-1.0], dtype=np.float32))[0]
+    out = oracle.forward_expert_major(inp, cfg.k, intermediates=True)
+    assert np.all(out["h"] == 0.0)
+    b_dn = f32_from_bf16_bits(inp["dn_bias"]).astype(np.float64)
+    want = np.zeros((12, 64))
+    for j in range(cfg.k):
+        want += out["w"][:, j:j + 1] * b_dn[out["idx"][:, j]]
+    np.testing.assert_allclose(out["y"], want, rtol=1e-15, atol=0)
+
+
+def test_swiglu_n_matches_scalar():
+    rng = np.random.default_rng(4)
+    g = rng.standard_normal(1000) * 10
+    u = rng.standard_normal(1000) * 10
+    h = oracle.swiglu_n(g, u)
+    assert np.array_equal(h, np.array([oracle.swiglu(a, b) for a, b in zip(g, u)]))
