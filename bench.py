@@ -548,24 +548,33 @@ def host_info():
 
 
 def hbm_probe():
-    """Streaming-read bandwidth of this GPU with a plain library reduction (torch.sum over
-    2 GiB of fp32, best of 5), as context for the roofline's published 8 TB/s."""
+    """Bandwidth of this GPU's HBM with plain library kernels, as context for the roofline's
+    published 8 TB/s: a 1 GiB device-to-device copy (bytes read + written) and a reduction over
+    2 GiB of fp32 (bytes read), best of 5 each."""
     import torch
-    a = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
-    a.sum()
-    torch.cuda.synchronize()
-    best = None
-    for _ in range(5):
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record()
-        a.sum()
-        end.record()
+
+    def best_ms(fn):
+        fn()
         torch.cuda.synchronize()
-        ms = start.elapsed_time(end)
-        best = ms if best is None else min(best, ms)
-    del a
-    return {"read_GBps": round(4 * (1 << 29) / (best * 1e-3) / 1e9, 1),
-            "method": "torch.sum over 2 GiB fp32, best of 5"}
+        best = None
+        for _ in range(5):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            fn()
+            end.record()
+            torch.cuda.synchronize()
+            ms = start.elapsed_time(end)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    a = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    read = 4 * (1 << 29) / (best_ms(lambda: a.sum()) * 1e-3) / 1e9
+    src = a[: 1 << 28]
+    dst = torch.empty_like(src)
+    copy = 2 * 4 * (1 << 28) / (best_ms(lambda: dst.copy_(src)) * 1e-3) / 1e9
+    del a, dst
+    return {"copy_GBps": round(copy, 1), "sum_read_GBps": round(read, 1),
+            "method": "torch copy of 1 GiB (read + write bytes) and torch.sum over 2 GiB fp32, best of 5"}
 
 
 def record(wl, res, cpu):
