@@ -141,6 +141,32 @@ moe_status_t moe_mxfp4_forward_prenorm(const moe_mxfp4_shape_t *shape,
                                        moe_bf16_t *y, int32_t *topk_idx, float *topk_w,
                                        void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * moe_mxfp4_forward without a workspace argument and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The workspace is a static device array of the library: one copy of
+ * moe_mxfp4_noalloc_max_bytes() = 64 MiB per GPU the library runs on, allocated when the
+ * library's code object is loaded on that GPU and held until the process ends. The call
+ * itself allocates and frees nothing. Every call on one GPU uses that GPU's copy, so calls
+ * that overlap on one GPU (on different streams, or from different threads without ordering)
+ * race and give undefined results; calls ordered on one stream are safe. Shapes whose
+ * moe_mxfp4_workspace_bytes() exceeds the array return MOE_EWORKSPACE (at the GPT-OSS-20B
+ * shape: up to 820 tokens, which covers every decode batch). The GPU is the
+ * stream's (the current device for the NULL stream). Arguments, results and every other error
+ * as moe_mxfp4_forward (same kernels, bit-identical results).
+ */
+moe_status_t moe_mxfp4_forward_noalloc(const moe_mxfp4_shape_t *shape,
+                                       const moe_bf16_t *x,
+                                       const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                                       const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                                       const moe_bf16_t *gu_bias,
+                                       const uint8_t *dn_blocks, const uint8_t *dn_scales,
+                                       const moe_bf16_t *dn_bias,
+                                       moe_bf16_t *y, int32_t *topk_idx, float *topk_w, void *stream);
+
+/* Bytes of the per-GPU static workspace of moe_mxfp4_forward_noalloc. Host-only. */
+size_t moe_mxfp4_noalloc_max_bytes(void);
+
 /* Most kernels one moe_mxfp4_forward or moe_mxfp4_forward_prenorm call launches. */
 #define MOE_MXFP4_MAX_LAUNCHES 6
 

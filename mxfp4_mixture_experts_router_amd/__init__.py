@@ -84,6 +84,8 @@ _SIGS = {
                                                ctypes.POINTER(ctypes.c_int)]),
     "moe_mxfp4_workspace_bytes_dequantized": (ctypes.c_int, [ctypes.POINTER(Shape),
                                                              ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_mxfp4_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 12 + [_vp]),
+    "moe_mxfp4_noalloc_max_bytes": (ctypes.c_size_t, []),
     "moe_mxfp4_rmsnorm": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, _vp, _vp]),
     "moe_mxfp4_route": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 7),
     "moe_mxfp4_permute": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 7),

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -347,6 +348,76 @@ MOE_EXPORT moe_status_t moe_mxfp4_forward_timed(
     return run_forward(shape, x, nullptr, 0.0, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks,
                        dn_scales, dn_bias, y, topk_idx, topk_w, workspace, workspace_bytes, stream,
                        events, n_events, n_launches);
+}
+
+// ---------------------------------------------------------------------------------------
+// The allocation-free forward: the workspace is a static device array of the library, one
+// copy per GPU (allocated by the runtime when the code object is loaded on that GPU, held until
+// the process ends). In host code `scratch` names a host-side stand-in, never the device
+// memory: the device address is taken once per GPU with hipGetSymbolAddress and only that
+// address is passed to kernels.
+namespace {
+
+constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on `device` (looked up once, with that device current).
+moe_status_t scratch_of(int device, void **out) {
+    if (device < 0 || device >= kMaxDevices) return fail(MOE_EHIP, "device %d outside 0..%d", device, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[device]) {
+        int prev = 0;
+        hipError_t e = hipGetDevice(&prev);
+        if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+        if (prev != device && (e = hipSetDevice(device)) != hipSuccess) return hip_status(e, "hipSetDevice");
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        hipError_t e2 = prev != device ? hipSetDevice(prev) : hipSuccess;
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (e2 != hipSuccess) return hip_status(e2, "hipSetDevice");
+        if (!p) return fail(MOE_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[device] = p;
+    }
+    *out = g_scratch_ptr[device];
+    return MOE_OK;
+}
+
+}  // namespace
+
+MOE_EXPORT size_t moe_mxfp4_noalloc_max_bytes(void) { return kScratchBytes; }
+
+MOE_EXPORT moe_status_t moe_mxfp4_forward_noalloc(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
+                                                  const moe_bf16_t *router_w, const moe_bf16_t *router_b,
+                                                  const uint8_t *gu_blocks, const uint8_t *gu_scales,
+                                                  const moe_bf16_t *gu_bias, const uint8_t *dn_blocks,
+                                                  const uint8_t *dn_scales, const moe_bf16_t *dn_bias,
+                                                  moe_bf16_t *y, int32_t *topk_idx, float *topk_w, void *stream) {
+    moe_status_t st = check_shape(shape, true);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    const size_t need = layout_of(shape).total;
+    if (need > kScratchBytes)
+        return fail(MOE_EWORKSPACE,
+                    "this shape needs %zu bytes of workspace; the allocation-free entry point has %zu "
+                    "(use moe_mxfp4_forward with a workspace, or split the batch)",
+                    need, kScratchBytes);
+    int device = 0;
+    hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &device) : hipGetDevice(&device);
+    if (e != hipSuccess) return hip_status(e, "device of the stream");
+    void *ws = nullptr;
+    st = scratch_of(device, &ws);
+    if (st != MOE_OK) return st;
+    return run_forward(shape, x, nullptr, 0.0, router_w, router_b, gu_blocks, gu_scales, gu_bias, dn_blocks,
+                       dn_scales, dn_bias, y, topk_idx, topk_w, ws, kScratchBytes, stream, nullptr, 0, nullptr);
 }
 
 MOE_EXPORT moe_status_t moe_mxfp4_workspace_bytes_dequantized(const moe_mxfp4_shape_t *shape, size_t *bytes) {

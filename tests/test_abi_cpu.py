@@ -277,3 +277,18 @@ def test_permute_ws_validation(lib):
     assert lib.moe_mxfp4_permute_ws(ctypes.byref(bad_shape), *args, A, need, None) == ESHAPE
     zero = shape(T=0, E=32, k=4)
     assert lib.moe_mxfp4_permute_ws(ctypes.byref(zero), None, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_noalloc_limit_and_rejection(lib):
+    """The allocation-free forward states its scratch size and rejects larger workspaces on the
+    host, before touching the GPU."""
+    limit = lib.moe_mxfp4_noalloc_max_bytes()
+    assert limit == 64 << 20
+    assert moe.workspace_bytes(64, 2880, 2880, 32, 4) <= limit          # every decode batch fits
+    s = shape(T=4096)
+    assert moe.workspace_bytes(4096, 2880, 2880, 32, 4) > limit
+    st = lib.moe_mxfp4_forward_noalloc(ctypes.byref(s), *([A] * 10), None, None, None)
+    assert st == EWORKSPACE
+    assert "workspace" in lib.moe_mxfp4_last_error().decode()
+    bad = shape(H=2881)
+    assert lib.moe_mxfp4_forward_noalloc(ctypes.byref(bad), *([A] * 10), None, None, None) == ESHAPE
