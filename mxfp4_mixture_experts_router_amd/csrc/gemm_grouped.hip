@@ -18,17 +18,18 @@
 //
 // Block tile: BM = 128 activation rows (256 A rows: hi, lo) x BN = 256 output columns; the
 // contraction advances BK = 128 (one MFMA step = four scale blocks) per stage. Eight
-// wavefronts, two per SIMD (so that one's LDS waits overlap the other's MFMAs), in a 4 x 2
-// arrangement: wavefront (wm, wn) owns the 16-row A tiles 4 i + wm (i < 4; interleaved so that
-// the rows of a partly filled tile are shared evenly, and tiles past the expert's rows are
-// skipped) and columns 128 wn .. 128 wn + 127, i.e. 4 x 8 MFMA tiles (128 accumulators).
+// wavefronts, two per SIMD, in a 4 x 2 arrangement: wavefront (wm, wn) owns the 16-row A
+// tiles 4 i + wm (i < 4; interleaved so that the rows of a partly filled tile are shared
+// evenly, and tiles past the expert's rows are skipped) and columns 128 wn .. 128 wn + 127,
+// i.e. 4 x 8 MFMA tiles (128 accumulators). The two wavefronts of a SIMD (wn = 0 and 1) run
+// one phase apart (ping-pong): while one multiplies from registers, the other reads its
+// next operands from LDS and issues global loads, and barriers separate the phases.
 // Operands go from global memory straight into LDS (global_load_lds: each
 // lane's 16 or 4 bytes land at the instruction's LDS base + lane * size) into a ring of
-// three stage buffers; a stage's loads are issued two stages before it is multiplied, and
-// one barrier per stage both publishes the stage and retires the buffer the next issue
-// overwrites. The loads are issued from inline assembly: the compiler then neither knows of
-// them nor inserts its own (all-draining) waits before LDS reads; the kernel waits for
-// exactly the stage it needs with vmcnt and publishes it with a barrier.
+// three stage buffers; a stage's loads are issued two stages before it is multiplied. The
+// loads are issued from inline assembly: the compiler then neither knows of them nor
+// inserts its own (all-draining) waits before LDS reads; the kernel waits for exactly the
+// stage it needs with vmcnt and publishes it with a barrier.
 //
 // Stage buffer layout (bytes):
 //   A   [256 rows][128]: row R = 2 * (tile row) + part; its eight 16-byte chunks c are stored
@@ -49,6 +50,15 @@ namespace moe {
 namespace {
 
 template <int N> struct IntC { static constexpr int value = N; };
+
+// f(IntC<0>{}), ..., f(IntC<N - 1>{}): compile-time indices (instruction operand selects).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(IntC<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
 
 constexpr int kBM = 128;                       // activation rows per tile
 constexpr int kAR = 2 * kBM;                   // A rows per tile (hi, lo)
@@ -206,8 +216,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         const uint32_t b_ch = 16 * b_c, b_ch_last = b_c < b_vb ? 16 * b_c : 0;
 
         const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)g_stages;
-        // the loads of stage kt into buffer buf, in parts issued between the row tiles'
-        // MFMAs of the current stage, so that no wavefront stalls on a burst of them
+        // the wavefront's share of stage kt's loads into buffer buf, in three parts (A rows of
+        // instructions 0-1, 2-3 with the A scales, B rows with the B scales)
         auto issue_part_of = [&](const Addr &S, int part, int buf, int kt) {
             const uint32_t lbuf = lds0 + buf * kStage;
             const uint32_t ach = kt == kt_last ? a_ch_last : a_ch;
@@ -241,58 +251,96 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
 #pragma unroll
             for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // --- multiply. B fragments and scales of the wavefront's eight column tiles are read
-        // first and kept; A fragments are then streamed one row tile at a time (8 MFMAs
-        // each). LDS addresses are one per-lane base per operand plus constants. The scales
-        // are read as single bytes: A row R's block g, and weight row n's block g at byte
-        // (n K/32) % 4 + g of its 8-byte window (the same for all eight column tiles: they
-        // are 16 rows apart).
+        // --- multiply: an 8-wavefront ping-pong. The wavefronts 0-3 (one per SIMD) and 4-7 (the
+        // other one per SIMD) alternate between a memory phase and a matrix phase, one phase
+        // apart, separated by workgroup barriers: while one wavefront of a SIMD multiplies
+        // from registers, the other reads its next stage's operands from LDS and issues its
+        // share of a later stage's global loads, so the matrix unit is fed from both.
+        //   phase 2s:     wavefronts 0-3 read stage s;       4-7 multiply stage s - 1
+        //   phase 2s + 1: wavefronts 0-3 multiply stage s;   4-7 read stage s
+        // In its memory phase for stage s a wavefront also issues its loads of stage s + 2
+        // into the buffer stage s - 1 used (both groups have read it by then). Before phase 2s
+        // every wavefront waits for its loads of stage s (only stage s + 1's stay in flight),
+        // and the barrier then publishes the stage; a memory phase ends with its LDS reads
+        // complete, so the buffer is free for the refill that follows.
+        //
+        // Operand reads: B fragments and scales of the wavefront's eight column tiles, then
+        // the A fragments of its row tiles. LDS addresses are one per-lane base per operand
+        // plus constants. The scales are read as single bytes: A row R's block g, and weight
+        // row n's block g at byte (n K/32) % 4 + g of its 8-byte window (the same for all
+        // eight column tiles: they are 16 rows apart).
         const uint32_t lb_b = kOffB + 8192 * wn + 64 * m + 16 * (g ^ ((m >> 1) & 3));
         const uint32_t lb_bs = kOffBS + 1024 * wn + 8 * m + (((n0 + 128 * wn + m) * nkb) & 3) + g;
         const uint32_t lb_a = 2048 * wm + 128 * m + 16 * (g ^ (m & 7));
         const uint32_t lb_as = kOffAS + 64 * wm + 4 * m + g;
         // the wavefront's row tiles are the tile's 16-row tiles 4 mt + wm (interleaved, so
         // that a partly filled tile splits its rows evenly); only the first NL are multiplied
+        uint4 bq[8], alo[4], ahi[4];
+        // scale bytes packed four to a register (column tiles 4i .. 4i + 3 in sbp[i], row
+        // tiles in sap); the instruction's operand select picks the byte
+        uint32_t sbp[2], sap;
         // In the last stage of a contraction whose block count is not a multiple of 4
         // (vb < 4, a uniform branch), blocks past K get zero A data and unit scales, so they
-        // add exactly 0. Stage kt + 2's loads (if any) go out between the row tiles.
-        auto compute = [&](int buf, int kt, bool refill, int buf2) {
+        // add exactly 0.
+        auto read_stage = [&](int kt) {
+            const int buf = kt % 3;
             const uint8_t *base = g_stages + buf * kStage;
-            i32x8 bop[8];
-            uint32_t sb[8];
+            const int vb = nkb - 4 * kt;
+            uint32_t sb[8], sa[4];
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
-                bop[nt] = mx_b_operand(*reinterpret_cast<const uint4 *>(base + lb_b + 1024 * nt));
+                bq[nt] = *reinterpret_cast<const uint4 *>(base + lb_b + 1024 * nt);
                 sb[nt] = base[lb_bs + 128 * nt];
             }
-            const int vb = nkb - 4 * kt;
+#pragma unroll
+            for (int mt = 0; mt < NL; ++mt) {
+                alo[mt] = *reinterpret_cast<const uint4 *>(base + lb_a + 8192 * mt);
+                ahi[mt] = *reinterpret_cast<const uint4 *>(base + (lb_a ^ 64u) + 8192 * mt);   // chunk g + 4
+                sa[mt] = base[lb_as + 256 * mt];
+            }
+#pragma unroll
+            for (int mt = NL; mt < 4; ++mt) sa[mt] = 127u;
             if (vb < 4) {
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt) sb[nt] = g < vb ? sb[nt] : 127u;
-            }
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                if (mt < NL) {
-                    uint4 lo16 = *reinterpret_cast<const uint4 *>(base + lb_a + 8192 * mt);
-                    uint4 hi16 = *reinterpret_cast<const uint4 *>(base + (lb_a ^ 64u) + 8192 * mt);   // chunk g + 4
-                    uint32_t sa = base[lb_as + 256 * mt];
-                    if (vb < 4) {
-                        // lane group g carries blocks g / 2 (low half) and 2 + g / 2 (high half)
-                        if ((g >> 1) >= vb) lo16 = zero4();
-                        if (2 + (g >> 1) >= vb) hi16 = zero4();
-                        if (g >= vb) sa = 127u;
-                    }
-                    const i32x8 af = mx_a_operand(lo16, hi16);
-#pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = mfma_mx(af, bop[nt], acc[mt][nt], sa, sb[nt]);
+                for (int mt = 0; mt < NL; ++mt) {
+                    // lane group g carries blocks g / 2 (low half) and 2 + g / 2 (high half)
+                    if ((g >> 1) >= vb) alo[mt] = zero4();
+                    if (2 + (g >> 1) >= vb) ahi[mt] = zero4();
+                    if (g >= vb) sa[mt] = 127u;
                 }
-                if (refill && mt < 3) issue_part(mt, buf2, kt + 2);
+            }
+            sbp[0] = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
+            sbp[1] = sb[4] | (sb[5] << 8) | (sb[6] << 16) | (sb[7] << 24);
+            sap = sa[0] | (sa[1] << 8) | (sa[2] << 16) | (sa[3] << 24);
+        };
+        auto multiply = [&]() {
+            static_for<NL>([&](auto mt_c) {
+                constexpr int mt = decltype(mt_c)::value;
+                const i32x8 af = mx_a_operand(alo[mt], ahi[mt]);
+                static_for<8>([&](auto nt_c) {
+                    constexpr int nt = decltype(nt_c)::value;
+                    acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        af, mx_b_operand(bq[nt]), acc[mt][nt], 0, 4, mt, static_cast<int>(sap), nt & 3,
+                        static_cast<int>(sbp[nt >> 2]));
+                });
+            });
+        };
+        // every wavefront's loads of stage s have landed (stage s + 1's, if any, stay in flight)
+        auto wait_stage = [&](int s) {
+            if (s + 1 < kt_total) {
+                if (wave < 4) wait_vm<kOpsLo>(); else wait_vm<kOpsHi>();
+            } else {
+                wait_vm<0>();
             }
         };
+        auto phase_end = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            barrier_only();
+            __builtin_amdgcn_sched_barrier(0);
+        };
 
-        // stage kt (buffer kt % 3): wait for its loads (stage kt + 1's stay in flight),
-        // publish it to all wavefronts, multiply while refilling the buffer stage kt - 1 used
-        // with stage kt + 2.
         // the epilogue's bias and routing-weight loads go out now (their latency hides behind
         // the contraction) and land in LDS after it
         const int bcol = min(n0 + tid, Nrows - 1);
@@ -319,17 +367,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         }
         issue(0, 0);
         if (kt_total > 1) issue(1, 1);
-        int buf = 0;
-        for (int kt = 0; kt < kt_total; ++kt) {
-            if (kt + 1 < kt_total) {
-                if (wave < 4) wait_vm<kOpsLo>(); else wait_vm<kOpsHi>();
-            } else {
-                wait_vm<0>();
+        wait_stage(0);
+        phase_end();
+        // the memory phase for stage kt: its operands into registers, stage kt + 2's loads out
+        auto mem_phase = [&](int kt) {
+            read_stage(kt);
+            if (kt + 2 < kt_total) issue((kt + 2) % 3, kt + 2);
+            wait_lgkm0();
+        };
+        if (wave < 4) {
+            for (int kt = 0; kt < kt_total; ++kt) {
+                mem_phase(kt);                               // phase 2 kt
+                phase_end();
+                multiply();                                  // phase 2 kt + 1
+                if (kt + 1 < kt_total) wait_stage(kt + 1);
+                phase_end();
             }
-            barrier_only();
-            const int buf2 = buf == 0 ? 2 : buf - 1;     // (kt + 2) % 3
-            compute(buf, kt, kt + 2 < kt_total, buf2);
-            buf = buf == 2 ? 0 : buf + 1;
+            phase_end();                                     // phase 2 kt_total: idle
+        } else {
+            phase_end();                                     // phase 0: idle
+            for (int kt = 0; kt < kt_total; ++kt) {
+                mem_phase(kt);                               // phase 2 kt + 1
+                if (kt + 1 < kt_total) wait_stage(kt + 1);
+                phase_end();
+                multiply();                                  // phase 2 kt + 2
+                phase_end();
+            }
         }
         if (tid < kBN) s_bias[tid] = bias_v;
         if (!UP && tid < kBM) s_rw[tid] = rw_v;

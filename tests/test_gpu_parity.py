@@ -261,6 +261,9 @@ FORWARD_CASES = [
     ("tiny", 17, 4128, 64, 4, 2, 17),
     ("tiny", 3, 64, 4128, 4, 2, 3),         # I > 4096 at few tokens: the grouped sequence
     ("tiny", 17, 64, 4128, 4, 2, 17),
+    ("tiny", 1, 3104, 64, 4, 2, 1),         # T = 1 at widths past 3072
+    ("tiny", 1, 64, 3072, 4, 4, 1),
+    ("tiny", 1, 64, 3104, 2, 2, 1),
     ("decode_20b", None, None, None, None, None, 1),
     ("decode_20b", 2, None, None, None, None, 2),
     ("batched_decode_20b", None, None, None, None, None, 64),
