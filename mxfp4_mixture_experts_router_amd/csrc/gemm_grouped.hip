@@ -31,14 +31,22 @@
 // inserts its own (all-draining) waits before LDS reads; the kernel waits for exactly the
 // stage it needs with vmcnt and publishes it with a barrier.
 //
+// Scale loads fetch a few bytes from each of many rows, so they touch far more cache lines
+// than their size suggests; they are kept few. Only the hi rows' A scales are loaded (an
+// mx8 lo row's scale is always its hi row's minus 4), and the weight scales are loaded in
+// 16-byte windows that serve three stages.
+//
 // Stage buffer layout (bytes):
 //   A   [256 rows][128]: row R = 2 * (tile row) + part; its eight 16-byte chunks c are stored
 //       at slot c ^ (R & 7) (conflict-free operand reads).
 //   B   [256 rows][64]: the stage's four packed MXFP4 blocks of weight row n, block c at
 //       slot c ^ ((n >> 1) & 3).
-//   AS  [256 rows] 4 bytes: the E8M0 scales of the stage's four blocks of A row R.
-//   BS  [256 rows] 8 bytes: the 4-byte-aligned 8 bytes of the weight scale row holding the
-//       stage's four scale bytes (weight scale rows are K / 32 bytes long, not 4-aligned).
+//   AS  [128 tile rows] 4 bytes: the E8M0 scales of the stage's four blocks of the hi row.
+// Then two weight-scale group buffers (group j = stages 3j .. 3j + 2, buffer j % 2):
+//   BSG [256 rows] 16 bytes: the four 4-byte-aligned dwords of weight scale row n that hold
+//       the group's twelve scale bytes (weight scale rows are K / 32 bytes long, not
+//       4-aligned); a dword past the tensor's end holds no valid byte and reads the last
+//       dword instead.
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -68,14 +76,16 @@ constexpr int kThreads = 512;                  // 8 wavefronts: 4 row groups x 2
 constexpr int kChunk = 32;                     // items per XCD chunk (= blocks per XCD)
 constexpr int kOffB = kAR * kBK;               // 32768
 constexpr int kOffAS = kOffB + kBN * kBK / 2;  // 49152
-constexpr int kOffBS = kOffAS + kAR * 4;       // 50176
-constexpr int kStage = kOffBS + kBN * 8;       // 52224
-// global_load_lds per wavefront per stage: 4 A, 2 B, 1 B-scale, and 1 A-scale for wavefronts 0-3
-constexpr int kOpsLo = 8, kOpsHi = 7;
+constexpr int kStage = kOffAS + kBM * 4;       // 49664
+constexpr int kGS = 3;                         // stages per weight-scale group
+constexpr int kOffBSG = 3 * kStage;            // 148992
+constexpr int kBSG = kBN * 16;                 // bytes per weight-scale group buffer
+// global_load_lds per wavefront per stage: 4 A, 2 B, 1 A-scale for wavefronts 0-1, and 2
+// weight-scale dwords per group (with the group's first stage)
 constexpr int kHS = 67;                        // up epilogue: padded row of 64 fp32 pairs
 constexpr int kOS = 132;                       // down epilogue: padded row of 128 fp32 outputs
 
-__shared__ __attribute__((aligned(16))) uint8_t g_stages[3 * kStage];
+__shared__ __attribute__((aligned(16))) uint8_t g_stages[3 * kStage + 2 * kBSG];
 
 template <bool UP>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
     // (the host keeps every operand below 4 GiB).
     struct Addr {
         int e, row0, rows, n0;
-        uint32_t a_off[4], as_off, b_off[2], bs_off[1], last4;
+        uint32_t a_off[4], as_off, b_off[2], bs_off[2], last4;
         const uint8_t *wblk, *wsc;
     };
     // the tile rows' token indices: tok (LDS, the tile's rows in order) or, with nullptr, the
@@ -170,19 +180,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         // A: instruction i of wavefront w fills A rows 32 w + 8 i + lane / 8
 #pragma unroll
         for (int i = 0; i < 4; ++i) A.a_off[i] = a_src(32 * wave + 8 * i + (lane >> 3)) * static_cast<uint32_t>(K);
-        // A scales: wavefront w < 4 fills rows 64 w + lane
-        A.as_off = a_src(64 * (wave & 3) + lane) * static_cast<uint32_t>(ass);
+        // A scales of the hi rows: wavefront w < 2 fills tile rows 64 w + lane
+        A.as_off = a_src(2 * (64 * (wave & 1) + lane)) * static_cast<uint32_t>(ass);
         // B: instruction i fills weight rows 32 w + 16 i + lane / 4 (clamped to the matrix)
         A.wblk = wblocks + static_cast<int64_t>(A.e) * Nrows * kbytes;
 #pragma unroll
         for (int i = 0; i < 2; ++i) A.b_off[i] = min(A.n0 + 32 * wave + 16 * i + (lane >> 2), Nrows - 1) * kbytes;
-        // B scales, read as aligned dwords: the pair at (p & ~3) holds the stage's bytes
-        // p .. p + 3; a second dword past the tensor's end holds no valid byte and reads the
-        // last dword instead. Wavefront w fills rows 32 w + lane / 2, dword lane % 2.
+        // weight scales, read as aligned dwords: for group j the four dwords from
+        // ((n K/32 + 12 j) & ~3) hold the group's bytes; instruction i of wavefront w fills
+        // rows 32 w + 16 i + lane / 4, dword lane % 4
         A.wsc = wscales + static_cast<int64_t>(A.e) * Nrows * nkb;
         const int64_t sc_len = static_cast<int64_t>(E - A.e) * Nrows * nkb;   // to the tensor's end
         A.last4 = static_cast<uint32_t>(min<int64_t>(sc_len, 0x7fffffff) - 4);
-        A.bs_off[0] = (min(A.n0 + 32 * wave + (lane >> 1), Nrows - 1) * nkb & ~3) + 4 * (lane & 1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            A.bs_off[i] = (min(A.n0 + 32 * wave + 16 * i + (lane >> 2), Nrows - 1) * nkb & ~3) + 4 * (lane & 3);
         return A;
     };
 
@@ -227,11 +239,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             if (part < 2) {
 #pragma unroll
                 for (int i = 2 * part; i < 2 * part + 2; ++i) dma16(a_k, S.a_off[i] + ach, lbuf + (4 * wave + i) * 1024);
-                if (part == 0 && wave < 4) dma4(a_sc + 4 * kt, S.as_off, lbuf + kOffAS + 256 * wave);
+                if (part == 0 && wave < 2) dma4(a_sc + 4 * kt, S.as_off, lbuf + kOffAS + 256 * wave);
             } else if (part == 2) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i) dma16(b_k, S.b_off[i] + bch, lbuf + kOffB + (2 * wave + i) * 1024);
-                dma4(S.wsc, min(S.bs_off[0] + 4 * kt, S.last4), lbuf + kOffBS + wave * 256);
+                if (kt % kGS == 0) {
+                    const int j = kt / kGS;
+                    const uint32_t gbuf = lds0 + kOffBSG + (j & 1) * kBSG + 512 * wave;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) dma4(S.wsc, min(S.bs_off[i] + 12 * j, S.last4), gbuf + 256 * i);
+                }
             }
         };
         auto issue_part = [&](int part, int buf, int kt) { issue_part_of(A, part, buf, kt); };
@@ -266,13 +283,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         //
         // Operand reads: B fragments and scales of the wavefront's eight column tiles, then
         // the A fragments of its row tiles. LDS addresses are one per-lane base per operand
-        // plus constants. The scales are read as single bytes: A row R's block g, and weight
-        // row n's block g at byte (n K/32) % 4 + g of its 8-byte window (the same for all
-        // eight column tiles: they are 16 rows apart).
+        // plus constants. The scales are read as single bytes: the hi row of A row R's block
+        // g (minus 4 for a lo row), and weight row n's block g of group stage s at byte
+        // (n K/32) % 4 + 4 s + g of its 16-byte window (the same offset for all eight column
+        // tiles: they are 16 rows apart).
         const uint32_t lb_b = kOffB + 8192 * wn + 64 * m + 16 * (g ^ ((m >> 1) & 3));
-        const uint32_t lb_bs = kOffBS + 1024 * wn + 8 * m + (((n0 + 128 * wn + m) * nkb) & 3) + g;
+        const uint32_t lb_bs = kOffBSG + 16 * (128 * wn + m) + (((n0 + 128 * wn + m) * nkb) & 3) + g;
         const uint32_t lb_a = 2048 * wm + 128 * m + 16 * (g ^ (m & 7));
-        const uint32_t lb_as = kOffAS + 64 * wm + 4 * m + g;
+        const uint32_t lb_as = kOffAS + 32 * wm + 4 * (m >> 1) + g;
+        const uint32_t lo_row = 4u * (m & 1);
         // the wavefront's row tiles are the tile's 16-row tiles 4 mt + wm (interleaved, so
         // that a partly filled tile splits its rows evenly); only the first NL are multiplied
         uint4 bq[8], alo[4], ahi[4];
@@ -285,18 +304,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         auto read_stage = [&](int kt) {
             const int buf = kt % 3;
             const uint8_t *base = g_stages + buf * kStage;
+            const uint8_t *gsc = g_stages + ((kt / kGS) & 1) * kBSG + 4 * (kt % kGS);
             const int vb = nkb - 4 * kt;
             uint32_t sb[8], sa[4];
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
                 bq[nt] = *reinterpret_cast<const uint4 *>(base + lb_b + 1024 * nt);
-                sb[nt] = base[lb_bs + 128 * nt];
+                sb[nt] = gsc[lb_bs + 256 * nt];
             }
 #pragma unroll
             for (int mt = 0; mt < NL; ++mt) {
                 alo[mt] = *reinterpret_cast<const uint4 *>(base + lb_a + 8192 * mt);
                 ahi[mt] = *reinterpret_cast<const uint4 *>(base + (lb_a ^ 64u) + 8192 * mt);   // chunk g + 4
-                sa[mt] = base[lb_as + 256 * mt];
+                sa[mt] = base[lb_as + 128 * mt] - lo_row;
             }
 #pragma unroll
             for (int mt = NL; mt < 4; ++mt) sa[mt] = 127u;
@@ -330,7 +350,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         // every wavefront's loads of stage s have landed (stage s + 1's, if any, stay in flight)
         auto wait_stage = [&](int s) {
             if (s + 1 < kt_total) {
-                if (wave < 4) wait_vm<kOpsLo>(); else wait_vm<kOpsHi>();
+                // this wavefront's loads of stage s + 1
+                const int n = 6 + (wave < 2 ? 1 : 0) + ((s + 1) % kGS == 0 ? 2 : 0);
+                if (n == 6) wait_vm<6>();
+                else if (n == 7) wait_vm<7>();
+                else if (n == 8) wait_vm<8>();
+                else wait_vm<9>();
             } else {
                 wait_vm<0>();
             }
