@@ -46,15 +46,17 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 LLC_BYTES = 256 << 20            # MI355X Infinity Cache
 KERNEL_SOURCES = {               # kernel -> files whose text defines it
-    "route": ["route.hip", "device_common.h", "rms.h"],
+    "route": ["route.hip", "device_common.h", "rms.h", "mx_mfma.h", "topk.h", "lds_dma.h"],
     "permute": ["permute.hip", "device_common.h"],
-    "logits": ["route.hip", "device_common.h", "rms.h"],
-    "up_decode": ["gemm_decode.hip", "device_common.h", "weight_tiles.h", "routing.h", "topk.h"],
-    "down_decode": ["gemm_decode.hip", "device_common.h", "weight_tiles.h", "routing.h"],
-    "up_stream": ["gemm_stream.hip", "device_common.h", "weight_tiles.h", "routing.h", "lds_dma.h"],
-    "down_stream": ["gemm_stream.hip", "device_common.h", "weight_tiles.h", "routing.h", "lds_dma.h"],
-    "up_grouped": ["gemm_grouped.hip", "device_common.h", "lds_dma.h"],
-    "down_grouped": ["gemm_grouped.hip", "device_common.h", "lds_dma.h"],
+    "logits": ["route.hip", "device_common.h", "rms.h", "mx_mfma.h", "topk.h", "lds_dma.h"],
+    "up_decode": ["gemm_decode.hip", "device_common.h", "weight_tiles.h", "routing.h", "topk.h", "mx_mfma.h",
+                  "lds_dma.h"],
+    "down_decode": ["gemm_decode.hip", "device_common.h", "weight_tiles.h", "routing.h", "topk.h", "mx_mfma.h",
+                    "lds_dma.h"],
+    "up_stream": ["gemm_stream.hip", "device_common.h", "weight_tiles.h", "routing.h", "lds_dma.h", "mx_mfma.h"],
+    "down_stream": ["gemm_stream.hip", "device_common.h", "weight_tiles.h", "routing.h", "lds_dma.h", "mx_mfma.h"],
+    "up_grouped": ["gemm_grouped.hip", "device_common.h", "lds_dma.h", "mx_mfma.h"],
+    "down_grouped": ["gemm_grouped.hip", "device_common.h", "lds_dma.h", "mx_mfma.h"],
     "combine": ["gemm_grouped.hip", "device_common.h", "lds_dma.h"],
     "combine_decode": ["gemm_decode.hip", "device_common.h"],
     "rmsnorm": ["norm.hip", "device_common.h", "rms.h"],

@@ -97,7 +97,8 @@ __device__ __forceinline__ void mx8_split_block(const float (&x)[32], uint32_t (
 
 // E4M3 activation matrices ("mx8"): for R activation rows of K elements, 2R byte rows of K
 // (row 2r = hi, row 2r + 1 = lo of activation row r), followed by 2R scale rows of
-// mx8_scale_stride(K) bytes (K / 32 E8M0 bytes, padded to a multiple of 16).
+// mx8_scale_stride(K) bytes (K / 32 E8M0 bytes, padded to a multiple of 16). A lo row's
+// scale is always its hi row's minus 4 (every writer below); readers may rely on it.
 __host__ __device__ inline int mx8_scale_stride(int K) { return ((K / 32) + 15) & ~15; }
 __host__ __device__ inline size_t mx8_bytes(int64_t rows, int K) {
     return static_cast<size_t>(2 * rows) * (static_cast<size_t>(K) + static_cast<size_t>(mx8_scale_stride(K)));
