@@ -68,7 +68,7 @@ moe::Dims dims_of(const moe_mxfp4_shape_t *s) {
 
 // Workspace regions (each 256-byte aligned), in order.
 struct Layout {
-    size_t idx, w, logits, offsets, sorted_token, sorted_w, slot_row, o, part, x8, h8, xn, hist, total;
+    size_t idx, w, logits, offsets, sorted_token, sorted_w, slot_row, o, part, x8, h8, xn, hist, rpart, total;
 };
 
 size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -100,6 +100,8 @@ Layout layout_of(const moe_mxfp4_shape_t *s) {
         L.x8 = p;           p += round_up(moe::mx8_bytes(s->T, s->H));
         L.h8 = p;           p += round_up(moe::mx8_bytes(static_cast<int64_t>(N), s->I));
         L.o = p;            p += round_up(N * static_cast<size_t>(s->H) * 4);
+        // the router's partial logits over slices of H (few token groups, many experts)
+        L.rpart = p;        p += round_up(static_cast<size_t>(moe::route_part_doubles(dims_of(s))) * 8);
         L.part = 0;
     }
     L.total = p;
@@ -279,7 +281,8 @@ moe_status_t run_forward(const moe_mxfp4_shape_t *shape, const moe_bf16_t *x,
         return ok();
     }
     uint8_t *x8 = ws + L.x8, *h8 = ws + L.h8;
-    STEP(moe::launch_route(d, x, nullptr, 0.0, router_w, router_b, idx, w, nullptr, x8, s), "route");
+    STEP(moe::launch_route(d, x, nullptr, 0.0, router_w, router_b, idx, w, nullptr, x8, s,
+                           reinterpret_cast<double *>(ws + L.rpart)), "route");
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
     int32_t *sorted_token = reinterpret_cast<int32_t *>(ws + L.sorted_token);
     float *sorted_w = reinterpret_cast<float *>(ws + L.sorted_w);

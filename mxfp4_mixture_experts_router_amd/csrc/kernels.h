@@ -53,9 +53,16 @@ inline bool route_normalizes(const Dims &d) { return d.T <= kDecodeMaxT && d.H <
 
 // Router, top-k and softmax; with x8 != nullptr (T <= kDecodeMaxT) also writes x as an mx8
 // matrix. With gamma != nullptr (only where route_normalizes) both take the RMSNorm of x.
+// Above kDecodeMaxT tokens, when there are fewer 16-token groups than kRouteSplitCUs and
+// E >= 64, the router sums slices of H in route_split(d) blocks per group into `part`
+// (route_part_doubles(d) doubles of workspace), then a second kernel adds the slices, the bias
+// and selects; otherwise (and then `part` may be null) one kernel does everything.
+constexpr int kRouteSplitCUs = 256;
+int route_split(const Dims &d);
+int64_t route_part_doubles(const Dims &d);
 hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *gamma, double eps,
                         const uint16_t *router_w, const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
-                        float *logits, uint8_t *x8, hipStream_t s);
+                        float *logits, uint8_t *x8, hipStream_t s, double *part = nullptr);
 
 // hist (optional): workspace of permute_hist_ints(T k, E) ints; with it (and that count
 // nonzero) the permutation runs on many workgroups (a histogram pass, then a scatter pass),

@@ -259,12 +259,17 @@ __device__ __forceinline__ void mx8_store_quarter(const uint4 &u, uint8_t *q8, i
     }
 }
 
-template <int NT>
+// With SPLIT, block (g, s) = (blockIdx.x / S, blockIdx.x % S) of a grid of S blocks per
+// 16-token group sums only the chunks of slice s of H (slices of ceil(nch / S) chunks) and
+// writes those partial logits, without bias, to part[s][t][e]; k_route_topk then adds the S
+// slices in order, adds the bias and selects. For few token groups (fewer than the CUs), so
+// that the fp64 MFMA work of the whole chip is used.
+template <int NT, bool SPLIT>
 __global__ __launch_bounds__(kRouteThreads) void k_route(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     const uint16_t *__restrict__ br, int64_t T, int H, int E, int k,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ logits_out,
-    uint8_t *__restrict__ x8) {
+    uint8_t *__restrict__ x8, double *__restrict__ part, int S) {
     constexpr int NW = kRouteThreads / kWave;
     constexpr int kAhead = NT >= 16 ? 1 : (NT >= 8 ? 2 : 3);   // chunks loaded together (registers)
     constexpr int LS = 16 * NT + 1;   // LDS row of one token's logits (padded)
@@ -273,20 +278,25 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int m = lane & 15, g = lane >> 4;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRT;
+    const int grp = SPLIT ? static_cast<int>(blockIdx.x) / S : static_cast<int>(blockIdx.x);
+    const int slice = SPLIT ? static_cast<int>(blockIdx.x) % S : 0;
+    const int64_t t0 = static_cast<int64_t>(grp) * kRT;
     const int64_t tm = t0 + m;
     const uint16_t *xrow = x + min(tm, T - 1) * H;      // past T: a duplicate row
     const uint16_t *wrow[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) wrow[nt] = wr + static_cast<int64_t>(min(16 * nt + m, E - 1)) * H;
     const bool quant = x8 != nullptr && tm < T;
-    const int nch = H / 32;
+    const int nch_all = H / 32;
+    const int per = SPLIT ? (nch_all + S - 1) / S : nch_all;
+    const int c_lo = slice * per;                       // this block's chunks [c_lo, nch)
+    const int nch = min(nch_all, c_lo + per);
 
     f64x4 acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] = f64x4{0.0, 0.0, 0.0, 0.0};
     // chunks c = wave + NW i, loaded kAhead at a time so that their latencies overlap
-    for (int c0 = wave; c0 < nch; c0 += kAhead * NW) {
+    for (int c0 = c_lo + wave; c0 < nch; c0 += kAhead * NW) {
         uint4 xv[kAhead], wv[kAhead][NT];
 #pragma unroll
         for (int a = 0; a < kAhead; ++a) {
@@ -327,6 +337,13 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
         }
         __syncthreads();
     }
+    if (SPLIT) {
+        for (int i = threadIdx.x; i < kRT * E; i += kRouteThreads) {
+            const int j = i / E, e = i % E;
+            if (t0 + j < T) part[(static_cast<int64_t>(slice) * T + t0 + j) * E + e] = lg[j * LS + e];
+        }
+        return;
+    }
     for (int i = threadIdx.x; i < kRT * E; i += kRouteThreads) {
         const int j = i / E, e = i % E;
         lg[j * LS + e] += static_cast<double>(bf16_to_f32(br[e]));
@@ -338,6 +355,32 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
             topk_softmax_wave(&lg[j * LS], E, k, lane, topk_idx + t * k, topk_w + t * k, nullptr, nullptr,
                               logits_out ? logits_out + t * E : nullptr, s_tk[wave]);
     }
+}
+
+// Logits from S slices of partial sums (added in slice order) plus the bias, then the top-k
+// and softmax of the token: one wavefront per token.
+__global__ __launch_bounds__(512) void k_route_topk(const double *__restrict__ part, int S,
+                                                    const uint16_t *__restrict__ br, int64_t T, int E, int k,
+                                                    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+                                                    float *__restrict__ logits_out) {
+    __shared__ __attribute__((aligned(16))) uint64_t s_tk[8][kTopkScratch];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 8 + wave;
+    if (t >= T) return;
+    double v[kTopkC];
+#pragma unroll
+    for (int c = 0; c < kTopkC; ++c) {
+        const int e = lane + kWave * c;
+        double l = 0.0;
+        if (e < E) {
+            l = part[t * E + e];
+            for (int q = 1; q < S; ++q) l += part[(static_cast<int64_t>(q) * T + t) * E + e];
+            l += static_cast<double>(bf16_to_f32(br[e]));
+            if (logits_out) logits_out[t * E + e] = static_cast<float>(l);
+        }
+        v[c] = l;
+    }
+    topk_softmax_values(v, E, k, lane, topk_idx + t * k, topk_w + t * k, nullptr, nullptr, s_tk[wave]);
 }
 
 template <int NI>
@@ -364,9 +407,21 @@ hipError_t launch_logits(const Dims &d, const uint16_t *x, const uint16_t *gamma
     return hipGetLastError();
 }
 
+int route_split(const Dims &d) {
+    if (d.T <= kDecodeMaxT) return 1;
+    const int64_t groups = (d.T + kRT - 1) / kRT;
+    if (d.E < 64 || groups >= kRouteSplitCUs) return 1;       // enough 16-token groups (or little work per group)
+    return groups * 2 >= kRouteSplitCUs ? 2 : 4;
+}
+
+int64_t route_part_doubles(const Dims &d) {
+    const int S = route_split(d);
+    return S > 1 ? static_cast<int64_t>(S) * d.T * d.E : 0;
+}
+
 hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *gamma, double eps,
                         const uint16_t *router_w, const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
-                        float *logits, uint8_t *x8, hipStream_t s) {
+                        float *logits, uint8_t *x8, hipStream_t s, double *part) {
     if (d.T <= 0) return hipSuccess;
     const int ni = (d.H + 511) / 512;
     if (gamma != nullptr && !route_normalizes(d)) return hipErrorInvalidValue;
@@ -381,15 +436,34 @@ hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *gamma,
             default: launch_token<7>(d, x, gamma, eps, router_w, router_b, topk_idx, topk_w, logits, x8, s); break;
         }
     } else {
-        const dim3 grid(static_cast<unsigned>((d.T + kRT - 1) / kRT));
-#define MOE_ROUTE(NT) MOE_LAUNCH((k_route<NT>), grid, dim3(kRouteThreads), 0, s, x, router_w, router_b, d.T, \
-                                         d.H, d.E, d.k, topk_idx, topk_w, logits, x8)
+        const int64_t groups = (d.T + kRT - 1) / kRT;
+        const int S = part != nullptr ? route_split(d) : 1;
+        const dim3 grid(static_cast<unsigned>(groups * S));
+        // with S > 1: one stage, two launches (the partial-logit kernel records the stage's start
+        // event, the top-k kernel its stop event)
+        const LaunchEvents ev = launch_events();
+        if (S > 1) launch_events() = LaunchEvents{ev.start, nullptr};
+#define MOE_ROUTE(NT) do { if (S > 1) MOE_LAUNCH((k_route<NT, true>), grid, dim3(kRouteThreads), 0, s, x, router_w, \
+                                         router_b, d.T, d.H, d.E, d.k, topk_idx, topk_w, logits, x8, part, S); \
+                           else MOE_LAUNCH((k_route<NT, false>), grid, dim3(kRouteThreads), 0, s, x, router_w, \
+                                         router_b, d.T, d.H, d.E, d.k, topk_idx, topk_w, logits, x8, part, 1); } while (0)
         if (d.E <= 16) MOE_ROUTE(1);
         else if (d.E <= 32) MOE_ROUTE(2);
         else if (d.E <= 64) MOE_ROUTE(4);
         else if (d.E <= 128) MOE_ROUTE(8);
         else MOE_ROUTE(16);
 #undef MOE_ROUTE
+        if (S > 1) {
+            const hipError_t e1 = hipGetLastError();
+            if (e1 != hipSuccess) {
+                launch_events() = ev;
+                return e1;
+            }
+            launch_events() = LaunchEvents{nullptr, ev.stop};
+            MOE_LAUNCH(k_route_topk, dim3(static_cast<unsigned>((d.T + 7) / 8)), dim3(512), 0, s, part, S, router_b,
+                       d.T, d.E, d.k, topk_idx, topk_w, logits);
+            launch_events() = ev;
+        }
     }
     return hipGetLastError();
 }

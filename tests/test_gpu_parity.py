@@ -261,6 +261,11 @@ FORWARD_CASES = [
     ("tiny", 17, 4128, 64, 4, 2, 17),
     ("tiny", 3, 64, 4128, 4, 2, 3),         # I > 4096 at few tokens: the grouped sequence
     ("tiny", 17, 64, 4128, 4, 2, 17),
+    # the router over slices of H (few 16-token groups, E >= 64): 4 slices (the last one empty
+    # at H = 96), 2 slices
+    ("tiny", 300, 256, 64, 64, 4, 300),
+    ("tiny", 1100, 96, 64, 128, 4, 1100),
+    ("tiny", 2100, 128, 64, 64, 2, 2100),
     ("tiny", 1, 3104, 64, 4, 2, 1),         # T = 1 at widths past 3072
     ("tiny", 1, 64, 3072, 4, 4, 1),
     ("tiny", 1, 64, 3104, 2, 2, 1),
@@ -357,14 +362,16 @@ class _HipEvents:
             self.lib.hipEventDestroy(self.c.c_void_p(ev))
 
 
-@pytest.mark.parametrize("T,launches,prenorm,H,I", [
-    (1, 3, False, 64, 64), (3, 3, False, 64, 64), (4, 4, False, 64, 64), (17, 4, False, 64, 64),
-    (65, 5, False, 64, 64), (1, 3, True, 64, 64), (17, 4, True, 64, 64), (65, 6, True, 64, 64),
+@pytest.mark.parametrize("T,launches,prenorm,H,I,E", [
+    (1, 3, False, 64, 64, 4), (3, 3, False, 64, 64, 4), (4, 4, False, 64, 64, 4), (17, 4, False, 64, 64, 4),
+    (65, 5, False, 64, 64, 4), (1, 3, True, 64, 64, 4), (17, 4, True, 64, 64, 4), (65, 6, True, 64, 64, 4),
     # H or I above 4096: the grouped sequence at any token count
-    (3, 5, False, 4128, 64), (17, 5, False, 64, 4128), (3, 6, True, 4128, 64), (17, 6, True, 64, 4128)])
-def test_forward_timed_matches_forward(T, launches, prenorm, H, I):
+    (3, 5, False, 4128, 64, 4), (17, 5, False, 64, 4128, 4), (3, 6, True, 4128, 64, 4), (17, 6, True, 64, 4128, 4),
+    # the router in two kernels (slices of H, then the top-k): still one stage
+    (300, 5, False, 128, 64, 64), (300, 6, True, 128, 64, 64)])
+def test_forward_timed_matches_forward(T, launches, prenorm, H, I, E):
     import ctypes
-    cfg = CONFIGS["tiny"].with_(H=H, I=I)
+    cfg = CONFIGS["tiny"].with_(H=H, I=I, E=E)
     inp = upload(make_inputs(cfg, seed=5, T=T))
     norm = dict(norm_weight=inp["norm_w"], norm_eps=1e-5) if prenorm else {}
     y_ref = _forward(inp, cfg.k, cfg, **norm)
