@@ -68,26 +68,53 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
-constexpr int kBM = 128;                       // activation rows per tile
-constexpr int kAR = 2 * kBM;                   // A rows per tile (hi, lo)
 constexpr int kBN = 256;                       // output columns (weight rows) per tile
 constexpr int kBK = 128;                       // contraction per stage
 constexpr int kThreads = 512;                  // 8 wavefronts: 4 row groups x 2 column halves
 constexpr int kChunk = 32;                     // items per XCD chunk (= blocks per XCD)
-constexpr int kOffB = kAR * kBK;               // 32768
-constexpr int kOffAS = kOffB + kBN * kBK / 2;  // 49152
-constexpr int kStage = kOffAS + kBM * 4;       // 49664
-constexpr int kGS = 3;                         // stages per weight-scale group
-constexpr int kOffBSG = 3 * kStage;            // 148992
-constexpr int kBSG = kBN * 16;                 // bytes per weight-scale group buffer
-// global_load_lds per wavefront per stage: 4 A, 2 B, 1 A-scale for wavefronts 0-1, and 2
-// weight-scale dwords per group (with the group's first stage)
 constexpr int kHS = 67;                        // up epilogue: padded row of 64 fp32 pairs
 constexpr int kOS = 132;                       // down epilogue: padded row of 128 fp32 outputs
 
-__shared__ __attribute__((aligned(16))) uint8_t g_stages[3 * kStage + 2 * kBSG];
+// The two tile configurations (LDS byte offsets).
+//   Full tiles (SMALL = false): 128 activation rows; each stage buffer holds the stage's A
+//   rows, its 256 weight rows' 64 bytes (half of a 128-byte line) and the hi rows' A scales;
+//   weight scales in 16-byte windows per three stages (group ring of two).
+//   Small groups (SMALL = true, experts of at most about 96 rows): 96 activation rows; the
+//   stage buffers hold A and its scales only; the weights come as whole 128-byte lines that
+//   serve two stages, into a ring of two such pair slots per column half (each half is read
+//   only by the wavefronts of its column half, which also load it), with their scale windows
+//   per pair.
+// Global-to-LDS instructions per wavefront: full: 4 A, 2 B per stage, 1 A-scale (wavefronts
+// 0-1), 2 weight-scale dwords every third stage; small: 3 A per stage, 1 A-scale (wavefronts
+// 0-1), and with every even stage 4 B and 2 weight-scale dwords.
+template <bool SMALL> struct GemmCfg;
+template <> struct GemmCfg<false> {
+    static constexpr int BM = 128, NA = 4, NLMAX = 4;
+    static constexpr int OFF_B = 2 * BM * kBK;                 // 32768
+    static constexpr int OFF_AS = OFF_B + kBN * kBK / 2;       // 49152
+    static constexpr int STAGE = OFF_AS + 128 * 4;             // 49664
+    static constexpr int GS = 3;                               // stages per weight-scale group
+    static constexpr int OFF_BSG = 3 * STAGE;                  // 148992
+    static constexpr int BSG = kBN * 16;                       // one group buffer
+    static constexpr int TOTAL = OFF_BSG + 2 * BSG;            // 157184
+};
+template <> struct GemmCfg<true> {
+    static constexpr int BM = 96, NA = 3, NLMAX = 3;
+    static constexpr int OFF_AS = 2 * BM * kBK;                // 24576
+    static constexpr int STAGE = OFF_AS + 128 * 4;             // 25088
+    static constexpr int OFF_BP = 3 * STAGE;                   // 75264: pair slots [half][2]
+    static constexpr int BP = 128 * 128;                       // one slot: 128 rows x 128 bytes
+    static constexpr int OFF_BSG = OFF_BP + 4 * BP;            // 140800: scale slots [half][2]
+    static constexpr int BSG = 128 * 16;
+    static constexpr int TOTAL = OFF_BSG + 4 * BSG;            // 148992
+    static constexpr int OFF_B = 0, GS = 2;                    // (weights and their scales per pair)
+};
 
-template <bool UP>
+__shared__ __attribute__((aligned(16))) uint8_t g_stages[GemmCfg<false>::TOTAL];
+static_assert(GemmCfg<true>::TOTAL <= GemmCfg<false>::TOTAL, "one LDS array serves both configurations");
+static_assert(8 * 32 * kOS * 4 <= GemmCfg<true>::TOTAL, "the epilogue's staging fits both configurations");
+
+template <bool UP, bool SMALL>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
     const uint8_t *__restrict__ a8, int64_t a_rows,  // mx8 activations: up x8 (T rows), down h8 (T k rows)
     const int32_t *__restrict__ sorted_token,        // up only
@@ -100,7 +127,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
     __shared__ int s_off[kMaxE + 1];
     __shared__ int s_icum[kMaxE + 1];               // item prefix over experts
     __shared__ uint16_t s_bias[kBN];                // the tile's biases (bf16)
-    __shared__ float s_rw[kBM];                     // down: the tile rows' routing weights
+    using C = GemmCfg<SMALL>;
+    constexpr int kBM = C::BM;
+    __shared__ float s_rw[128];                     // down: the tile rows' routing weights
 
     const int ntn = (Nrows + kBN - 1) / kBN;
     const int tid0 = threadIdx.x;
@@ -149,7 +178,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
     // (the host keeps every operand below 4 GiB).
     struct Addr {
         int e, row0, rows, n0;
-        uint32_t a_off[4], as_off, b_off[2], bs_off[2], last4;
+        uint32_t a_off[C::NA], as_off, b_off[SMALL ? 4 : 2], bs_off[2], last4;
         const uint8_t *wblk, *wsc;
     };
     // the tile rows' token indices: tok (LDS, the tile's rows in order) or, with nullptr, the
@@ -177,30 +206,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             const int src = UP ? (tok ? tok[ar] : sorted_token[A.row0 + ar]) : A.row0 + ar;
             return static_cast<uint32_t>(2 * src + (R & 1));
         };
-        // A: instruction i of wavefront w fills A rows 32 w + 8 i + lane / 8
+        // A: instruction i of wavefront w fills A rows 8 (NA w + i) + lane / 8
 #pragma unroll
-        for (int i = 0; i < 4; ++i) A.a_off[i] = a_src(32 * wave + 8 * i + (lane >> 3)) * static_cast<uint32_t>(K);
+        for (int i = 0; i < C::NA; ++i)
+            A.a_off[i] = a_src(8 * (C::NA * wave + i) + (lane >> 3)) * static_cast<uint32_t>(K);
         // A scales of the hi rows: wavefront w < 2 fills tile rows 64 w + lane
         A.as_off = a_src(2 * (64 * (wave & 1) + lane)) * static_cast<uint32_t>(ass);
-        // B: instruction i fills weight rows 32 w + 16 i + lane / 4 (clamped to the matrix)
         A.wblk = wblocks + static_cast<int64_t>(A.e) * Nrows * kbytes;
+        if constexpr (SMALL) {
+            // B pairs: instruction i of wavefront w fills rows 32 (w % 4) + 8 i + lane / 8 of
+            // column half w / 4 (clamped to the matrix), a whole 128-byte line each
 #pragma unroll
-        for (int i = 0; i < 2; ++i) A.b_off[i] = min(A.n0 + 32 * wave + 16 * i + (lane >> 2), Nrows - 1) * kbytes;
+            for (int i = 0; i < 4; ++i)
+                A.b_off[i] = min(A.n0 + 128 * (wave >> 2) + 32 * (wave & 3) + 8 * i + (lane >> 3), Nrows - 1) * kbytes;
+        } else {
+            // B: instruction i fills weight rows 32 w + 16 i + lane / 4 (clamped to the matrix)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) A.b_off[i] = min(A.n0 + 32 * wave + 16 * i + (lane >> 2), Nrows - 1) * kbytes;
+        }
         // weight scales, read as aligned dwords: for group j the four dwords from
         // ((n K/32 + 12 j) & ~3) hold the group's bytes; instruction i of wavefront w fills
         // rows 32 w + 16 i + lane / 4, dword lane % 4
         A.wsc = wscales + static_cast<int64_t>(A.e) * Nrows * nkb;
         const int64_t sc_len = static_cast<int64_t>(E - A.e) * Nrows * nkb;   // to the tensor's end
         A.last4 = static_cast<uint32_t>(min<int64_t>(sc_len, 0x7fffffff) - 4);
+        // (small groups: rows 32 (w % 4) + 16 i + lane / 4 of column half w / 4, per pair)
+        const int bs_row0 = SMALL ? 128 * (wave >> 2) + 32 * (wave & 3) : 32 * wave;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            A.bs_off[i] = (min(A.n0 + 32 * wave + 16 * i + (lane >> 2), Nrows - 1) * nkb & ~3) + 4 * (lane & 3);
+            A.bs_off[i] = (min(A.n0 + bs_row0 + 16 * i + (lane >> 2), Nrows - 1) * nkb & ~3) + 4 * (lane & 3);
         return A;
     };
 
     // up: the next tile's token indices, loaded into LDS while the current tile runs, so that
     // its stage addresses need no dependent global load when it starts
-    __shared__ int s_ntok[2][kBM];
+    __shared__ int s_ntok[2][128];
     int ntile = 0;  // tiles this workgroup has started
     for (int c = xcd; c * kChunk < items; c += 8, ++ntile) {
         const int item = c * kChunk + lb;
@@ -228,34 +268,45 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         const uint32_t b_ch = 16 * b_c, b_ch_last = b_c < b_vb ? 16 * b_c : 0;
 
         const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)g_stages;
-        // the wavefront's share of stage kt's loads into buffer buf, in three parts (A rows of
-        // instructions 0-1, 2-3 with the A scales, B rows with the B scales)
-        auto issue_part_of = [&](const Addr &S, int part, int buf, int kt) {
-            const uint32_t lbuf = lds0 + buf * kStage;
+        // a B pair's 16-byte chunk past the row (last pair only) loads the pair's chunk 0
+        const int kbp = (kbytes - 128 * (kt_total / 2 + (kt_total & 1) - 1)) / 16;   // valid chunks of the last pair
+        const uint32_t bp_ch = 16 * a_c, bp_ch_last = a_c < kbp ? 16 * a_c : 0;
+        // the wavefront's share of stage kt's loads into buffer buf (A rows and the hi rows'
+        // scales; the weight rows and their scales as the configuration takes them)
+        auto issue_of = [&](const Addr &S, int buf, int kt) {
+            const uint32_t lbuf = lds0 + buf * C::STAGE;
             const uint32_t ach = kt == kt_last ? a_ch_last : a_ch;
-            const uint32_t bch = kt == kt_last ? b_ch_last : b_ch;
             const uint8_t *a_k = a8 + kBK * kt;          // uniform bases
-            const uint8_t *b_k = S.wblk + 64 * kt;
-            if (part < 2) {
 #pragma unroll
-                for (int i = 2 * part; i < 2 * part + 2; ++i) dma16(a_k, S.a_off[i] + ach, lbuf + (4 * wave + i) * 1024);
-                if (part == 0 && wave < 2) dma4(a_sc + 4 * kt, S.as_off, lbuf + kOffAS + 256 * wave);
-            } else if (part == 2) {
+            for (int i = 0; i < C::NA; ++i) dma16(a_k, S.a_off[i] + ach, lbuf + (C::NA * wave + i) * 1024);
+            if (wave < 2) dma4(a_sc + 4 * kt, S.as_off, lbuf + C::OFF_AS + 256 * wave);
+            if constexpr (SMALL) {
+                if ((kt & 1) == 0) {
+                    const int q = kt >> 1;                  // pair q: stages 2q, 2q + 1
+                    const bool last = 2 * q + 2 >= kt_total;
+                    const uint32_t slot = static_cast<uint32_t>(2 * (wave >> 2) + (q & 1));
+                    const uint32_t pb = lds0 + C::OFF_BP + slot * C::BP + 4096 * (wave & 3);
+                    const uint8_t *b_k = S.wblk + 128 * q;
 #pragma unroll
-                for (int i = 0; i < 2; ++i) dma16(b_k, S.b_off[i] + bch, lbuf + kOffB + (2 * wave + i) * 1024);
-                if (kt % kGS == 0) {
-                    const int j = kt / kGS;
-                    const uint32_t gbuf = lds0 + kOffBSG + (j & 1) * kBSG + 512 * wave;
+                    for (int i = 0; i < 4; ++i) dma16(b_k, S.b_off[i] + (last ? bp_ch_last : bp_ch), pb + 1024 * i);
+                    const uint32_t gb = lds0 + C::OFF_BSG + slot * C::BSG + 512 * (wave & 3);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) dma4(S.wsc, min(S.bs_off[i] + 8 * q, S.last4), gb + 256 * i);
+                }
+            } else {
+                const uint32_t bch = kt == kt_last ? b_ch_last : b_ch;
+                const uint8_t *b_k = S.wblk + 64 * kt;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) dma16(b_k, S.b_off[i] + bch, lbuf + C::OFF_B + (2 * wave + i) * 1024);
+                if (kt % C::GS == 0) {
+                    const int j = kt / C::GS;
+                    const uint32_t gbuf = lds0 + C::OFF_BSG + (j & 1) * C::BSG + 512 * wave;
 #pragma unroll
                     for (int i = 0; i < 2; ++i) dma4(S.wsc, min(S.bs_off[i] + 12 * j, S.last4), gbuf + 256 * i);
                 }
             }
         };
-        auto issue_part = [&](int part, int buf, int kt) { issue_part_of(A, part, buf, kt); };
-        auto issue = [&](int buf, int kt) {
-#pragma unroll
-            for (int part = 0; part < 3; ++part) issue_part(part, buf, kt);
-        };
+        auto issue = [&](int buf, int kt) { issue_of(A, buf, kt); };
 
         // The tile body, for NL = the wavefront's row tiles that hold valid rows (0 to 4; a
         // compile-time constant, so that skipped tiles cost no branches and the accumulators
@@ -286,11 +337,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         // plus constants. The scales are read as single bytes: the hi row of A row R's block
         // g (minus 4 for a lo row), and weight row n's block g of group stage s at byte
         // (n K/32) % 4 + 4 s + g of its 16-byte window (the same offset for all eight column
-        // tiles: they are 16 rows apart).
-        const uint32_t lb_b = kOffB + 8192 * wn + 64 * m + 16 * (g ^ ((m >> 1) & 3));
-        const uint32_t lb_bs = kOffBSG + 16 * (128 * wn + m) + (((n0 + 128 * wn + m) * nkb) & 3) + g;
+        // tiles: they are 16 rows apart). Small groups: the B fragment of stage s is chunk
+        // 4 (s % 2) + g of the pair's 128-byte row, stored at slot chunk ^ (row % 8).
+        const uint32_t lb_b = SMALL ? 128 * m + 16 * (g ^ (m & 7))
+                                    : C::OFF_B + 8192 * wn + 64 * m + 16 * (g ^ ((m >> 1) & 3));
+        const uint32_t lb_bs = C::OFF_BSG + 16 * ((SMALL ? 0 : 128 * wn) + m) + (((n0 + 128 * wn + m) * nkb) & 3) + g;
         const uint32_t lb_a = 2048 * wm + 128 * m + 16 * (g ^ (m & 7));
-        const uint32_t lb_as = kOffAS + 32 * wm + 4 * (m >> 1) + g;
+        const uint32_t lb_as = C::OFF_AS + 32 * wm + 4 * (m >> 1) + g;
         const uint32_t lo_row = 4u * (m & 1);
         // the wavefront's row tiles are the tile's 16-row tiles 4 mt + wm (interleaved, so
         // that a partly filled tile splits its rows evenly); only the first NL are multiplied
@@ -303,13 +356,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         // add exactly 0.
         auto read_stage = [&](int kt) {
             const int buf = kt % 3;
-            const uint8_t *base = g_stages + buf * kStage;
-            const uint8_t *gsc = g_stages + ((kt / kGS) & 1) * kBSG + 4 * (kt % kGS);
+            const uint8_t *base = g_stages + buf * C::STAGE;
+            const uint8_t *bsrc, *gsc;
+            uint32_t lbb = lb_b;
+            int bstride;
+            if constexpr (SMALL) {
+                const int slot = 2 * wn + ((kt >> 1) & 1);
+                bsrc = g_stages + C::OFF_BP + slot * C::BP;
+                lbb ^= (kt & 1) ? 64u : 0u;          // chunk g + 4 for the pair's second stage
+                bstride = 2048;                      // 16 rows of 128 bytes
+                gsc = g_stages + slot * C::BSG + 4 * (kt & 1);
+            } else {
+                bsrc = base;
+                bstride = 1024;
+                gsc = g_stages + ((kt / C::GS) & 1) * C::BSG + 4 * (kt % C::GS);
+            }
             const int vb = nkb - 4 * kt;
             uint32_t sb[8], sa[4];
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
-                bq[nt] = *reinterpret_cast<const uint4 *>(base + lb_b + 1024 * nt);
+                bq[nt] = *reinterpret_cast<const uint4 *>(bsrc + lbb + bstride * nt);
                 sb[nt] = gsc[lb_bs + 256 * nt];
             }
 #pragma unroll
@@ -351,11 +417,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         auto wait_stage = [&](int s) {
             if (s + 1 < kt_total) {
                 // this wavefront's loads of stage s + 1
-                const int n = 6 + (wave < 2 ? 1 : 0) + ((s + 1) % kGS == 0 ? 2 : 0);
-                if (n == 6) wait_vm<6>();
-                else if (n == 7) wait_vm<7>();
-                else if (n == 8) wait_vm<8>();
-                else wait_vm<9>();
+                const int n = SMALL ? 3 + (wave < 2 ? 1 : 0) + (((s + 1) & 1) == 0 ? 6 : 0)
+                                    : 6 + (wave < 2 ? 1 : 0) + ((s + 1) % C::GS == 0 ? 2 : 0);
+                switch (n) {
+                    case 3: wait_vm<3>(); break;
+                    case 4: wait_vm<4>(); break;
+                    case 6: wait_vm<6>(); break;
+                    case 7: wait_vm<7>(); break;
+                    case 8: wait_vm<8>(); break;
+                    case 9: wait_vm<9>(); break;
+                    default: wait_vm<10>(); break;
+                }
             } else {
                 wait_vm<0>();
             }
@@ -505,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         // when all its 128 columns lie past the matrix (the last column tile of a matrix whose
         // row count is not a multiple of 256), so that the SIMD's other wavefront runs alone
         const int nloc = n0 + 128 * wn >= Nrows ? 0 : ((rows + 7) / 8 - wm + 3) / 4;
-        if (nloc > 3) tile_body(IntC<4>{});
+        if (nloc > 3) { if constexpr (!SMALL) tile_body(IntC<4>{}); }
         else if (nloc > 2) tile_body(IntC<3>{});
         else if (nloc > 1) tile_body(IntC<2>{});
         else if (nloc > 0) tile_body(IntC<1>{});
@@ -595,26 +667,41 @@ unsigned grid_for(int64_t items) {
 // One block per CU (the LDS stages take most of a CU's LDS), a multiple of 8 (XCDs).
 int persistent_blocks() { return 256; }
 
+// The small-group tiles (96 rows, whole-line weight pairs) when the experts average at most
+// 96 routed rows: their 128-row tiles would be mostly empty and the weight stream bound.
+bool small_groups(const Dims &d) { return d.T * d.k <= static_cast<int64_t>(GemmCfg<true>::BM) * d.E; }
+
+template <bool UP, bool SMALL>
+hipError_t launch_gemm(const Dims &d, const uint8_t *a8, int64_t a_rows, const int32_t *sorted_token,
+                       const float *sorted_w, const uint8_t *wb, const uint8_t *ws, const uint16_t *wbias,
+                       const int32_t *offsets, int K, int Nrows, uint8_t *h8, int64_t h_rows, float *o, hipStream_t s) {
+    MOE_LAUNCH((k_gemm_mx<UP, SMALL>), dim3(persistent_blocks()), dim3(kThreads), 0, s, a8, a_rows, sorted_token,
+               sorted_w, wb, ws, wbias, offsets, d.E, K, Nrows, d.alpha, d.limit, h8, h_rows, o);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_up_grouped(const Dims &d, const uint8_t *x8, const uint8_t *gu_blocks,
                              const uint8_t *gu_scales, const uint16_t *gu_bias,
                              const int32_t *offsets, const int32_t *sorted_token,
                              uint8_t *h8, hipStream_t s) {
-    MOE_LAUNCH((k_gemm_mx<true>), dim3(persistent_blocks()), dim3(kThreads), 0, s, x8, d.T, sorted_token,
-                       nullptr, gu_blocks, gu_scales, gu_bias, offsets, d.E, d.H, 2 * d.I, d.alpha, d.limit,
-                       h8, d.T * d.k, nullptr);
-    return hipGetLastError();
+    if (small_groups(d))
+        return launch_gemm<true, true>(d, x8, d.T, sorted_token, nullptr, gu_blocks, gu_scales, gu_bias, offsets,
+                                       d.H, 2 * d.I, h8, d.T * d.k, nullptr, s);
+    return launch_gemm<true, false>(d, x8, d.T, sorted_token, nullptr, gu_blocks, gu_scales, gu_bias, offsets,
+                                    d.H, 2 * d.I, h8, d.T * d.k, nullptr, s);
 }
 
 hipError_t launch_down_grouped(const Dims &d, const uint8_t *h8, const uint8_t *dn_blocks,
                                const uint8_t *dn_scales, const uint16_t *dn_bias,
                                const int32_t *offsets, const float *sorted_w, float *o,
                                hipStream_t s) {
-    MOE_LAUNCH((k_gemm_mx<false>), dim3(persistent_blocks()), dim3(kThreads), 0, s, h8, d.T * d.k, nullptr,
-                       sorted_w, dn_blocks, dn_scales, dn_bias, offsets, d.E, d.I, d.H, d.alpha, d.limit,
-                       nullptr, 0, o);
-    return hipGetLastError();
+    if (small_groups(d))
+        return launch_gemm<false, true>(d, h8, d.T * d.k, nullptr, sorted_w, dn_blocks, dn_scales, dn_bias, offsets,
+                                        d.I, d.H, nullptr, 0, o, s);
+    return launch_gemm<false, false>(d, h8, d.T * d.k, nullptr, sorted_w, dn_blocks, dn_scales, dn_bias, offsets,
+                                     d.I, d.H, nullptr, 0, o, s);
 }
 
 hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row, const uint16_t *residual,
