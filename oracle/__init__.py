@@ -43,24 +43,33 @@ _f64 = _P(dtype=np.float64, flags="C_CONTIGUOUS")
 _f64_or_null = ctypes.c_void_p
 
 
-def build(force: bool = True) -> str:
-    """Compile ``oracle.c`` into ``liboracle.so`` next to it (gcc, OpenMP)."""
-    if force or not os.path.exists(_LIB):
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+def build(force: bool = True, sanitize: bool = False, out: Optional[str] = None) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` next to it (gcc, OpenMP). With ``sanitize``
+    the build carries AddressSanitizer and UndefinedBehaviorSanitizer checks (every
+    undefined-behaviour report is fatal) and goes to ``out``; a process loading it needs
+    gcc's libasan and libubsan preloaded, and names the file in ORACLE_LIB."""
+    lib = out or _LIB
+    if force or not os.path.exists(lib):
+        opt = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"])
+        cmd = ["gcc", *opt, "-std=c11", "-fPIC", "-shared", "-fopenmp",
                "-fno-fast-math", "-ffp-contract=off", "-fvisibility=hidden",
-               _SRC, "-o", _LIB + ".tmp", "-lm"]
+               _SRC, "-o", lib + ".tmp", "-lm"]
         subprocess.check_call(cmd)
-        os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+        os.replace(lib + ".tmp", lib)
+    return lib
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB)
+    path = os.environ.get("ORACLE_LIB")
+    if path is None:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+    lib = ctypes.CDLL(path)
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_e2m1.restype = ctypes.c_double
