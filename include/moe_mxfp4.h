@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_MXFP4_ABI_VERSION 4
+#define MOE_MXFP4_ABI_VERSION 5
 
 typedef uint16_t moe_bf16_t;
 
@@ -298,11 +298,31 @@ moe_status_t moe_mxfp4_quantize_act(const moe_bf16_t *x, int64_t rows, int32_t c
                                     uint8_t *q8, void *stream);
 
 /*
+ * h8 matrix: the format of the expert intermediate h between moe_mxfp4_expert_up and
+ * moe_mxfp4_expert_down (step 4's output, step 5's input; ZeroModels GPT-OSS page,
+ * "Mixture-of-experts feed-forward"). The same 2R data rows of K bytes and the same hi/lo
+ * values and scales as an mx8 matrix, with the scales grouped by four blocks instead of
+ * by row: after the data rows come ceil(K/128) groups of R 32-bit words; byte b % 4 of word
+ * r of group b / 4 is the hi scale (127 + eb) of row r's block b. Lo scales are not stored
+ * (always the hi scale minus 4); bytes for blocks past K/32 are unused. The down GEMM then
+ * reads the scales of 128 consecutive rows for one 128-element step as 512 contiguous bytes.
+ * Size: 2RK + 4R ceil(K/128) bytes, at most moe_mxfp4_mx8_bytes(R, K), which callers allocate.
+ */
+
+/*
+ * bf16 [rows, cols] -> h8 (layout above): the input moe_mxfp4_expert_down takes, for an h
+ * computed elsewhere. h8 needs moe_mxfp4_mx8_bytes(rows, cols) bytes, 16-byte aligned; cols a
+ * positive multiple of 32; rows >= 0. Errors as moe_mxfp4_quantize_act.
+ */
+moe_status_t moe_mxfp4_quantize_h(const moe_bf16_t *h, int64_t rows, int32_t cols,
+                                  uint8_t *h8, void *stream);
+
+/*
  * Steps 3-4 over the sorted rows (grouped gate_up GEMM on the block-scaled MFMA, bias,
  * clamped SwiGLU): h[r, :] = swiglu(x[sorted_token[r]] . Wgu[e]^T + bgu[e]) for every row r
  * of expert e. x8: x as an mx8 matrix of T rows of H (from moe_mxfp4_quantize_act);
- * h8 (out): h as an mx8 matrix of T*k rows of I (moe_mxfp4_mx8_bytes(T*k, I) bytes),
- * rows in sorted order. expert_offsets / sorted_token as produced by moe_mxfp4_permute.
+ * h8 (out): h as an h8 matrix (group-major scales, layout above) of T*k rows of I
+ * (moe_mxfp4_mx8_bytes(T*k, I) bytes), rows in sorted order. expert_offsets / sorted_token as produced by moe_mxfp4_permute.
  */
 moe_status_t moe_mxfp4_expert_up(const moe_mxfp4_shape_t *shape,
                                  const uint8_t *x8,
@@ -314,7 +334,8 @@ moe_status_t moe_mxfp4_expert_up(const moe_mxfp4_shape_t *shape,
 /*
  * Step 5 over the sorted rows (grouped down GEMM on the block-scaled MFMA, bias), scaled
  * by the row's routing weight: o[r, :] = sorted_weight[r] * (h[r] . Wdn[e]^T + bdn[e]).
- * h8: an mx8 matrix of T*k rows of I; o [T*k, H] fp32 (out).
+ * h8: an h8 matrix of T*k rows of I (from moe_mxfp4_expert_up or moe_mxfp4_quantize_h);
+ * o [T*k, H] fp32 (out).
  */
 moe_status_t moe_mxfp4_expert_down(const moe_mxfp4_shape_t *shape,
                                    const uint8_t *h8,

@@ -25,7 +25,7 @@ __all__ = [
     "MoeError", "MoeLibraryMissing", "library_path", "load_library", "abi_version",
     "workspace_bytes", "moe_forward", "route", "permute", "expert_up", "expert_down",
     "combine", "dequant", "permute_workspace_bytes", "DECODE_MAX_T", "DECODE_MAX_K", "uses_decode_path", "mx8_bytes",
-    "quantize_act", "rmsnorm", "moe_forward_dequantized", "dequantize_bank", "workspace_bytes_dequantized",
+    "quantize_act", "quantize_h", "rmsnorm", "moe_forward_dequantized", "dequantize_bank", "workspace_bytes_dequantized",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -98,6 +98,7 @@ _SIGS = {
     "moe_mxfp4_dequant": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp]),
     "moe_mxfp4_mx8_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
     "moe_mxfp4_quantize_act": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp]),
+    "moe_mxfp4_quantize_h": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp]),
 }
 
 
@@ -350,10 +351,21 @@ def quantize_act(x, stream=None):
     return q8
 
 
+def quantize_h(h, stream=None):
+    """bf16 [R, K] -> h8 matrix (group-major scales; what expert_down takes), a flat uint8
+    tensor of mx8_bytes(R, K) bytes."""
+    R, K = h.shape
+    dev = h.device
+    _need(h, "h", _BF16, (R, K), dev)
+    h8 = torch.empty(mx8_bytes(R, K), dtype=torch.uint8, device=dev)
+    _check(load_library().moe_mxfp4_quantize_h(_ptr(h), R, K, _ptr(h8), _stream(stream)))
+    return h8
+
+
 def expert_up(x8, T: int, gu_blocks, gu_scales, gu_bias, offsets, sorted_token, k: int,
               alpha: float = 1.702, limit: float = 7.0, stream=None):
     """Grouped gate_up GEMM + SwiGLU over sorted rows, from x8 (mx8, T rows of H). Returns
-    h8: the mx8 matrix of T*k rows of I (flat uint8)."""
+    h8: the h8 matrix (group-major scales) of T*k rows of I (flat uint8)."""
     E, I2, Hh = gu_blocks.shape
     I, H = I2 // 2, 2 * Hh
     dev = gu_blocks.device
@@ -372,7 +384,8 @@ def expert_up(x8, T: int, gu_blocks, gu_scales, gu_bias, offsets, sorted_token, 
 
 
 def expert_down(h8, T: int, dn_blocks, dn_scales, dn_bias, offsets, sorted_weight, k: int, stream=None):
-    """Grouped down GEMM + bias, times the row's routing weight, from h8 (mx8, T*k rows of I).
+    """Grouped down GEMM + bias, times the row's routing weight, from h8 (T*k rows of I, as
+    expert_up or quantize_h write it).
     Returns o [T*k, H] fp32."""
     E, H, Ih = dn_blocks.shape
     I, N = 2 * Ih, T * k

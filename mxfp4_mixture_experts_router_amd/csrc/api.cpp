@@ -614,15 +614,26 @@ MOE_EXPORT size_t moe_mxfp4_mx8_bytes(int64_t rows, int32_t cols) {
     return rows > 0 && cols > 0 ? moe::mx8_bytes(rows, cols) : 0;
 }
 
-MOE_EXPORT moe_status_t moe_mxfp4_quantize_act(const moe_bf16_t *x, int64_t rows, int32_t cols,
-                                               uint8_t *q8, void *stream) {
+namespace {
+moe_status_t quantize_rows(const moe_bf16_t *x, int64_t rows, int32_t cols, uint8_t *q8, bool h8, void *stream) {
     if (rows < 0) return fail(MOE_EINVAL, "rows must be >= 0 (got %lld)", static_cast<long long>(rows));
     if (cols <= 0 || cols % 32 != 0) return fail(MOE_ESHAPE, "cols must be a positive multiple of 32 (got %d)", cols);
     if (rows == 0) return ok();
     REQUIRE16(x, "x");
     REQUIRE16(q8, "q8");
-    LAUNCH(moe::launch_quantize(x, rows, cols, q8, static_cast<hipStream_t>(stream)), "quantize");
+    LAUNCH(moe::launch_quantize(x, rows, cols, q8, h8, static_cast<hipStream_t>(stream)), "quantize");
     return ok();
+}
+}  // namespace
+
+MOE_EXPORT moe_status_t moe_mxfp4_quantize_act(const moe_bf16_t *x, int64_t rows, int32_t cols,
+                                               uint8_t *q8, void *stream) {
+    return quantize_rows(x, rows, cols, q8, false, stream);
+}
+
+MOE_EXPORT moe_status_t moe_mxfp4_quantize_h(const moe_bf16_t *h, int64_t rows, int32_t cols,
+                                             uint8_t *h8, void *stream) {
+    return quantize_rows(h, rows, cols, h8, true, stream);
 }
 
 MOE_EXPORT moe_status_t moe_mxfp4_expert_up(const moe_mxfp4_shape_t *shape, const uint8_t *x8,

@@ -34,7 +34,10 @@
 // Scale loads fetch a few bytes from each of many rows, so they touch far more cache lines
 // than their size suggests; they are kept few. Only the hi rows' A scales are loaded (an
 // mx8 lo row's scale is always its hi row's minus 4), and the weight scales are loaded in
-// 16-byte windows that serve three stages.
+// 16-byte windows that serve three stages. The up GEMM writes h with group-major scales
+// (mx_mfma.h), so that the down GEMM's A scales of a stage are 512 contiguous bytes (4
+// cache lines) instead of 4 bytes from each of 128 rows (up: the x rows are gathered
+// tokens, whose row-major scale rows stay in L2 across the stages).
 //
 // Stage buffer layout (bytes):
 //   A   [256 rows][128]: row R = 2 * (tile row) + part; its eight 16-byte chunks c are stored
@@ -210,8 +213,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
 #pragma unroll
         for (int i = 0; i < C::NA; ++i)
             A.a_off[i] = a_src(8 * (C::NA * wave + i) + (lane >> 3)) * static_cast<uint32_t>(K);
-        // A scales of the hi rows: wavefront w < 2 fills tile rows 64 w + lane
-        A.as_off = a_src(2 * (64 * (wave & 1) + lane)) * static_cast<uint32_t>(ass);
+        // A scales of the hi rows: wavefront w < 2 fills tile rows 64 w + lane (up: x8's
+        // row-major scale rows; down: h8's group-major dwords, one per row and stage)
+        const uint32_t asrc = a_src(2 * (64 * (wave & 1) + lane));
+        A.as_off = UP ? asrc * static_cast<uint32_t>(ass) : (asrc >> 1) * 4u;
         A.wblk = wblocks + static_cast<int64_t>(A.e) * Nrows * kbytes;
         if constexpr (SMALL) {
             // B pairs: instruction i of wavefront w fills rows 32 (w % 4) + 8 i + lane / 8 of
@@ -279,7 +284,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             const uint8_t *a_k = a8 + kBK * kt;          // uniform bases
 #pragma unroll
             for (int i = 0; i < C::NA; ++i) dma16(a_k, S.a_off[i] + ach, lbuf + (C::NA * wave + i) * 1024);
-            if (wave < 2) dma4(a_sc + 4 * kt, S.as_off, lbuf + C::OFF_AS + 256 * wave);
+            if (wave < 2) dma4(UP ? a_sc + 4 * kt : a_sc + static_cast<size_t>(4 * kt) * a_rows, S.as_off,
+                               lbuf + C::OFF_AS + 256 * wave);
             if constexpr (SMALL) {
                 if ((kt & 1) == 0) {
                     const int q = kt >> 1;                  // pair q: stages 2q, 2q + 1
@@ -521,7 +527,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             }
             __syncthreads();
             const int Iw = Nrows / 2;
-            const int is8 = mx8_scale_stride(Iw);
             uint8_t *h_sc = h8 + static_cast<size_t>(2 * h_rows) * Iw;
             {
                 const int r = lane >> 1, blk = lane & 1;
@@ -531,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
                     float v[32];
 #pragma unroll
                     for (int i = 0; i < 32; ++i) v[i] = s_h[r * kHS + 32 * blk + i];
-                    store_mx8_block(v, h8, h_sc, static_cast<int64_t>(row0 + R), Iw, is8, ib);
+                    store_h8_block(v, h8, h_sc, static_cast<int64_t>(row0 + R), Iw, h_rows, ib);
                 }
             }
         } else {
@@ -632,7 +637,9 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ blo
     }
 }
 
-// bf16 rows -> mx8 matrix: one thread per 32-element block per grid-stride step.
+// bf16 rows -> mx8 matrix (H8: with the h8 matrix's group-major scales): one thread per
+// 32-element block per grid-stride step.
+template <bool H8>
 __global__ __launch_bounds__(256) void k_quantize(const uint16_t *__restrict__ x, int64_t rows, int cols,
                                                   uint8_t *__restrict__ q8) {
     const int nb = cols / 32;
@@ -655,7 +662,8 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t *__restrict__ x
                 v[8 * j + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
             }
         }
-        store_mx8_block(v, q8, qs, r, cols, ss, b);
+        if constexpr (H8) store_h8_block(v, q8, qs, r, cols, rows, b);
+        else store_mx8_block(v, q8, qs, r, cols, ss, b);
     }
 }
 
@@ -722,10 +730,11 @@ hipError_t launch_combine(const Dims &d, const float *o, const int32_t *slot_row
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const uint16_t *x, int64_t rows, int cols, uint8_t *q8, hipStream_t s) {
+hipError_t launch_quantize(const uint16_t *x, int64_t rows, int cols, uint8_t *q8, bool h8, hipStream_t s) {
     const int64_t nblk = rows * (cols / 32);
     if (nblk == 0) return hipSuccess;
-    MOE_LAUNCH(k_quantize, dim3(grid_for(nblk)), dim3(256), 0, s, x, rows, cols, q8);
+    if (h8) MOE_LAUNCH(k_quantize<true>, dim3(grid_for(nblk)), dim3(256), 0, s, x, rows, cols, q8);
+    else MOE_LAUNCH(k_quantize<false>, dim3(grid_for(nblk)), dim3(256), 0, s, x, rows, cols, q8);
     return hipGetLastError();
 }
 

@@ -138,8 +138,9 @@ hipError_t launch_down_bank(const Dims &d, const uint16_t *h, const uint16_t *dn
 hipError_t launch_rmsnorm(const Dims &d, const uint16_t *x, const uint16_t *gamma, double eps, uint16_t *xn,
                           hipStream_t s);
 
-// bf16 [rows, cols] -> mx8 matrix (mx_mfma.h).
-hipError_t launch_quantize(const uint16_t *x, int64_t rows, int cols, uint8_t *q8, hipStream_t s);
+// bf16 [rows, cols] -> mx8 matrix, or with h8 the grouped down GEMM's h8 layout (group-major
+// scales; both in mx_mfma.h).
+hipError_t launch_quantize(const uint16_t *x, int64_t rows, int cols, uint8_t *q8, bool h8, hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t *blocks, const uint8_t *scales, int64_t rows, int cols,
                           uint16_t *out, hipStream_t s);

@@ -120,6 +120,31 @@ __device__ __forceinline__ void store_mx8_block(const float (&v)[32], uint8_t *q
     qs[(2 * n + 1) * ss + b] = static_cast<uint8_t>(sl);
 }
 
+// The expert intermediate h ("h8": written by the grouped gate_up GEMM, read by the grouped
+// down GEMM) uses the same data rows with group-major scales: for R rows, group j of four
+// scale blocks (4j .. 4j + 3) is R dwords, dword n holding row n's hi scales of those blocks
+// (byte b % 4); a lo scale is its hi scale minus 4 and is not stored. A GEMM stage of 128
+// contraction elements is one group, so its scales for consecutive rows are contiguous.
+// 4 R ceil(K / 128) scale bytes, never more than the row-major layout's 2 R S.
+__host__ __device__ inline size_t h8_scale_offset(int64_t R, int64_t n, int b) {
+    return static_cast<size_t>(4 * (static_cast<int64_t>(b >> 2) * R + n) + (b & 3));
+}
+
+// Writes one 32-element block v of row n as store_mx8_block does, into an h8 matrix of R
+// rows (group-major scales at qs).
+__device__ __forceinline__ void store_h8_block(const float (&v)[32], uint8_t *q8, uint8_t *qs, int64_t n, int K,
+                                               int64_t R, int b) {
+    uint32_t hi[8], lo[8], sh, sl;
+    mx8_split_block(v, hi, lo, sh, sl);
+    uint4 *dh = reinterpret_cast<uint4 *>(q8 + (2 * n) * K + 32 * b);
+    uint4 *dl = reinterpret_cast<uint4 *>(q8 + (2 * n + 1) * K + 32 * b);
+    dh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    dh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+    dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+    qs[h8_scale_offset(R, n, b)] = static_cast<uint8_t>(sh);
+}
+
 // The mx8 rows of bf16 activation row `xrow` (K elements) as row r of the mx8 matrix q8
 // holding R rows; the calling block's threads from `first` on share the K / 32 blocks
 // (threads below `first` do nothing).

@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert moe.abi_version() == 4
-    assert "#define MOE_MXFP4_ABI_VERSION 4" in open(HEADER).read()
+    assert moe.abi_version() == 5
+    assert "#define MOE_MXFP4_ABI_VERSION 5" in open(HEADER).read()
 
 
 def shape(T=1, H=2880, I=2880, E=32, k=4, alpha=1.702, limit=7.0):
@@ -235,6 +235,14 @@ def test_mx8_format_entry_points(lib):
     assert lib.moe_mxfp4_quantize_act(A, 4, 64, None, None) == EINVAL
     assert lib.moe_mxfp4_quantize_act(A + 2, 4, 64, A, None) == EALIGN
     assert lib.moe_mxfp4_quantize_act(None, 0, 64, None, None) == 0
+    # the h8 layout (group-major scales) fits the same allocation for every K
+    for K in range(32, 4097, 32):
+        assert 2 * K + 4 * ((K + 127) // 128) <= lib.moe_mxfp4_mx8_bytes(1, K)
+    assert lib.moe_mxfp4_quantize_h(A, 4, 48, A, None) == ESHAPE
+    assert lib.moe_mxfp4_quantize_h(A, -1, 64, A, None) == EINVAL
+    assert lib.moe_mxfp4_quantize_h(A, 4, 64, None, None) == EINVAL
+    assert lib.moe_mxfp4_quantize_h(A, 4, 64, A + 8, None) == EALIGN
+    assert lib.moe_mxfp4_quantize_h(None, 0, 64, None, None) == 0
 
 
 def test_dequant_validates(lib):

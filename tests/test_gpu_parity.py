@@ -18,7 +18,7 @@ import mxfp4_mixture_experts_router_amd as moe
 import oracle
 from workloads import CONFIGS, make_inputs, f32_from_bf16_bits, bf16_bits_from_f32
 
-from gpu_util import (assert_close_rows, bf16_bits, bf16_to_f64, check_selection, decode_mx8,
+from gpu_util import (assert_close_rows, bf16_bits, bf16_to_f64, check_selection, decode_h8, decode_mx8,
                       host_permutation, to_dev, upload)
 
 pytestmark = pytest.mark.gpu
@@ -203,14 +203,14 @@ def test_expert_up_and_down_grouped(name, T, H, I, E, k):
     h8 = moe.expert_up(x8, T, d["gu_blocks"], d["gu_scales"], d["gu_bias"], to_dev(offsets),
                        to_dev(sorted_token), k, cfg.alpha, cfg.limit)
     rows = slot_row.reshape(T, k)[tokens]                      # [n, k] sorted rows of the sample
-    h_np = decode_mx8(h8, T * k, I)
+    h_np = decode_h8(h8, T * k, I)
     assert_close_rows(h_np[rows.reshape(-1)], ref["h"].reshape(-1, I), "h")
-    # down: feed the oracle's h (rounded to bf16, then to mx8 on the GPU) so this step is
+    # down: feed the oracle's h (rounded to bf16, then to h8 on the GPU) so this step is
     # checked on its own
     h_in = np.zeros((T * k, I), dtype=np.uint16)
     h_in[rows.reshape(-1)] = bf16_bits_from_f32(ref["h"].reshape(-1, I).astype(np.float32))
     sorted_w = w.reshape(-1)[order].astype(np.float32)
-    o = moe.expert_down(moe.quantize_act(to_dev(h_in)), T, d["dn_blocks"], d["dn_scales"], d["dn_bias"],
+    o = moe.expert_down(moe.quantize_h(to_dev(h_in)), T, d["dn_blocks"], d["dn_scales"], d["dn_bias"],
                         to_dev(offsets), to_dev(sorted_w), k)
     o_np = o.cpu().numpy().astype(np.float64)[rows.reshape(-1)]
     want = (ref["o"] * ref["w"][:, :, None]).reshape(-1, H)
@@ -238,6 +238,24 @@ def test_quantize_act_is_exact_for_bf16(R, K):
     near = np.abs(xv) >= bmax * 2.0 ** -13
     assert np.array_equal(got[near], xv[near])
     assert np.all(np.abs(got - xv) <= bmax * 2.0 ** -21)
+
+
+@pytest.mark.parametrize("R,K", [(1, 32), (37, 96), (300, 2880), (129, 160)])
+def test_quantize_h_is_mx8_with_group_major_scales(R, K):
+    """The h8 matrix holds the same data rows as the mx8 one, and byte b % 4 of word r of
+    scale group b // 4 is the mx8 hi scale of row r's block b (every lo scale is hi - 4)."""
+    rng = np.random.default_rng(R + K)
+    x = (rng.standard_normal((R, K // 32, 32)) * np.exp2(rng.integers(-30, 30, size=(R, K // 32, 1)))).reshape(R, K)
+    bits = to_dev(bf16_bits_from_f32(x.astype(np.float32)))
+    q8 = moe.quantize_act(bits).cpu().numpy()
+    h8 = moe.quantize_h(bits).cpu().numpy()
+    nb, G, S = K // 32, (K + 127) // 128, (K // 32 + 15) // 16 * 16
+    assert np.array_equal(h8[: 2 * R * K], q8[: 2 * R * K])
+    sc = q8[2 * R * K: 2 * R * K + 2 * R * S].reshape(2 * R, S)[:, :nb].astype(np.int64)
+    assert np.array_equal(sc[1::2], sc[0::2] - 4)
+    grp = h8[2 * R * K: 2 * R * K + 4 * R * G].reshape(G, R, 4).transpose(1, 0, 2).reshape(R, 4 * G)[:, :nb]
+    assert np.array_equal(grp, sc[0::2])
+    assert np.array_equal(decode_h8(h8, R, K), decode_mx8(q8, R, K))
 
 
 # ----------------------------------------------------------------------------- whole layer

@@ -128,6 +128,8 @@ assert lib.moe_mxfp4_mx8_bytes(i64(3), ctypes.c_int32(64)) > 0
 assert lib.moe_mxfp4_route(ctypes.byref(s), vp(A), vp(A), vp(A), None, vp(A), None, None) == 1
 assert lib.moe_mxfp4_permute(ctypes.byref(s), vp(A), vp(A), vp(A), vp(A), vp(A), None, None) == 1
 assert lib.moe_mxfp4_dequant(None, vp(A), i64(4), ctypes.c_int32(64), vp(A), None) == 1
+assert lib.moe_mxfp4_quantize_h(vp(A), i64(4), ctypes.c_int32(48), vp(A), None) == 2
+assert lib.moe_mxfp4_quantize_h(vp(A), i64(4), ctypes.c_int32(64), None, None) == 1
 assert lib.moe_mxfp4_last_error()
 print("sanitized run done")
 """
