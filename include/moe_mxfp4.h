@@ -301,12 +301,13 @@ moe_status_t moe_mxfp4_quantize_act(const moe_bf16_t *x, int64_t rows, int32_t c
  * h8 matrix: the format of the expert intermediate h between moe_mxfp4_expert_up and
  * moe_mxfp4_expert_down (step 4's output, step 5's input; ZeroModels GPT-OSS page,
  * "Mixture-of-experts feed-forward"). The same 2R data rows of K bytes and the same hi/lo
- * values and scales as an mx8 matrix, with the scales grouped by four blocks instead of
- * by row: after the data rows come ceil(K/128) groups of R 32-bit words; byte b % 4 of word
- * r of group b / 4 is the hi scale (127 + eb) of row r's block b. Lo scales are not stored
- * (always the hi scale minus 4); bytes for blocks past K/32 are unused. The down GEMM then
- * reads the scales of 128 consecutive rows for one 128-element step as 512 contiguous bytes.
- * Size: 2RK + 4R ceil(K/128) bytes, at most moe_mxfp4_mx8_bytes(R, K), which callers allocate.
+ * values and scales as an mx8 matrix, with the scales grouped by sixteen blocks instead of
+ * by row: after the data rows come ceil(K/512) groups of R 16-byte words; byte b % 16 of
+ * word r of group b / 16 is the hi scale (127 + eb) of row r's block b. Lo scales are not
+ * stored (always the hi scale minus 4); bytes for blocks past K/32 are unused. The down GEMM
+ * then reads the scales of 128 consecutive rows for four 128-element steps as 2 KB of
+ * contiguous bytes. Size: 2RK + 16R ceil(K/512) bytes, less than moe_mxfp4_mx8_bytes(R, K),
+ * which callers allocate.
  */
 
 /*

@@ -33,23 +33,23 @@
 //
 // Scale loads fetch a few bytes from each of many rows, so they touch far more cache lines
 // than their size suggests; they are kept few. Only the hi rows' A scales are loaded (an
-// mx8 lo row's scale is always its hi row's minus 4), and the weight scales are loaded in
-// 16-byte windows that serve three stages. The up GEMM writes h with group-major scales
-// (mx_mfma.h), so that the down GEMM's A scales of a stage are 512 contiguous bytes (4
-// cache lines) instead of 4 bytes from each of 128 rows (up: the x rows are gathered
-// tokens, whose row-major scale rows stay in L2 across the stages).
+// mx8 lo row's scale is always its hi row's minus 4) in aligned 16-byte windows that serve
+// four stages, and the weight scales in 16-byte windows that serve three stages. The up GEMM
+// writes h with group-major scales (mx_mfma.h), so that the down GEMM's A-scale windows of 128
+// rows are 2 KB of contiguous bytes.
 //
 // Stage buffer layout (bytes):
 //   A   [256 rows][128]: row R = 2 * (tile row) + part; its eight 16-byte chunks c are stored
 //       at slot c ^ (R & 7) (conflict-free operand reads).
 //   B   [256 rows][64]: the stage's four packed MXFP4 blocks of weight row n, block c at
 //       slot c ^ ((n >> 1) & 3).
-//   AS  [128 tile rows] 4 bytes: the E8M0 scales of the stage's four blocks of the hi row.
 // Then two weight-scale group buffers (group j = stages 3j .. 3j + 2, buffer j % 2):
 //   BSG [256 rows] 16 bytes: the four 4-byte-aligned dwords of weight scale row n that hold
 //       the group's twelve scale bytes (weight scale rows are K / 32 bytes long, not
 //       4-aligned); a dword past the tensor's end holds no valid byte and reads the last
 //       dword instead.
+// Then two A-scale group buffers (group j = stages 4j .. 4j + 3, buffer j % 2):
+//   ASG [128 tile rows] 16 bytes: the E8M0 scales of the hi row's blocks 16j .. 16j + 15.
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -77,45 +77,48 @@ constexpr int kThreads = 512;                  // 8 wavefronts: 4 row groups x 2
 constexpr int kChunk = 32;                     // items per XCD chunk (= blocks per XCD)
 constexpr int kHS = 67;                        // up epilogue: padded row of 64 fp32 pairs
 constexpr int kOS = 132;                       // down epilogue: padded row of 128 fp32 outputs
+constexpr int kGA = 4;                         // stages per A-scale group (16 blocks)
+constexpr int kASG = 128 * 16;                 // one A-scale group buffer
 
 // The two tile configurations (LDS byte offsets).
 //   Full tiles (SMALL = false): 128 activation rows; each stage buffer holds the stage's A
-//   rows, its 256 weight rows' 64 bytes (half of a 128-byte line) and the hi rows' A scales;
-//   weight scales in 16-byte windows per three stages (group ring of two).
+//   rows and its 256 weight rows' 64 bytes (half of a 128-byte line); weight scales in
+//   16-byte windows per three stages (group ring of two).
 //   Small groups (SMALL = true, experts of at most about 96 rows): 96 activation rows; the
-//   stage buffers hold A and its scales only; the weights come as whole 128-byte lines that
-//   serve two stages, into a ring of two such pair slots per column half (each half is read
-//   only by the wavefronts of its column half, which also load it), with their scale windows
-//   per pair.
-// Global-to-LDS instructions per wavefront: full: 4 A, 2 B per stage, 1 A-scale (wavefronts
-// 0-1), 2 weight-scale dwords every third stage; small: 3 A per stage, 1 A-scale (wavefronts
-// 0-1), and with every even stage 4 B and 2 weight-scale dwords.
+//   stage buffers hold A only; the weights come as whole 128-byte lines that serve two
+//   stages, into a ring of two such pair slots per column half (each half is read only by
+//   the wavefronts of its column half, which also load it), with their scale windows per pair.
+//   Both: the hi rows' A scales in 16-byte windows per four stages (group ring of two).
+// Global-to-LDS instructions per wavefront: full: 4 A, 2 B per stage, 2 weight-scale dwords
+// every third stage; small: 3 A per stage, and with every even stage 4 B and 2 weight-scale
+// dwords; both: 1 A-scale window every fourth stage (wavefronts 0-1).
 template <bool SMALL> struct GemmCfg;
 template <> struct GemmCfg<false> {
     static constexpr int BM = 128, NA = 4, NLMAX = 4;
     static constexpr int OFF_B = 2 * BM * kBK;                 // 32768
-    static constexpr int OFF_AS = OFF_B + kBN * kBK / 2;       // 49152
-    static constexpr int STAGE = OFF_AS + 128 * 4;             // 49664
+    static constexpr int STAGE = OFF_B + kBN * kBK / 2;        // 49152
     static constexpr int GS = 3;                               // stages per weight-scale group
-    static constexpr int OFF_BSG = 3 * STAGE;                  // 148992
+    static constexpr int OFF_BSG = 3 * STAGE;                  // 147456
     static constexpr int BSG = kBN * 16;                       // one group buffer
-    static constexpr int TOTAL = OFF_BSG + 2 * BSG;            // 157184
+    static constexpr int OFF_ASG = OFF_BSG + 2 * BSG;          // 155648
+    static constexpr int TOTAL = OFF_ASG + 2 * kASG;           // 159744
 };
 template <> struct GemmCfg<true> {
     static constexpr int BM = 96, NA = 3, NLMAX = 3;
-    static constexpr int OFF_AS = 2 * BM * kBK;                // 24576
-    static constexpr int STAGE = OFF_AS + 128 * 4;             // 25088
-    static constexpr int OFF_BP = 3 * STAGE;                   // 75264: pair slots [half][2]
+    static constexpr int STAGE = 2 * BM * kBK;                 // 24576
+    static constexpr int OFF_BP = 3 * STAGE;                   // 73728: pair slots [half][2]
     static constexpr int BP = 128 * 128;                       // one slot: 128 rows x 128 bytes
-    static constexpr int OFF_BSG = OFF_BP + 4 * BP;            // 140800: scale slots [half][2]
+    static constexpr int OFF_BSG = OFF_BP + 4 * BP;            // 139264: scale slots [half][2]
     static constexpr int BSG = 128 * 16;
-    static constexpr int TOTAL = OFF_BSG + 4 * BSG;            // 148992
+    static constexpr int OFF_ASG = OFF_BSG + 4 * BSG;          // 147456
+    static constexpr int TOTAL = OFF_ASG + 2 * kASG;           // 151552
     static constexpr int OFF_B = 0, GS = 2;                    // (weights and their scales per pair)
 };
 
 __shared__ __attribute__((aligned(16))) uint8_t g_stages[GemmCfg<false>::TOTAL];
 static_assert(GemmCfg<true>::TOTAL <= GemmCfg<false>::TOTAL, "one LDS array serves both configurations");
-static_assert(8 * 32 * kOS * 4 <= GemmCfg<true>::TOTAL, "the epilogue's staging fits both configurations");
+static_assert(8 * 32 * kOS * 4 <= GemmCfg<true>::OFF_ASG && 8 * 32 * kOS * 4 <= GemmCfg<false>::OFF_ASG,
+              "the epilogue's staging fits both configurations below the A-scale groups");
 
 template <bool UP, bool SMALL>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
@@ -132,7 +135,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
     __shared__ uint16_t s_bias[kBN];                // the tile's biases (bf16)
     using C = GemmCfg<SMALL>;
     constexpr int kBM = C::BM;
-    __shared__ float s_rw[128];                     // down: the tile rows' routing weights
+    // up: the next tile's token indices ([2][128]); down: the tile rows' routing weights
+    __shared__ int s_tok_rw[256];
+    float *s_rw = reinterpret_cast<float *>(s_tok_rw);
 
     const int ntn = (Nrows + kBN - 1) / kBN;
     const int tid0 = threadIdx.x;
@@ -213,10 +218,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
 #pragma unroll
         for (int i = 0; i < C::NA; ++i)
             A.a_off[i] = a_src(8 * (C::NA * wave + i) + (lane >> 3)) * static_cast<uint32_t>(K);
-        // A scales of the hi rows: wavefront w < 2 fills tile rows 64 w + lane (up: x8's
-        // row-major scale rows; down: h8's group-major dwords, one per row and stage)
+        // A-scale windows of the hi rows: wavefront w < 2 fills tile rows 64 w + lane (up:
+        // window j of x8's row-major scale row, at byte 16 j; down: row r's 16 bytes of h8's
+        // group j, at 16 (j rows + r))
         const uint32_t asrc = a_src(2 * (64 * (wave & 1) + lane));
-        A.as_off = UP ? asrc * static_cast<uint32_t>(ass) : (asrc >> 1) * 4u;
+        A.as_off = UP ? asrc * static_cast<uint32_t>(ass) : (asrc >> 1) * 16u;
         A.wblk = wblocks + static_cast<int64_t>(A.e) * Nrows * kbytes;
         if constexpr (SMALL) {
             // B pairs: instruction i of wavefront w fills rows 32 (w % 4) + 8 i + lane / 8 of
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
 
     // up: the next tile's token indices, loaded into LDS while the current tile runs, so that
     // its stage addresses need no dependent global load when it starts
-    __shared__ int s_ntok[2][128];
+    int (*s_ntok)[128] = reinterpret_cast<int (*)[128]>(s_tok_rw);
     int ntile = 0;  // tiles this workgroup has started
     for (int c = xcd; c * kChunk < items; c += 8, ++ntile) {
         const int item = c * kChunk + lb;
@@ -284,8 +290,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             const uint8_t *a_k = a8 + kBK * kt;          // uniform bases
 #pragma unroll
             for (int i = 0; i < C::NA; ++i) dma16(a_k, S.a_off[i] + ach, lbuf + (C::NA * wave + i) * 1024);
-            if (wave < 2) dma4(UP ? a_sc + 4 * kt : a_sc + static_cast<size_t>(4 * kt) * a_rows, S.as_off,
-                               lbuf + C::OFF_AS + 256 * wave);
+            if (kt % kGA == 0 && wave < 2)
+                dma16(UP ? a_sc + 4 * kt : a_sc + static_cast<size_t>(4 * kt) * a_rows, S.as_off,
+                      lds0 + C::OFF_ASG + ((kt / kGA) & 1) * kASG + 1024 * wave);
             if constexpr (SMALL) {
                 if ((kt & 1) == 0) {
                     const int q = kt >> 1;                  // pair q: stages 2q, 2q + 1
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
                                     : C::OFF_B + 8192 * wn + 64 * m + 16 * (g ^ ((m >> 1) & 3));
         const uint32_t lb_bs = C::OFF_BSG + 16 * ((SMALL ? 0 : 128 * wn) + m) + (((n0 + 128 * wn + m) * nkb) & 3) + g;
         const uint32_t lb_a = 2048 * wm + 128 * m + 16 * (g ^ (m & 7));
-        const uint32_t lb_as = C::OFF_AS + 32 * wm + 4 * (m >> 1) + g;
+        const uint32_t lb_as = 16 * (8 * wm + (m >> 1)) + g;
         const uint32_t lo_row = 4u * (m & 1);
         // the wavefront's row tiles are the tile's 16-row tiles 4 mt + wm (interleaved, so
         // that a partly filled tile splits its rows evenly); only the first NL are multiplied
@@ -378,6 +385,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
                 gsc = g_stages + ((kt / C::GS) & 1) * C::BSG + 4 * (kt % C::GS);
             }
             const int vb = nkb - 4 * kt;
+            const uint8_t *asg = g_stages + C::OFF_ASG + ((kt / kGA) & 1) * kASG + 4 * (kt % kGA);
             uint32_t sb[8], sa[4];
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
@@ -388,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
             for (int mt = 0; mt < NL; ++mt) {
                 alo[mt] = *reinterpret_cast<const uint4 *>(base + lb_a + 8192 * mt);
                 ahi[mt] = *reinterpret_cast<const uint4 *>(base + (lb_a ^ 64u) + 8192 * mt);   // chunk g + 4
-                sa[mt] = base[lb_as + 128 * mt] - lo_row;
+                sa[mt] = asg[lb_as + 512 * mt] - lo_row;
             }
 #pragma unroll
             for (int mt = NL; mt < 4; ++mt) sa[mt] = 127u;
@@ -423,8 +431,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         auto wait_stage = [&](int s) {
             if (s + 1 < kt_total) {
                 // this wavefront's loads of stage s + 1
-                const int n = SMALL ? 3 + (wave < 2 ? 1 : 0) + (((s + 1) & 1) == 0 ? 6 : 0)
-                                    : 6 + (wave < 2 ? 1 : 0) + ((s + 1) % C::GS == 0 ? 2 : 0);
+                const int nas = wave < 2 && (s + 1) % kGA == 0 ? 1 : 0;
+                const int n = SMALL ? 3 + nas + (((s + 1) & 1) == 0 ? 6 : 0)
+                                    : 6 + nas + ((s + 1) % C::GS == 0 ? 2 : 0);
                 switch (n) {
                     case 3: wait_vm<3>(); break;
                     case 4: wait_vm<4>(); break;

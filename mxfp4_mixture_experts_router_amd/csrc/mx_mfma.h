@@ -121,13 +121,13 @@ __device__ __forceinline__ void store_mx8_block(const float (&v)[32], uint8_t *q
 }
 
 // The expert intermediate h ("h8": written by the grouped gate_up GEMM, read by the grouped
-// down GEMM) uses the same data rows with group-major scales: for R rows, group j of four
-// scale blocks (4j .. 4j + 3) is R dwords, dword n holding row n's hi scales of those blocks
-// (byte b % 4); a lo scale is its hi scale minus 4 and is not stored. A GEMM stage of 128
-// contraction elements is one group, so its scales for consecutive rows are contiguous.
-// 4 R ceil(K / 128) scale bytes, never more than the row-major layout's 2 R S.
+// down GEMM) uses the same data rows with group-major scales: for R rows, group j of sixteen
+// scale blocks (16j .. 16j + 15, four GEMM stages of 128 elements) is R 16-byte words, word n
+// holding row n's hi scales of those blocks (byte b % 16); a lo scale is its hi scale minus 4
+// and is not stored. The windows of consecutive rows are then contiguous. 16 R ceil(K / 512)
+// scale bytes: half of the row-major layout's 2 R S.
 __host__ __device__ inline size_t h8_scale_offset(int64_t R, int64_t n, int b) {
-    return static_cast<size_t>(4 * (static_cast<int64_t>(b >> 2) * R + n) + (b & 3));
+    return static_cast<size_t>(16 * (static_cast<int64_t>(b >> 4) * R + n) + (b & 15));
 }
 
 // Writes one 32-element block v of row n as store_mx8_block does, into an h8 matrix of R

@@ -84,13 +84,13 @@ def decode_mx8(q8, R: int, K: int) -> np.ndarray:
 
 
 def decode_h8(q8, R: int, K: int) -> np.ndarray:
-    """Values [R, K] of an h8 matrix (mx8 data rows; hi scales group-major, byte b % 4 of
-    word r of group b // 4; lo scale = hi - 4; layout in moe_mxfp4.h)."""
+    """Values [R, K] of an h8 matrix (mx8 data rows; hi scales group-major, byte b % 16 of
+    word r of group b // 16; lo scale = hi - 4; layout in moe_mxfp4.h)."""
     q = np.asarray(q8.cpu().numpy() if hasattr(q8, "cpu") else q8, dtype=np.uint8)
-    nb, G = K // 32, (K + 127) // 128
+    nb, G = K // 32, (K + 511) // 512
     data = q[: 2 * R * K].reshape(2 * R, K)
-    grp = q[2 * R * K: 2 * R * K + 4 * R * G].reshape(G, R, 4)
-    s_hi = grp.transpose(1, 0, 2).reshape(R, 4 * G)[:, :nb].astype(np.int64)
+    grp = q[2 * R * K: 2 * R * K + 16 * R * G].reshape(G, R, 16)
+    s_hi = grp.transpose(1, 0, 2).reshape(R, 16 * G)[:, :nb].astype(np.int64)
     hi = E4M3[data[0::2]] * np.ldexp(1.0, np.repeat(s_hi, 32, axis=1) - 127)
     lo = E4M3[data[1::2]] * np.ldexp(1.0, np.repeat(s_hi - 4, 32, axis=1) - 127)
     return hi + lo

@@ -240,20 +240,20 @@ def test_quantize_act_is_exact_for_bf16(R, K):
     assert np.all(np.abs(got - xv) <= bmax * 2.0 ** -21)
 
 
-@pytest.mark.parametrize("R,K", [(1, 32), (37, 96), (300, 2880), (129, 160)])
+@pytest.mark.parametrize("R,K", [(1, 32), (37, 96), (300, 2880), (129, 160), (5, 1056)])
 def test_quantize_h_is_mx8_with_group_major_scales(R, K):
-    """The h8 matrix holds the same data rows as the mx8 one, and byte b % 4 of word r of
-    scale group b // 4 is the mx8 hi scale of row r's block b (every lo scale is hi - 4)."""
+    """The h8 matrix holds the same data rows as the mx8 one, and byte b % 16 of word r of
+    scale group b // 16 is the mx8 hi scale of row r's block b (every lo scale is hi - 4)."""
     rng = np.random.default_rng(R + K)
     x = (rng.standard_normal((R, K // 32, 32)) * np.exp2(rng.integers(-30, 30, size=(R, K // 32, 1)))).reshape(R, K)
     bits = to_dev(bf16_bits_from_f32(x.astype(np.float32)))
     q8 = moe.quantize_act(bits).cpu().numpy()
     h8 = moe.quantize_h(bits).cpu().numpy()
-    nb, G, S = K // 32, (K + 127) // 128, (K // 32 + 15) // 16 * 16
+    nb, G, S = K // 32, (K + 511) // 512, (K // 32 + 15) // 16 * 16
     assert np.array_equal(h8[: 2 * R * K], q8[: 2 * R * K])
     sc = q8[2 * R * K: 2 * R * K + 2 * R * S].reshape(2 * R, S)[:, :nb].astype(np.int64)
     assert np.array_equal(sc[1::2], sc[0::2] - 4)
-    grp = h8[2 * R * K: 2 * R * K + 4 * R * G].reshape(G, R, 4).transpose(1, 0, 2).reshape(R, 4 * G)[:, :nb]
+    grp = h8[2 * R * K: 2 * R * K + 16 * R * G].reshape(G, R, 16).transpose(1, 0, 2).reshape(R, 16 * G)[:, :nb]
     assert np.array_equal(grp, sc[0::2])
     assert np.array_equal(decode_h8(h8, R, K), decode_mx8(q8, R, K))
 
