@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         // share of a later stage's global loads, so the matrix unit is fed from both.
         //   phase 2s:     wavefronts 0-3 read stage s;       4-7 multiply stage s - 1
         //   phase 2s + 1: wavefronts 0-3 multiply stage s;   4-7 read stage s
-        // In its memory phase for stage s a wavefront first issues its loads of stage s + 2
+        // In its memory phase for stage s a wavefront also issues its loads of stage s + 2
         // into the buffer stage s - 1 used (both groups have read it by then). Before phase 2s
         // every wavefront waits for its loads of stage s (only stage s + 1's stay in flight),
         // and the barrier then publishes the stage; a memory phase ends with its LDS reads
@@ -481,13 +481,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(
         if (kt_total > 1) issue(1, 1);
         wait_stage(0);
         phase_end();
-        // the memory phase for stage kt: stage kt + 2's loads out first (the buffer they fill,
-        // stage kt - 1's, was read by both groups two phases ago; issued first, they have the
-        // operand reads' time more to land before the wait that publishes them), then stage
-        // kt's operands into registers
+        // the memory phase for stage kt: stage kt's operands into registers and stage kt + 2's
+        // loads out (into the buffer of stage kt - 1, read by both groups two phases ago). The
+        // small-group tiles issue the loads first, so that they have the operand reads' time
+        // more to land before the wait that publishes them (120B gate_up 410 -> 405 us, down
+        // 210 -> 202 us); the full tiles read first (no gain there, and issuing first keeps one
+        // more address live across the reads: a spill in the full-tile gate_up GEMM).
         auto mem_phase = [&](int kt) {
-            if (kt + 2 < kt_total) issue((kt + 2) % 3, kt + 2);
-            read_stage(kt);
+            if constexpr (SMALL) {
+                if (kt + 2 < kt_total) issue((kt + 2) % 3, kt + 2);
+                read_stage(kt);
+            } else {
+                read_stage(kt);
+                if (kt + 2 < kt_total) issue((kt + 2) % 3, kt + 2);
+            }
             wait_lgkm0();
         };
         if (wave < 4) {

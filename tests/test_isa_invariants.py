@@ -64,3 +64,37 @@ def test_stream_copies_wait_counts_the_younger_loads(tmp_path):
             younger = [lines[i] for i in range(copies[-1] + 1, w)
                        if load.match(lines[i]) and "global_load_lds" not in lines[i]]
             assert len(younger) == younger_expected, (sym, w, len(younger))
+
+
+def _blocks_with_depth(lines):
+    """(loop depth, line) for every line of a kernel body, from the compiler's block comments
+    ('; in Loop: Header=... Depth=n' on each basic-block label inside a loop)."""
+    depth = 0
+    for line in lines:
+        if re.match(r"^(\.LBB\d+_\d+:|; %bb\.\d+:)", line):
+            m = re.search(r"Depth=(\d+)", line)
+            depth = int(m.group(1)) if m else 0
+        yield depth, line
+
+
+def test_grouped_gemm_waits_are_its_own(tmp_path):
+    """The prefill GEMMs issue their operand loads from inline assembly (global_load_lds, which
+    the compiler does not track) and wait for a stage with s_waitcnt vmcnt(n), n = the loads of
+    the next stage (3 to 10). That is only right if, inside the contraction loop, no load the
+    compiler issued itself (a scratch spill reload, a global load hoisted into the loop) adds
+    to the count or brings a compiler-inserted wait: every vector-memory load there must be a
+    global_load_lds, every vmcnt one of the kernel's own counts, and no kernel may use scratch."""
+    asm = _device_asm("gemm_grouped.hip", tmp_path)
+    kernels = _kernels(asm, "k_gemm_mx")
+    assert len(kernels) == 4   # up / down x full / small-group tiles
+    vload = re.compile(r"^\s*(global_load|buffer_load|flat_load|scratch_load)\w*\s")
+    vmcnt = re.compile(r"s_waitcnt\s+vmcnt\((\d+)\)")
+    for sym, lines in kernels:
+        assert not any("scratch_" in l for l in lines), sym
+        inner = [l for d, l in _blocks_with_depth(lines) if d >= 2]
+        assert any("global_load_lds" in l for l in inner), sym
+        assert any("v_mfma_scale_f32_16x16x128_f8f6f4" in l for l in inner), sym
+        stray = [l.strip() for l in inner if vload.match(l) and "global_load_lds" not in l]
+        assert not stray, (sym, stray[:4])
+        counts = {int(m.group(1)) for l in inner for m in [vmcnt.search(l)] if m}
+        assert counts <= {0, 3, 4, 6, 7, 8, 9, 10}, (sym, sorted(counts))
