@@ -81,11 +81,25 @@ def stages_of(T: int, variant: str = "layer"):
     return (["rmsnorm"] if variant == "prenorm" and T > 64 else []) + st
 
 
-def kernel_source_sha(kernel: str) -> str:
+def code_only(text: str) -> str:
+    """The source without its comments and with whitespace runs collapsed: a comment edit does
+    not change the kernel, so it does not make a profile of it stale. (The kernel sources hold
+    no string literal containing a comment marker.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_sha(kernel: str, read=None) -> str:
+    """sha256 (16 hex digits) of the kernel's sources, code only; `read(name)` supplies a
+    source's text (default: the file under csrc/)."""
+    if read is None:
+        def read(f):
+            with open(os.path.join(ROOT, "mxfp4_mixture_experts_router_amd", "csrc", f)) as fh:
+                return fh.read()
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "mxfp4_mixture_experts_router_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        h.update(code_only(read(f)).encode())
     return h.hexdigest()[:16]
 
 

@@ -5,8 +5,9 @@
 //  up  : h[r, i] = swiglu(x[tok(r)] . Wgu[e, 2i] + bgu[e, 2i], x[tok(r)] . Wgu[e, 2i+1] + bgu[e, 2i+1])
 //        (ZeroModels GPT-OSS page, "Mixture-of-experts feed-forward"; gate/up interleave:
 //        MaxText PR "Checkpoint conversion utility ...", "1 Support many-to-one transform";
-//        orientation [E, 2I, H]: Megatron-Bridge gpt_oss_bridge page), written as the mx8
-//        matrix h8 (T k rows of I, sorted-row order)
+//        orientation [E, 2I, H]: Megatron-Bridge gpt_oss_bridge page), written as the h8
+//        matrix (mx8 data rows with group-major scales, mx_mfma.h; T k rows of I, sorted-row
+//        order)
 //  down: o[r, d] = w[r] * (h[r] . Wdn[e, d] + bdn[e, d])    (orientation [E, H, I], same page)
 //
 // Work list: every expert's rows [offsets[e], offsets[e+1]) are cut into BM-row tiles; each
@@ -40,9 +41,14 @@
 //
 // Stage buffer layout (bytes):
 //   A   [256 rows][128]: row R = 2 * (tile row) + part; its eight 16-byte chunks c are stored
-//       at slot c ^ (R & 7) (conflict-free operand reads).
+//       at slot c ^ (R & 7).
 //   B   [256 rows][64]: the stage's four packed MXFP4 blocks of weight row n, block c at
 //       slot c ^ ((n >> 1) & 3).
+//   (In a 16-byte operand read the eight lanes m .. m + 7 of a lane group hit eight different
+//   slots of a 128-byte bank row. Orders that also keep lanes m and m + 8 apart over 256 bytes
+//   measured slower, so the hardware serves these reads as the first layout assumes. Where
+//   the bank conflicts its counters report arise is not separated by measurement; the
+//   single-byte scale reads and the epilogue's staging are the remaining candidates.)
 // Then two weight-scale group buffers (group j = stages 3j .. 3j + 2, buffer j % 2):
 //   BSG [256 rows] 16 bytes: the four 4-byte-aligned dwords of weight scale row n that hold
 //       the group's twelve scale bytes (weight scale rows are K / 32 bytes long, not
