@@ -100,7 +100,7 @@ constexpr int kASG = 128 * 16;                 // one A-scale group buffer
 // dwords; both: 1 A-scale window every fourth stage (wavefronts 0-1).
 template <bool SMALL> struct GemmCfg;
 template <> struct GemmCfg<false> {
-    static constexpr int BM = 128, NA = 4, NLMAX = 4;
+    static constexpr int BM = 128, NA = 4;
     static constexpr int OFF_B = 2 * BM * kBK;                 // 32768
     static constexpr int STAGE = OFF_B + kBN * kBK / 2;        // 49152
     static constexpr int GS = 3;                               // stages per weight-scale group
@@ -110,7 +110,7 @@ template <> struct GemmCfg<false> {
     static constexpr int TOTAL = OFF_ASG + 2 * kASG;           // 159744
 };
 template <> struct GemmCfg<true> {
-    static constexpr int BM = 96, NA = 3, NLMAX = 3;
+    static constexpr int BM = 96, NA = 3;
     static constexpr int STAGE = 2 * BM * kBK;                 // 24576
     static constexpr int OFF_BP = 3 * STAGE;                   // 73728: pair slots [half][2]
     static constexpr int BP = 128 * 128;                       // one slot: 128 rows x 128 bytes
