@@ -272,6 +272,10 @@ FORWARD_CASES = [
     ("tiny", 140, 64, 64, 256, 8, 140),     # maximal E and k, prefill path
     ("tiny", 2, 64, 64, 1, 1, 2),           # one expert, k = 1 (weight 1), few-token path
     ("tiny", 9, 64, 64, 1, 1, 9),           # one expert, batched decode path
+    # batched decode with runs of several weight tiles per pair group (127 tiles in runs of 2,
+    # the last run one tile; 125 tiles in runs of 3, the last run two)
+    ("tiny", 64, 64, 4064, 1, 1, 64),
+    ("tiny", 48, 64, 4000, 2, 2, 48),
     ("tiny", 70, 64, 64, 1, 1, 70),         # one expert, prefill path
     ("tiny", 9, 64, 64, 3, 3, 9),           # k = E: every expert routed
     ("tiny", 70, 96, 64, 3, 3, 70),         # k = E, prefill path
