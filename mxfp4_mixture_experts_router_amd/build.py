@@ -1,7 +1,8 @@
 """Build libmoe_mxfp4.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
 Every source under csrc/ is compiled to an object in ``_build/`` (in parallel) and
-linked into ``libmoe_mxfp4.so`` next to this file. Run ``python -m
+linked into ``libmoe_mxfp4.so`` next to this file. The build fails if the compiled kernels
+break the counted-wait invariants their correctness rests on (``isa_check``). Run ``python -m
 mxfp4_mixture_experts_router_amd.build``.
 """
 from __future__ import annotations
@@ -10,6 +11,12 @@ import concurrent.futures as cf
 import os
 import subprocess
 import sys
+
+if __package__:
+    from . import isa_check
+else:   # run as a file
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from mxfp4_mixture_experts_router_amd import isa_check
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -57,8 +64,11 @@ def build(verbose: bool = False, host_asan: bool = False, out: str | None = None
     extra = HOST_ASAN if host_asan else []
     os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        # the counted-wait invariants of the compiled kernels are checked alongside (isa_check)
+        checked = ex.submit(isa_check.check, build_dir)
         objs = list(ex.map(lambda s: _compile(s, build_dir, extra), srcs))
+        checked.result()
     tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
