@@ -557,10 +557,23 @@ def host_info():
         for f in sorted(os.listdir(d)):
             with open(os.path.join(d, f), "rb") as fh:
                 h.update(f.encode() + fh.read())
+    lib_sha = h.hexdigest()[:16]
     with open(os.path.abspath(__file__), "rb") as fh:
         h.update(fh.read())
+    # what the library was built from (written by the build next to it): the commit, when this
+    # run's tree has no history, and whether the library matches the sources in this tree
+    build = None
+    try:
+        with open(os.path.join(ROOT, "mxfp4_mixture_experts_router_amd", "build_info.json")) as f:
+            info = json.load(f)
+        build = {"git_sha": info.get("git_sha"), "sources_dirty": info.get("sources_dirty"),
+                 "library_matches_sources": info.get("sources_sha16") == lib_sha}
+        if git is None:
+            git = info.get("git_sha")
+    except (OSError, ValueError):
+        pass
     return {"cpu_model": model, "host_cores": len(os.sched_getaffinity(0)), "git_sha": git,
-            "source_sha16": h.hexdigest()[:16]}
+            "source_sha16": h.hexdigest()[:16], "build": build}
 
 
 def hbm_probe():

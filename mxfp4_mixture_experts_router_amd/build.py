@@ -75,9 +75,44 @@ def build(verbose: bool = False, host_asan: bool = False, out: str | None = None
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, lib)
+    if not host_asan:
+        write_build_info()
     if verbose:
         print(f"built {lib}")
     return lib
+
+
+BUILD_INFO = os.path.join(PKG, "build_info.json")
+
+
+def sources_sha16() -> str:
+    """Hash of the library's sources (the public header and csrc/), as bench.py also computes."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "include"), CSRC):
+        for f in sorted(os.listdir(d)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def write_build_info() -> None:
+    """Record next to the library which sources it was built from: the git commit (when the
+    tree is a checkout) and a hash of the sources, so that a run on a copy of the tree without
+    its history can still name the commit and tell whether the library matches the sources."""
+    import json
+    sha, dirty = None, None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        if r.returncode == 0:
+            sha = r.stdout.strip() or None
+            d = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--", "include",
+                                os.path.relpath(CSRC, ROOT)], capture_output=True, text=True, timeout=10)
+            dirty = bool(d.stdout.strip()) if d.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(BUILD_INFO, "w") as f:
+        json.dump({"git_sha": sha, "sources_dirty": dirty, "sources_sha16": sources_sha16()}, f)
 
 
 def asan_runtime() -> str:
