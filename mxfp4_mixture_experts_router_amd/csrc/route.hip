@@ -207,7 +207,8 @@ __global__ __launch_bounds__(256) void k_logits(const uint16_t *__restrict__ x, 
 }
 
 // Throughput router for many tokens on the fp64 MFMA (16 x 16 x 4 per instruction): block =
-// 8 wavefronts and 16 consecutive tokens, 16 NT experts. Wavefront w takes the 32-element
+// THREADS / 64 wavefronts (8; 16 for E <= 32, where the registers allow four wavefronts per SIMD to
+// hide more load latency) and 16 consecutive tokens, 16 NT experts. Wavefront w takes the 32-element
 // chunks c = w, w + 8, .. of H (up to three chunks' loads in flight at a time). For chunk c, lane (m, g) (m = lane % 16, g = lane / 16)
 // loads elements 32c + 8g .. 32c + 8g + 7 of token m and of experts 16 nt + m; MFMA step j
 // (0..7) multiplies element j of every lane, so that lane group g supplies contraction index
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(256) void k_logits(const uint16_t *__restrict__ x, 
 // tokens as mx8 rows (a 32-element block = lanes m, m + 16, m + 32, m + 48).
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kRT = 16;             // tokens per block
-constexpr int kRouteThreads = 512;  // 8 wavefronts split H
+constexpr int kRouteThreads = 512;  // 8 wavefronts split H (16 for E <= 32: 1024 threads)
 
 // Eight bf16 values (one uint4) as doubles.
 __device__ __forceinline__ void bf16x8_to_f64(const uint4 &u, double (&d)[8]) {
@@ -264,13 +265,13 @@ __device__ __forceinline__ void mx8_store_quarter(const uint4 &u, uint8_t *q8, i
 // writes those partial logits, without bias, to part[s][t][e]; k_route_topk then adds the S
 // slices in order, adds the bias and selects. For few token groups (fewer than the CUs), so
 // that the fp64 MFMA work of the whole chip is used.
-template <int NT, bool SPLIT>
-__global__ __launch_bounds__(kRouteThreads) void k_route(
+template <int NT, bool SPLIT, int THREADS = kRouteThreads>
+__global__ __launch_bounds__(THREADS) void k_route(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     const uint16_t *__restrict__ br, int64_t T, int H, int E, int k,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ logits_out,
     uint8_t *__restrict__ x8, double *__restrict__ part, int S) {
-    constexpr int NW = kRouteThreads / kWave;
+    constexpr int NW = THREADS / kWave;
     constexpr int kAhead = NT >= 16 ? 1 : (NT >= 8 ? 2 : 3);   // chunks loaded together (registers)
     constexpr int LS = 16 * NT + 1;   // LDS row of one token's logits (padded)
     __shared__ double lg[kRT * LS];
@@ -338,13 +339,13 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
         __syncthreads();
     }
     if (SPLIT) {
-        for (int i = threadIdx.x; i < kRT * E; i += kRouteThreads) {
+        for (int i = threadIdx.x; i < kRT * E; i += THREADS) {
             const int j = i / E, e = i % E;
             if (t0 + j < T) part[(static_cast<int64_t>(slice) * T + t0 + j) * E + e] = lg[j * LS + e];
         }
         return;
     }
-    for (int i = threadIdx.x; i < kRT * E; i += kRouteThreads) {
+    for (int i = threadIdx.x; i < kRT * E; i += THREADS) {
         const int j = i / E, e = i % E;
         lg[j * LS + e] += static_cast<double>(bf16_to_f32(br[e]));
     }
@@ -447,12 +448,17 @@ hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *gamma,
                                          router_b, d.T, d.H, d.E, d.k, topk_idx, topk_w, logits, x8, part, S); \
                            else MOE_LAUNCH((k_route<NT, false>), grid, dim3(kRouteThreads), 0, s, x, router_w, \
                                          router_b, d.T, d.H, d.E, d.k, topk_idx, topk_w, logits, x8, part, 1); } while (0)
-        if (d.E <= 16) MOE_ROUTE(1);
-        else if (d.E <= 32) MOE_ROUTE(2);
+#define MOE_ROUTE_WIDE(NT) do { if (S > 1) MOE_LAUNCH((k_route<NT, true, 1024>), grid, dim3(1024), 0, s, x, router_w, \
+                                         router_b, d.T, d.H, d.E, d.k, topk_idx, topk_w, logits, x8, part, S); \
+                           else MOE_LAUNCH((k_route<NT, false, 1024>), grid, dim3(1024), 0, s, x, router_w, \
+                                         router_b, d.T, d.H, d.E, d.k, topk_idx, topk_w, logits, x8, part, 1); } while (0)
+        if (d.E <= 16) MOE_ROUTE_WIDE(1);
+        else if (d.E <= 32) MOE_ROUTE_WIDE(2);
         else if (d.E <= 64) MOE_ROUTE(4);
         else if (d.E <= 128) MOE_ROUTE(8);
         else MOE_ROUTE(16);
 #undef MOE_ROUTE
+#undef MOE_ROUTE_WIDE
         if (S > 1) {
             const hipError_t e1 = hipGetLastError();
             if (e1 != hipSuccess) {
