@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void k_logits(const uint16_t *__restrict__ x, 
 // Throughput router for many tokens on the fp64 MFMA (16 x 16 x 4 per instruction): block =
 // THREADS / 64 wavefronts (8; 16 for E <= 32, where the registers allow four wavefronts per SIMD to
 // hide more load latency) and 16 consecutive tokens, 16 NT experts. Wavefront w takes the 32-element
-// chunks c = w, w + 8, .. of H (up to three chunks' loads in flight at a time). For chunk c, lane (m, g) (m = lane % 16, g = lane / 16)
+// chunks c = w, w + NW, .. of H (up to three chunks' loads in flight at a time). For chunk c, lane (m, g) (m = lane % 16, g = lane / 16)
 // loads elements 32c + 8g .. 32c + 8g + 7 of token m and of experts 16 nt + m; MFMA step j
 // (0..7) multiplies element j of every lane, so that lane group g supplies contraction index
 // g of the step and A and B agree on the element. Products of bf16 values are exact in
