@@ -104,7 +104,8 @@ def kernel_source_sha(kernel: str, read=None) -> str:
 
 
 OTHER_WORKLOADS = "batched_decode_20b,prefill_20b,prefill_120b"
-DEFAULT_STEPS = {"decode_20b": 2000, "batched_decode_20b": 500, "prefill_20b": 100, "prefill_120b": 100}
+DEFAULT_STEPS = {"decode_20b": 2000, "batched_decode_20b": 500, "prefill_20b": 100, "prefill_120b": 100,
+                 "decode_20b_tp8": 2000, "batched_decode_20b_tp8": 500, "prefill_20b_ep8": 100}
 REPEATS = 5
 
 

@@ -296,6 +296,10 @@ FORWARD_CASES = [
     ("batched_decode_20b", None, None, None, None, None, 64),
     ("prefill_20b", None, None, None, None, None, 4096),
     ("prefill_120b", None, None, None, None, None, 2048),
+    # one GPU's shard of the 20B layer on eight GPUs (tensor-parallel decode, expert-parallel prefill)
+    ("decode_20b_tp8", None, None, None, None, None, 1),
+    ("batched_decode_20b_tp8", None, None, None, None, None, 64),
+    ("prefill_20b_ep8", None, None, None, None, None, 2048),
 ]
 
 
@@ -487,6 +491,10 @@ PRENORM_CASES = [
     ("batched_decode_20b", None, None, None, None, None, 64),
     ("prefill_20b", None, None, None, None, None, 4096),
     ("prefill_120b", None, None, None, None, None, 2048),
+    # one GPU's shard of the 20B layer on eight GPUs (tensor-parallel decode, expert-parallel prefill)
+    ("decode_20b_tp8", None, None, None, None, None, 1),
+    ("batched_decode_20b_tp8", None, None, None, None, None, 64),
+    ("prefill_20b_ep8", None, None, None, None, None, 2048),
 ]
 
 
@@ -533,6 +541,10 @@ BANK_CASES = [
     ("batched_decode_20b", None, None, None, None, None, 64),
     ("prefill_20b", None, None, None, None, None, 4096),
     ("prefill_120b", None, None, None, None, None, 2048),
+    # one GPU's shard of the 20B layer on eight GPUs (tensor-parallel decode, expert-parallel prefill)
+    ("decode_20b_tp8", None, None, None, None, None, 1),
+    ("batched_decode_20b_tp8", None, None, None, None, None, 64),
+    ("prefill_20b_ep8", None, None, None, None, None, 2048),
 ]
 
 

@@ -60,9 +60,9 @@ class MoeConfig:
         return replace(self, **kw)
 
 
-# The five workloads: a tiny layer for exhaustive parity, and GPT-OSS-20B / 120B
-# shaped layers (embed_dim = mlp_dim = 2880, 32 or 128 experts, top-4; ZeroModels
-# GPT-OSS page, "API" table) at decode and prefill token counts.
+# The workloads: a tiny layer for exhaustive parity, GPT-OSS-20B / 120B shaped layers
+# (embed_dim = mlp_dim = 2880, 32 or 128 experts, top-4; ZeroModels GPT-OSS page, "API"
+# table) at decode and prefill token counts, and one GPU's shard of the 20B layer.
 CONFIGS: Dict[str, MoeConfig] = {
     "tiny": MoeConfig("tiny", 0, T=8, H=64, I=64, E=4, k=2, router_b_std=0.01,
                       scale_exp_lo=-6, scale_exp_hi=-2),
@@ -71,6 +71,15 @@ CONFIGS: Dict[str, MoeConfig] = {
                                     expert_offset_std=1.0),
     "prefill_20b": MoeConfig("prefill_20b", 3, T=4096, H=2880, I=2880, E=32, k=4),
     "prefill_120b": MoeConfig("prefill_120b", 4, T=2048, H=2880, I=2880, E=128, k=4),
+    # One GPU's share of the 20B layer on eight GPUs, at its real shape. Tensor-parallel decode:
+    # every expert's I sliced eight ways on 32-element block boundaries (90 blocks: shards of 11
+    # or 12 blocks; the larger, I = 384, sets the step), the router and x replicated.
+    # Expert-parallel prefill: four local experts receiving 2048 routed rows (a quarter each)
+    # of the 4096-token batch, drawn here as 2048 tokens routed top-1 over those four experts.
+    "decode_20b_tp8": MoeConfig("decode_20b_tp8", 5, T=1, H=2880, I=384, E=32, k=4),
+    "batched_decode_20b_tp8": MoeConfig("batched_decode_20b_tp8", 6, T=64, H=2880, I=384, E=32, k=4,
+                                        expert_offset_std=1.0),
+    "prefill_20b_ep8": MoeConfig("prefill_20b_ep8", 7, T=2048, H=2880, I=2880, E=4, k=1),
 }
 
 
