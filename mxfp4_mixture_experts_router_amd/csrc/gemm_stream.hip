@@ -281,13 +281,33 @@ __global__ __launch_bounds__(kThreads) void k_stream(
                 if ((m & 1) == 0 && s < ne) s_h[s * kHP + 8 * wave + (m >> 1)] = swiglu(v, other, alpha, limit);
             }
             __syncthreads();
-            if (tid < ne) {
-                float v[32];
+            // each pair's 32 values (one MX block of its h8 rows) on eight lanes of wavefront 0,
+            // four values each: the block maximum by three lane exchanges, then each lane splits
+            // and stores its own four hi and four lo bytes (the same bytes store_mx8_block writes)
+            if (wave == 0) {
+                const int sl = lane >> 3, j = lane & 7;
+                float v[4] = {0.f, 0.f, 0.f, 0.f};
+                if (sl < ne)
 #pragma unroll
-                for (int i = 0; i < 32; ++i) v[i] = s_h[tid * kHP + i];
-                const int Iw = Nrows / 2;
-                uint8_t *h_sc = h8 + static_cast<size_t>(2 * N) * Iw;
-                store_mx8_block(v, h8, h_sc, static_cast<int64_t>(s_pairs[p0 + tid]), Iw, mx8_scale_stride(Iw), tile);
+                    for (int i = 0; i < 4; ++i) v[i] = s_h[sl * kHP + 4 * j + i];
+                float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+                mx = fmaxf(mx, lane_xor1(mx));
+                mx = fmaxf(mx, lane_xor2(mx));
+                mx = fmaxf(mx, __shfl_xor(mx, 4));
+                if (sl < ne) {
+                    const int eb = mx8_block_exponent(mx);
+                    uint32_t hi, lo;
+                    mx8_split4(ldexpf(v[0], -eb), ldexpf(v[1], -eb), ldexpf(v[2], -eb), ldexpf(v[3], -eb), hi, lo);
+                    const int Iw = Nrows / 2, ss = mx8_scale_stride(Iw);
+                    uint8_t *h_sc = h8 + static_cast<size_t>(2 * N) * Iw;
+                    const int64_t n = s_pairs[p0 + sl];
+                    reinterpret_cast<uint32_t *>(h8 + (2 * n) * Iw + 32 * tile)[j] = hi;
+                    reinterpret_cast<uint32_t *>(h8 + (2 * n + 1) * Iw + 32 * tile)[j] = lo;
+                    if (j == 0) {
+                        h_sc[(2 * n) * ss + tile] = static_cast<uint8_t>(127 + eb);
+                        h_sc[(2 * n + 1) * ss + tile] = static_cast<uint8_t>(123 + eb);
+                    }
+                }
             }
         } else if (wvalid) {
 #pragma unroll
