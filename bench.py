@@ -607,6 +607,29 @@ def hbm_probe():
             "method": "torch copy of 1 GiB (read + write bytes) and torch.sum over 2 GiB fp32, best of 5"}
 
 
+def clock_probe():
+    """The shader clock under a full-chip ALU load (the library's clock probe: 1024 workgroups
+    timing a dependent multiply-add chain with the shader cycle counter against the constant
+    100 MHz counter), as context for the peak rates, which assume 2.4 GHz; median of 5."""
+    import torch
+    import mxfp4_mixture_experts_router_amd as moe
+    lib = moe.load_library()
+    blocks = 1024
+    buf = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    mhz = []
+    for _ in range(6):
+        st = lib.moe_mxfp4_clock_probe(ctypes.c_void_p(buf.data_ptr()), blocks, 200000, ctypes.c_void_p(stream))
+        if st != 0:
+            raise RuntimeError(lib.moe_mxfp4_last_error().decode())
+        torch.cuda.synchronize()
+        c = buf.view(blocks, 2).cpu()
+        mhz.append(100.0 * float(c[:, 0].sum()) / float(c[:, 1].sum()))
+    mhz = sorted(mhz[1:])
+    return {"sclk_MHz": round(mhz[len(mhz) // 2], 1), "method": "library clock probe: shader cycles / 100 MHz "
+            "ticks over a dependent FMA chain on 1024 workgroups, median of 5"}
+
+
 def record(wl, res, cpu):
     cfg = wl.cfg
     out = {
@@ -692,6 +715,7 @@ def main():
         out["other_workloads"] = others
     out["host"] = host_info()
     out["hbm_probe"] = hbm_probe()
+    out["clock_probe"] = clock_probe()
     print(json.dumps(out), flush=True)
 
 

@@ -81,6 +81,15 @@ typedef struct {
 /* ABI version of the loaded library (MOE_MXFP4_ABI_VERSION at build time). */
 int moe_mxfp4_abi_version(void);
 
+/* Measurement support, not a step of the layer: the clock the CUs run at under a full-chip
+ * ALU load (the published peak rates the benchmark divides by assume 2.4 GHz). Launches
+ * `blocks` workgroups of 256 threads, each timing `iters` dependent multiply-adds; workgroup b
+ * writes its shader-clock cycles to cycles[2b] and its ticks of the constant 100 MHz counter
+ * to cycles[2b + 1] (`cycles`: device memory, 2 * blocks uint64, owned by the caller). Clock in
+ * MHz = 100 * sum(cycles[2b]) / sum(cycles[2b + 1]). Asynchronous on `stream`.
+ * MOE_EINVAL if cycles is NULL, blocks is outside 1..65536 or iters < 1. */
+moe_status_t moe_mxfp4_clock_probe(uint64_t *cycles, int blocks, int iters, void *stream);
+
 /* Message describing the last error on this thread ("" if none). Never NULL. */
 const char *moe_mxfp4_last_error(void);
 

@@ -66,6 +66,7 @@ class Shape(ctypes.Structure):
 _vp = ctypes.c_void_p
 _SIGS = {
     "moe_mxfp4_abi_version": (ctypes.c_int, []),
+    "moe_mxfp4_clock_probe": (ctypes.c_int, [_vp, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_mxfp4_last_error": (ctypes.c_char_p, []),
     "moe_mxfp4_check_shape": (ctypes.c_int, [ctypes.POINTER(Shape)]),
     "moe_mxfp4_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)]),

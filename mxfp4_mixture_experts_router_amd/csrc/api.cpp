@@ -160,6 +160,14 @@ moe_status_t hip_status(hipError_t e, const char *what) {
 
 MOE_EXPORT int moe_mxfp4_abi_version(void) { return MOE_MXFP4_ABI_VERSION; }
 
+MOE_EXPORT moe_status_t moe_mxfp4_clock_probe(uint64_t *cycles, int blocks, int iters, void *stream) {
+    REQUIRE(cycles, "cycles");
+    if (blocks < 1 || blocks > 65536) return fail(MOE_EINVAL, "blocks = %d outside 1..65536", blocks);
+    if (iters < 1) return fail(MOE_EINVAL, "iters = %d is not positive", iters);
+    LAUNCH(moe::launch_clock_probe(cycles, blocks, iters, static_cast<hipStream_t>(stream)), "clock probe");
+    return ok();
+}
+
 MOE_EXPORT const char *moe_mxfp4_last_error(void) { return g_last_error.c_str(); }
 
 MOE_EXPORT moe_status_t moe_mxfp4_check_shape(const moe_mxfp4_shape_t *shape) {

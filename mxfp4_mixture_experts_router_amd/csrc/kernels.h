@@ -145,4 +145,8 @@ hipError_t launch_quantize(const uint16_t *x, int64_t rows, int cols, uint8_t *q
 hipError_t launch_dequant(const uint8_t *blocks, const uint8_t *scales, int64_t rows, int cols,
                           uint16_t *out, hipStream_t s);
 
+// Shader-clock probe (benchmark context): workgroup b writes its shader cycles and its 100 MHz
+// ticks over a fixed ALU chain to out[2b], out[2b + 1].
+hipError_t launch_clock_probe(uint64_t *out, int blocks, int iters, hipStream_t s);
+
 }  // namespace moe

@@ -253,6 +253,13 @@ def test_dequant_validates(lib):
     assert lib.moe_mxfp4_dequant(A, A, 0, 64, A, None) == 0       # empty: no launch
 
 
+def test_clock_probe_validates(lib):
+    assert lib.moe_mxfp4_clock_probe(None, 256, 100, None) == EINVAL
+    assert lib.moe_mxfp4_clock_probe(A, 0, 100, None) == EINVAL
+    assert lib.moe_mxfp4_clock_probe(A, 65537, 100, None) == EINVAL
+    assert lib.moe_mxfp4_clock_probe(A, 256, 0, None) == EINVAL
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "_lib", None)
     monkeypatch.setattr(moe, "_LIB_PATH", str(tmp_path / "missing.so"))

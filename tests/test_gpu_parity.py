@@ -10,6 +10,8 @@ decode/prefill switch. Full-size configs run in the same launch configuration as
 benchmark and are compared on every token (the 4096-token and 120B-shaped workloads against
 the oracle's expert-major mode).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -18,7 +20,7 @@ import mxfp4_mixture_experts_router_amd as moe
 import oracle
 from workloads import CONFIGS, make_inputs, f32_from_bf16_bits, bf16_bits_from_f32
 
-from gpu_util import (assert_close_rows, bf16_bits, bf16_to_f64, check_selection, decode_h8, decode_mx8,
+from gpu_util import (assert_close_rows, bf16_bits, bf16_to_f64, check_selection, decode_h8, decode_mx8, dev,
                       host_permutation, to_dev, upload)
 
 pytestmark = pytest.mark.gpu
@@ -574,3 +576,18 @@ def test_forward_dequantized_matches_oracle(name, T, H, I, E, k, n_cmp):
     y2 = moe.moe_forward_dequantized(d["x"], d["router_w"], d["router_b"], gu_w, d["gu_bias"], dn_w,
                                      d["dn_bias"], cfg.k, cfg.alpha, cfg.limit)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.gpu
+def test_clock_probe_reports_a_plausible_clock():
+    """The benchmark's clock probe: shader cycles against the constant 100 MHz counter give a
+    clock between 0.5 and 3 GHz on every workgroup."""
+    lib = moe.load_library()
+    blocks = 512
+    buf = torch.zeros(2 * blocks, dtype=torch.int64, device=dev())
+    assert lib.moe_mxfp4_clock_probe(ctypes.c_void_p(buf.data_ptr()), blocks, 50000, None) == 0
+    torch.cuda.synchronize()
+    c = buf.view(blocks, 2).cpu().numpy().astype(np.float64)
+    assert np.all(c[:, 1] > 0)
+    mhz = 100.0 * c[:, 0] / c[:, 1]
+    assert np.all((mhz > 500) & (mhz < 3000)), (mhz.min(), mhz.max())
