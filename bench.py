@@ -652,7 +652,8 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer's multi-GPU sharding is a design note, not part of this build).",
+              "(the layer's multi-GPU sharding is described, not implemented; the per-GPU shard "
+              "shapes run as the workloads decode_20b_tp8, batched_decode_20b_tp8 and prefill_20b_ep8).",
               file=sys.stderr)
         sys.exit(2)
     import torch
