@@ -186,10 +186,9 @@ size_t moe_mxfp4_noalloc_max_bytes(void);
  * holds at least 2 * MOE_MXFP4_MAX_LAUNCHES hipEvent_t handles created by the caller
  * (timing enabled); stage i records events[2i] and events[2i + 1], so that
  * hipEventElapsedTime(events[2i], events[2i + 1]) is that stage's duration. Every stage is one
- * kernel except the permute stage of the grouped sequence (T > 64, or a larger H or I at any T)
- * while T*k <= 262144 (1024 blocks of 256 pairs): two kernels, a histogram pass and a scatter
- * pass; the first records the start event, the second the end event. Above 262144 pairs the
- * permute is one kernel on one workgroup (the moe_mxfp4_permute kernel).
+ * kernel except the permute stage of the grouped sequence (T > 64, or a larger H or I at any T):
+ * a histogram pass, above 16384 pairs (64 blocks of 256) a scan pass, and a scatter pass; the
+ * first records the start event, the last the end event.
  * *n_launches receives the number of stages. With H <= 4096 and I <= 4096: 3 for
  * T <= 3 (router logits, up-projection with the top-k, down-projection with the combine
  * folded in), 4 for 4 <= T <= 64 (route, up-projection, down-projection, combine); 5 for
@@ -264,14 +263,15 @@ moe_status_t moe_mxfp4_permute(const moe_mxfp4_shape_t *shape,
 
 /*
  * The same permutation on many workgroups: a histogram pass (one workgroup per 256 pairs
- * writes how many of its pairs each expert received) and a scatter pass (each workgroup sums
- * the histograms of the workgroups before it and ranks its own pairs). This is the permute
- * every forward call of the grouped sequence runs; the results are identical to
+ * writes how many of its pairs each expert received), then a scatter pass (each workgroup
+ * ranks its own pairs after those of the workgroups before it). Up to 16384 pairs each
+ * scatter workgroup sums the earlier histograms itself; above that a scan pass (one workgroup
+ * per expert) first turns them into prefix sums, so the work stays linear in T*k. This is the
+ * permute every forward call of the grouped sequence runs; the results are identical to
  * moe_mxfp4_permute's, bit for bit. The histograms need moe_mxfp4_permute_workspace_bytes()
- * bytes of device workspace (4-byte aligned; its contents on entry do not matter). Above
- * 262144 pairs that size is 0 and the call runs the one-workgroup kernel of
- * moe_mxfp4_permute (workspace may then be NULL). MOE_EWORKSPACE if the workspace is NULL or
- * short while a nonzero size is required; other arguments as moe_mxfp4_permute.
+ * bytes of device workspace (4-byte aligned; its contents on entry do not matter).
+ * MOE_EWORKSPACE if the workspace is NULL or short while T*k > 0; other arguments as
+ * moe_mxfp4_permute.
  */
 moe_status_t moe_mxfp4_permute_ws(const moe_mxfp4_shape_t *shape,
                                   const int32_t *topk_idx, const float *topk_w,
@@ -279,8 +279,9 @@ moe_status_t moe_mxfp4_permute_ws(const moe_mxfp4_shape_t *shape,
                                   float *sorted_weight, int32_t *slot_row,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace moe_mxfp4_permute_ws needs (T*k/256 rounded up, times E, times 4 bytes;
- * 0 above 262144 pairs). Only shape->T, E, k are used. Host-only. */
+/* Bytes of workspace moe_mxfp4_permute_ws needs: (T*k/256 rounded up, plus 1) times E times
+ * 4 bytes (one histogram row per workgroup and the per-expert totals); 0 for T*k = 0. Only
+ * shape->T, E, k are used. Host-only. */
 moe_status_t moe_mxfp4_permute_workspace_bytes(const moe_mxfp4_shape_t *shape, size_t *bytes);
 
 /*

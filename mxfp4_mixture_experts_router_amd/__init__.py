@@ -300,8 +300,8 @@ def permute_workspace_bytes(T: int, E: int, k: int) -> int:
 def permute(topk_idx, topk_w, E: int, stream=None, multi_block: bool = False):
     """Expert-sorted permutation. Returns (offsets [E+1], sorted_token, sorted_weight, slot_row).
 
-    ``multi_block``: the histogram + scatter passes the forward calls run (moe_mxfp4_permute_ws),
-    instead of the one-workgroup kernel (moe_mxfp4_permute)."""
+    ``multi_block``: the histogram (+ scan) + scatter passes the forward calls run
+    (moe_mxfp4_permute_ws), instead of the one-workgroup kernel (moe_mxfp4_permute)."""
     T, k = topk_idx.shape
     dev = topk_idx.device
     _need(topk_idx, "topk_idx", (torch.int32,), (T, k), dev)

@@ -64,10 +64,10 @@ hipError_t launch_route(const Dims &d, const uint16_t *x, const uint16_t *gamma,
                         const uint16_t *router_w, const uint16_t *router_b, int32_t *topk_idx, float *topk_w,
                         float *logits, uint8_t *x8, hipStream_t s, double *part = nullptr);
 
-// hist (optional): workspace of permute_hist_ints(T k, E) ints; with it (and that count
-// nonzero) the permutation runs on many workgroups (a histogram pass, then a scatter pass),
-// without it on one. Both give the same result.
-constexpr int64_t kPermuteMaxBlocks = 1024;
+// hist (optional): workspace of permute_hist_ints(T k, E) ints; with it the permutation runs
+// on many workgroups (a histogram pass, above kPermuteDirectBlocks blocks of 256 pairs a scan
+// pass, then a scatter pass), without it on one. All give the same result.
+constexpr int kPermuteDirectBlocks = 64;
 int64_t permute_hist_ints(int64_t N, int E);
 hipError_t launch_permute(const Dims &d, const int32_t *topk_idx, const float *topk_w,
                           int32_t *offsets, int32_t *sorted_token, float *sorted_w,

@@ -148,11 +148,16 @@ __global__ __launch_bounds__(kThreads) void k_permute(
 
 // The same permutation by many workgroups, for the forward passes (which have workspace for
 // the per-block histograms). Block b owns pairs [b P, (b + 1) P), one per thread.
-// k_permute_count writes hist[b][e], the number of block b's pairs routed to expert e.
-// k_permute_scatter then gives pair n (expert e, block b, wavefront w, lane l) the position
-//   offsets[e] + sum_{b' < b} hist[b'][e] + (pairs of e in wavefronts < w of block b)
+// k_permute_count writes hist[e][b], the number of block b's pairs routed to expert e
+// (expert-major: one row of nblk counts per expert). k_permute_scatter then gives pair n
+// (expert e, block b, wavefront w, lane l) the position
+//   offsets[e] + sum_{b' < b} hist[e][b'] + (pairs of e in wavefronts < w of block b)
 //              + (pairs of e in lanes < l of wavefront w),
 // the count of earlier pairs routed to e: the same stable order as k_permute.
+// Up to kPermuteDirectBlocks blocks every scatter block sums the histogram itself (nblk E
+// reads per block, so the total grows with nblk^2); above that k_permute_scan first turns
+// each expert's row into its exclusive prefix sums and its total, and a scatter block reads
+// only the E entries of its own column.
 constexpr int kPT = 256;   // threads (and pairs) per block
 constexpr int kPW = kPT / kWave;
 
@@ -169,13 +174,49 @@ __global__ __launch_bounds__(kPT) void k_permute_count(const int32_t *__restrict
     const uint64_t peers = same_expert_lanes<BITS>(e, valid);
     if (valid && (peers & lanemask_lt()) == 0) atomicAdd(&cnt[e], __popcll(peers));
     __syncthreads();
-    for (int e2 = tid; e2 < E; e2 += kPT) hist[static_cast<int64_t>(blockIdx.x) * E + e2] = cnt[e2];
+    for (int e2 = tid; e2 < E; e2 += kPT) hist[static_cast<int64_t>(e2) * gridDim.x + blockIdx.x] = cnt[e2];
 }
 
-template <int BITS>
+// One workgroup per expert e: hist[e][b] becomes sum_{b' < b} hist[e][b'] (in place) and
+// tot[e] the row's total, scanning kScanT entries at a time.
+constexpr int kScanT = 1024;
+__global__ __launch_bounds__(kScanT) void k_permute_scan(int32_t *__restrict__ hist, int nblk,
+                                                         int32_t *__restrict__ tot) {
+    __shared__ int wsum[kScanT / kWave];
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    int32_t *row = hist + static_cast<int64_t>(blockIdx.x) * nblk;
+    int carry = 0;
+    for (int base = 0; base < nblk; base += kScanT) {
+        const int i = base + tid;
+        const int v = i < nblk ? row[i] : 0;
+        int incl = v;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        if (lane == kWave - 1) wsum[wave] = incl;
+        __syncthreads();
+        int before = 0, chunk = 0;
+#pragma unroll
+        for (int w = 0; w < kScanT / kWave; ++w) {
+            const int c = wsum[w];
+            before += w < wave ? c : 0;
+            chunk += c;
+        }
+        if (i < nblk) row[i] = carry + before + incl - v;
+        carry += chunk;
+        __syncthreads();   // wsum is rewritten by the next chunk
+    }
+    if (tid == 0) tot[blockIdx.x] = carry;
+}
+
+template <int BITS, bool SCANNED>
 __global__ __launch_bounds__(kPT) void k_permute_scatter(
     const int32_t *__restrict__ topk_idx, const float *__restrict__ topk_w, int32_t N, int E, int k,
-    int nblk, const int32_t *__restrict__ hist, int32_t *__restrict__ offsets,
+    int nblk, const int32_t *__restrict__ hist, const int32_t *__restrict__ hist_tot, int32_t *__restrict__ offsets,
     int32_t *__restrict__ sorted_token, float *__restrict__ sorted_w, int32_t *__restrict__ slot_row) {
     __shared__ int tot[kMaxE];        // pairs per expert, all blocks
     __shared__ int before[kMaxE];     // pairs per expert in blocks < this one
@@ -186,8 +227,13 @@ __global__ __launch_bounds__(kPT) void k_permute_scatter(
     const int lane = tid % kWave;
     const int b = blockIdx.x;
     for (int e = tid; e < E; e += kPT) {
-        tot[e] = 0;
-        before[e] = 0;
+        if (SCANNED) {
+            tot[e] = hist_tot[e];
+            before[e] = hist[static_cast<int64_t>(e) * nblk + b];
+        } else {
+            tot[e] = 0;
+            before[e] = 0;
+        }
     }
 #pragma unroll
     for (int w = 0; w < kPW; ++w)
@@ -196,14 +242,16 @@ __global__ __launch_bounds__(kPT) void k_permute_scatter(
     const int e = n < N ? topk_idx[n] : -1;
     const float wt = n < N ? topk_w[n] : 0.f;
     __syncthreads();
-    // column sums of hist (integers: the order of the LDS atomics does not matter)
-    const int total = nblk * E;
+    if (!SCANNED) {
+        // row sums of hist (integers: the order of the LDS atomics does not matter)
+        const int total = nblk * E;
 #pragma unroll 8
-    for (int q = tid; q < total; q += kPT) {
-        const int c = hist[q];
-        const int i = q / E, ee = q - i * E;
-        atomicAdd(&tot[ee], c);
-        if (i < b) atomicAdd(&before[ee], c);
+        for (int q = tid; q < total; q += kPT) {
+            const int c = hist[q];
+            const int ee = q / nblk, i = q - ee * nblk;
+            atomicAdd(&tot[ee], c);
+            if (i < b) atomicAdd(&before[ee], c);
+        }
     }
     const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
     const uint64_t peers = same_expert_lanes<BITS>(e, valid);
@@ -226,7 +274,7 @@ __global__ __launch_bounds__(kPT) void k_permute_scatter(
 
 int64_t permute_hist_ints(int64_t N, int E) {
     const int64_t nblk = (N + kPT - 1) / kPT;
-    return nblk <= kPermuteMaxBlocks ? nblk * E : 0;
+    return N > 0 ? (nblk + 1) * E : 0;
 }
 
 hipError_t launch_permute(const Dims &d, const int32_t *topk_idx, const float *topk_w,
@@ -234,24 +282,33 @@ hipError_t launch_permute(const Dims &d, const int32_t *topk_idx, const float *t
                           int32_t *slot_row, hipStream_t s, int32_t *hist) {
     const int32_t N = static_cast<int32_t>(d.T * d.k);
     const int nblk = static_cast<int>((static_cast<int64_t>(N) + kPT - 1) / kPT);
-    if (hist != nullptr && N > 0 && permute_hist_ints(N, d.E) > 0) {
-        // one stage, two launches: the count kernel records the stage's start event, the
-        // scatter kernel its stop event
+    if (hist != nullptr && N > 0) {
+        // one stage, two or three launches: the count kernel records the stage's start event,
+        // the scatter kernel its stop event
+        int32_t *tot = hist + static_cast<int64_t>(nblk) * d.E;
         const LaunchEvents ev = launch_events();
-#define MOE_PERMUTE2(B)                                                                                  \
-    do {                                                                                                 \
-        launch_events() = LaunchEvents{ev.start, nullptr};                                               \
-        MOE_LAUNCH(k_permute_count<B>, dim3(nblk), dim3(kPT), 0, s, topk_idx, N, d.E, hist);             \
-        launch_events() = LaunchEvents{nullptr, ev.stop};                                                \
-        MOE_LAUNCH(k_permute_scatter<B>, dim3(nblk), dim3(kPT), 0, s, topk_idx, topk_w, N, d.E, d.k,     \
-                   nblk, hist, offsets, sorted_token, sorted_w, slot_row);                               \
-        launch_events() = ev;                                                                            \
+#define MOE_PERMUTE_MB(B)                                                                                 \
+    do {                                                                                                  \
+        launch_events() = LaunchEvents{ev.start, nullptr};                                                \
+        MOE_LAUNCH(k_permute_count<B>, dim3(nblk), dim3(kPT), 0, s, topk_idx, N, d.E, hist);              \
+        launch_events() = LaunchEvents{};                                                                 \
+        if (nblk > kPermuteDirectBlocks) {                                                                \
+            MOE_LAUNCH(k_permute_scan, dim3(d.E), dim3(kScanT), 0, s, hist, nblk, tot);                   \
+            launch_events() = LaunchEvents{nullptr, ev.stop};                                             \
+            MOE_LAUNCH((k_permute_scatter<B, true>), dim3(nblk), dim3(kPT), 0, s, topk_idx, topk_w, N,    \
+                       d.E, d.k, nblk, hist, tot, offsets, sorted_token, sorted_w, slot_row);             \
+        } else {                                                                                          \
+            launch_events() = LaunchEvents{nullptr, ev.stop};                                             \
+            MOE_LAUNCH((k_permute_scatter<B, false>), dim3(nblk), dim3(kPT), 0, s, topk_idx, topk_w, N,   \
+                       d.E, d.k, nblk, hist, tot, offsets, sorted_token, sorted_w, slot_row);             \
+        }                                                                                                 \
+        launch_events() = ev;                                                                             \
     } while (0)
-        if (d.E <= 32) MOE_PERMUTE2(5);
-        else if (d.E <= 64) MOE_PERMUTE2(6);
-        else if (d.E <= 128) MOE_PERMUTE2(7);
-        else MOE_PERMUTE2(8);
-#undef MOE_PERMUTE2
+        if (d.E <= 32) MOE_PERMUTE_MB(5);
+        else if (d.E <= 64) MOE_PERMUTE_MB(6);
+        else if (d.E <= 128) MOE_PERMUTE_MB(7);
+        else MOE_PERMUTE_MB(8);
+#undef MOE_PERMUTE_MB
         return hipGetLastError();
     }
 #define MOE_PERMUTE(B) MOE_LAUNCH(k_permute<B>, dim3(1), dim3(kThreads), 0, s, topk_idx, topk_w, N, d.E, d.k, \

@@ -268,18 +268,20 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 
 @pytest.mark.parametrize("T,E,k,blocks", [(64, 32, 4, 1), (65, 32, 4, 2), (4096, 32, 4, 64), (2048, 128, 4, 32),
-                                          (65536, 32, 4, 1024), (65537, 32, 4, 0), (1, 256, 8, 1)])
+                                          (65536, 32, 4, 1024), (65537, 32, 4, 1025), (1, 256, 8, 1),
+                                          (1 << 24, 128, 4, 1 << 18), (0, 32, 4, -1)])
 def test_permute_workspace_bytes(lib, T, E, k, blocks):
-    """One histogram row of E ints per 256 pairs, up to 1024 rows; none above (one workgroup)."""
+    """One histogram row of E ints per 256 pairs plus one row of per-expert totals, at any
+    size; nothing for no pairs."""
     s = shape(T=T, E=E, k=k)
     n = ctypes.c_size_t(12345)
     assert lib.moe_mxfp4_permute_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == 0
-    assert n.value == blocks * E * 4
+    assert n.value == (blocks + 1) * E * 4
 
 
 def test_permute_ws_validation(lib):
-    s = shape(T=100, E=32, k=4)       # 400 pairs: 2 histogram rows of 32 ints
-    need = 2 * 32 * 4
+    s = shape(T=100, E=32, k=4)       # 400 pairs: 2 histogram rows of 32 ints and the totals
+    need = 3 * 32 * 4
     args = [A, A, A, A, A, A]
     assert lib.moe_mxfp4_permute_ws(ctypes.byref(s), *args, None, need, None) == EWORKSPACE
     assert lib.moe_mxfp4_permute_ws(ctypes.byref(s), *args, A, need - 1, None) == EWORKSPACE

@@ -163,17 +163,20 @@ def _random_routing(T, E, k, seed, skew=0.0):
 PERMUTE_CASES = [(1, 32, 4, 0.0), (64, 32, 4, 2.0), (4096, 32, 4, 0.0), (2048, 128, 4, 1.0),
                  (333, 256, 8, 3.0), (1025, 4, 4, 0.0), (500, 16, 1, 5.0), (4097, 32, 4, 0.0),
                  (5000, 64, 4, 1.0),
-                 (32, 256, 8, 0.0),        # 256 pairs: one block of the two-pass permute
+                 (32, 256, 8, 0.0),        # 256 pairs: one block of the many-workgroup permute
+                 (4100, 32, 4, 0.0),       # 65 blocks: the first with the scan pass
                  (20000, 256, 8, 2.0),     # 625 blocks, E = 256, k = 8
-                 (65536, 32, 4, 1.0),      # 1024 blocks: the largest two-pass permute
-                 (65537, 32, 4, 1.0)]      # 262148 pairs: past 1024 blocks, one workgroup
+                 (65536, 32, 4, 1.0),      # 1024 blocks, a whole scan chunk
+                 (65537, 32, 4, 1.0),      # 1025 blocks: a second scan chunk of one entry
+                 (300000, 128, 4, 2.0)]    # 4688 blocks: five scan chunks, the last ragged
 
 
-@pytest.mark.parametrize("multi_block", [False, True], ids=["one_workgroup", "two_pass"])
+@pytest.mark.parametrize("multi_block", [False, True], ids=["one_workgroup", "multi_block"])
 @pytest.mark.parametrize("T,E,k,skew", PERMUTE_CASES)
 def test_permute_is_a_stable_sort(T, E, k, skew, multi_block):
     # one workgroup: T k = 16384 pairs and fewer are sorted in LDS, more take the direct path;
-    # two-pass: the histogram + scatter kernels every forward of the grouped sequence runs
+    # multi_block: the histogram (+ scan above 64 blocks) + scatter kernels every forward of
+    # the grouped sequence runs
     idx, w = _random_routing(T, E, k, seed=T + E, skew=skew)
     offsets, sorted_token, order, slot_row = host_permutation(idx, E)
     g_off, g_tok, g_w, g_slot = moe.permute(to_dev(idx), to_dev(w), E, multi_block=multi_block)
