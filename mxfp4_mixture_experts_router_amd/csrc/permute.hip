@@ -148,16 +148,16 @@ __global__ __launch_bounds__(kThreads) void k_permute(
 
 // The same permutation by many workgroups, for the forward passes (which have workspace for
 // the per-block histograms). Block b owns pairs [b P, (b + 1) P), one per thread.
-// k_permute_count writes hist[e][b], the number of block b's pairs routed to expert e
-// (expert-major: one row of nblk counts per expert). k_permute_scatter then gives pair n
-// (expert e, block b, wavefront w, lane l) the position
-//   offsets[e] + sum_{b' < b} hist[e][b'] + (pairs of e in wavefronts < w of block b)
+// k_permute_count writes hist(e, b), the number of block b's pairs routed to expert e.
+// k_permute_scatter then gives pair n (expert e, block b, wavefront w, lane l) the position
+//   offsets[e] + sum_{b' < b} hist(e, b') + (pairs of e in wavefronts < w of block b)
 //              + (pairs of e in lanes < l of wavefront w),
 // the count of earlier pairs routed to e: the same stable order as k_permute.
-// Up to kPermuteDirectBlocks blocks every scatter block sums the histogram itself (nblk E
-// reads per block, so the total grows with nblk^2); above that k_permute_scan first turns
-// each expert's row into its exclusive prefix sums and its total, and a scatter block reads
-// only the E entries of its own column.
+// Up to kPermuteDirectBlocks blocks the histogram is block-major (hist[b][e]) and every
+// scatter block sums it itself (nblk E reads per block, so the total grows with nblk^2);
+// above that it is expert-major (hist[e][b]), k_permute_scan first turns each expert's row
+// into its exclusive prefix sums and its total, and a scatter block reads only the E entries
+// of its own column.
 constexpr int kPT = 256;   // threads (and pairs) per block
 constexpr int kPW = kPT / kWave;
 
@@ -174,7 +174,12 @@ __global__ __launch_bounds__(kPT) void k_permute_count(const int32_t *__restrict
     const uint64_t peers = same_expert_lanes<BITS>(e, valid);
     if (valid && (peers & lanemask_lt()) == 0) atomicAdd(&cnt[e], __popcll(peers));
     __syncthreads();
-    for (int e2 = tid; e2 < E; e2 += kPT) hist[static_cast<int64_t>(e2) * gridDim.x + blockIdx.x] = cnt[e2];
+    // expert-major for the scan pass; block-major otherwise, so that the direct sums' adjacent
+    // lanes add into different experts' LDS counters
+    const bool by_expert = gridDim.x > kPermuteDirectBlocks;
+    for (int e2 = tid; e2 < E; e2 += kPT)
+        hist[by_expert ? static_cast<int64_t>(e2) * gridDim.x + blockIdx.x
+                       : static_cast<int64_t>(blockIdx.x) * E + e2] = cnt[e2];
 }
 
 // One workgroup per expert e: hist[e][b] becomes sum_{b' < b} hist[e][b'] (in place) and
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(kPT) void k_permute_scatter(
 #pragma unroll 8
         for (int q = tid; q < total; q += kPT) {
             const int c = hist[q];
-            const int ee = q / nblk, i = q - ee * nblk;
+            const int i = q / E, ee = q - i * E;
             atomicAdd(&tot[ee], c);
             if (i < b) atomicAdd(&before[ee], c);
         }
