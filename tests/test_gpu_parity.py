@@ -168,7 +168,9 @@ PERMUTE_CASES = [(1, 32, 4, 0.0), (64, 32, 4, 2.0), (4096, 32, 4, 0.0), (2048, 1
                  (20000, 256, 8, 2.0),     # 625 blocks, E = 256, k = 8
                  (65536, 32, 4, 1.0),      # 1024 blocks, a whole scan chunk
                  (65537, 32, 4, 1.0),      # 1025 blocks: a second scan chunk of one entry
-                 (300000, 128, 4, 2.0)]    # 4688 blocks: five scan chunks, the last ragged
+                 (300000, 128, 4, 2.0),    # 4688 blocks: five scan chunks, the last ragged
+                 (70000, 1, 1, 0.0),       # one expert: every pair keeps its place
+                 (9000, 3, 2, 1.0)]        # 71 blocks, an odd expert count
 
 
 @pytest.mark.parametrize("multi_block", [False, True], ids=["one_workgroup", "multi_block"])
