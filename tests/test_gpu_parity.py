@@ -295,6 +295,9 @@ FORWARD_CASES = [
     ("tiny", 300, 256, 64, 64, 4, 300),
     ("tiny", 1100, 96, 64, 128, 4, 1100),
     ("tiny", 2100, 128, 64, 64, 2, 2100),
+    # more than 64 blocks of 256 routed pairs: the permutation's scan pass
+    ("tiny", 9000, 64, 64, 4, 2, 9000),
+    ("tiny", 4500, 64, 96, 128, 4, 4500),
     ("tiny", 1, 3104, 64, 4, 2, 1),         # T = 1 at widths past 3072
     ("tiny", 1, 64, 3072, 4, 4, 1),
     ("tiny", 1, 64, 3104, 2, 2, 1),
@@ -401,7 +404,9 @@ class _HipEvents:
     # H or I above 4096: the grouped sequence at any token count
     (3, 5, False, 4128, 64, 4), (17, 5, False, 64, 4128, 4), (3, 6, True, 4128, 64, 4), (17, 6, True, 64, 4128, 4),
     # the router in two kernels (slices of H, then the top-k): still one stage
-    (300, 5, False, 128, 64, 64), (300, 6, True, 128, 64, 64)])
+    (300, 5, False, 128, 64, 64), (300, 6, True, 128, 64, 64),
+    # the permute in three kernels (histogram, scan, scatter): still one stage
+    (9000, 5, False, 64, 64, 4)])
 def test_forward_timed_matches_forward(T, launches, prenorm, H, I, E):
     import ctypes
     cfg = CONFIGS["tiny"].with_(H=H, I=I, E=E)
