@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kPT) void k_permute_scatter(
     const float wt = n < N ? topk_w[n] : 0.f;
     __syncthreads();
     if (!SCANNED) {
-        // row sums of hist (integers: the order of the LDS atomics does not matter)
+        // column sums of hist[b][e] (integers: the order of the LDS atomics does not matter)
         const int total = nblk * E;
 #pragma unroll 8
         for (int q = tid; q < total; q += kPT) {
