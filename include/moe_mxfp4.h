@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_MXFP4_ABI_VERSION 5
+#define MOE_MXFP4_ABI_VERSION 6
 
 typedef uint16_t moe_bf16_t;
 

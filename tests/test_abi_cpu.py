@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert moe.abi_version() == 5
-    assert "#define MOE_MXFP4_ABI_VERSION 5" in open(HEADER).read()
+    assert moe.abi_version() == 6
+    assert "#define MOE_MXFP4_ABI_VERSION 6" in open(HEADER).read()
 
 
 def shape(T=1, H=2880, I=2880, E=32, k=4, alpha=1.702, limit=7.0):
